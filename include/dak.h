@@ -1,0 +1,250 @@
+/*
+ * dak.h -- C ABI of libdak: direct-access split operators over two memory tiers
+ * (pinned host memory and HBM) on one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes follows the DAK paper ("DAK: Direct-Access-Enabled
+ * GPU Memory Offloading with Optimal Efficiency for LLM Inference", Lin, Guo and
+ * Lin) and its walkthrough (pinghaoyang.com.cn, "DAK 完全拆解").  The kernels
+ * are written for CDNA4; the paper's Hopper TMA/multicast design is not used.
+ *
+ * Conventions shared by every entry point
+ *   - Status codes: DAK_OK (0) on success, a negative dak_status otherwise.  On
+ *     error nothing has been launched and no output has been written;
+ *     dak_last_error() gives a message (thread-local).
+ *   - Ownership: the caller allocates and owns every buffer (device memory,
+ *     pinned host memory, workspaces).  The library never allocates on the
+ *     compute entry points.
+ *   - Streams: `stream` is a hipStream_t passed as void*; NULL means the null
+ *     stream.  Compute calls are asynchronous and stream-ordered: outputs are
+ *     valid once the stream has completed.  Probes synchronize to time.
+ *   - Pointers to device memory must be device allocations on the current
+ *     device; pointers to host memory must lie inside a pinned (page-locked)
+ *     allocation made with hipHostMalloc / torch pin_memory.  Both are checked
+ *     with hipPointerGetAttributes before any launch (DAK_EINVAL otherwise).
+ *   - bf16 means IEEE bfloat16 stored as 16-bit words; fp32 is IEEE binary32.
+ *   - Deterministic: no atomics in the compute path; for fixed shapes the
+ *     result bits do not depend on the host/HBM split, the host CU count or the
+ *     in-flight window.
+ */
+#ifndef DAK_H
+#define DAK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dak_status;
+enum {
+  DAK_OK = 0,
+  DAK_EINVAL = -1,        /* bad argument (shape, pointer, alignment, range) */
+  DAK_EINFEASIBLE = -2,   /* the host budget exceeds what the ops hold */
+  DAK_EHIP = -3,          /* a HIP runtime call failed; see dak_last_hip_error() */
+  DAK_EUNSUPPORTED = -4   /* a valid request this build does not implement */
+};
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* dak_last_error(void);
+/* hipError_t of the last DAK_EHIP on the calling thread (0 if none). */
+int32_t dak_last_hip_error(void);
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t dak_abi_version(void);
+#define DAK_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------ */
+/* Capacity and planning (pure CPU, deterministic)                            */
+/* ------------------------------------------------------------------------ */
+
+/* One operation for the planner.  DAK paper §4.2.2 "Optimal Greedy Offload".
+ *   units      n_i: tile-rows of a weight matrix, or requests of a KV cache
+ *   unit_bytes u_i: bytes per unit (C_i = n_i * u_i)
+ *   t_comp_s   T_comp,i: compute time of the op in seconds (>= 0), e.g. its
+ *              flops divided by the measured compute rate                      */
+typedef struct {
+  uint64_t units;
+  uint64_t unit_bytes;
+  double t_comp_s;
+} dak_op_desc;
+
+/* Lower bound on the global offload ratio for a footprint of M bytes (weights
+ * plus KV) and H bytes of usable HBM: max(0, (M - H) / M).  Walkthrough,
+ * capacity section (the x_global constraint; runtime workspace ignored).
+ * Returns 0 when M == 0. */
+double dak_min_offload_ratio(uint64_t footprint_bytes, uint64_t hbm_bytes);
+
+/* Greedy per-operation host-unit counts for a global ratio x_global.
+ * DAK paper §4.2.1 (cost model), §4.2.2 (three phases), App. A eq. (1).
+ *   T_i(h) = max(T_comp,i, (n_i - h) u_i / b_hbm, h u_i / b_host), byte counts
+ *            converted to double before dividing;
+ *   a_i, b_i = first and last h in [0, n_i] minimising T_i;
+ *   op i is memory-bound iff T_i(0) > T_comp,i;
+ *   W = ceil(x_global * sum_i C_i) (one double multiply, then ceil);
+ *   phase 1: memory-bound ops raised toward a_i; phase 2: all ops toward b_i;
+ *   phase 3: all ops toward n_i; ops visited in index order, each taking only
+ *   ceil((W - S) / u_i) more units; allocation stops once S >= W.
+ * Arguments
+ *   ops[n_ops]          caller-owned, n_ops >= 1, every units >= 1 and
+ *                       unit_bytes >= 1, sum C_i <= 2^53
+ *   b_hbm, b_host       bytes per second, > 0 and finite (measured)
+ *   x_global            in [0, 1]; the caller ensures it is at least
+ *                       dak_min_offload_ratio(M, H) (only it knows H)
+ *   host_units_out      caller-owned array of n_ops; receives h_i
+ *   modeled_time_s_out  nullable; receives sum_i T_i(h_i) (op order)
+ * Errors: DAK_EINVAL on bad arguments, DAK_EINFEASIBLE if S < W after phase 3
+ * (cannot happen for x_global <= 1).  Outputs are untouched on error. */
+dak_status dak_plan_offload(const dak_op_desc* ops, size_t n_ops, double b_hbm, double b_host,
+                            double x_global, uint64_t* host_units_out,
+                            double* modeled_time_s_out);
+
+/* The per-op quantities the planner uses: a_i, b_i (as above) and whether the
+ * op is memory-bound.  Any output pointer may be NULL. */
+dak_status dak_op_turning_points(const dak_op_desc* op, double b_hbm, double b_host,
+                                 uint64_t* a_out, uint64_t* b_out, int32_t* memory_bound_out);
+
+/* Host work-group count for `items` host work items under a cap of `cap`
+ * host work-groups: the G in [1, min(cap, items)] with the fewest waves
+ * ceil(items / G), and the smallest such G.  DAK paper §4.1 (wave alignment,
+ * congestion cap); walkthrough (waves = ceil(tiles / SMs)).  0 if items <= 0;
+ * -1 if cap <= 0. */
+int64_t dak_host_workgroups(int64_t items, int32_t cap);
+
+/* ------------------------------------------------------------------------ */
+/* Launch configuration (congestion control)                                  */
+/* ------------------------------------------------------------------------ */
+
+/* DAK paper §4.3.1 "Congestion Control over Local/Remote Access": the number
+ * of compute units reading the host and the requests each keeps in flight are
+ * capped; both come from an offline sweep.
+ *   host_cus       cap on work-groups (one per CU) that read host memory;
+ *                  0 = library default (16)
+ *   window         host in-flight window: 16-byte loads per lane issued ahead
+ *                  of use in the host role; one of 1, 2, 4, 8; 0 = default (4)
+ *   flags          bit-or of DAK_FLAG_*
+ *   byte_counters  device pointer to 2 uint64 (host bytes, HBM bytes), used
+ *                  only with DAK_FLAG_COUNT_BYTES: the kernels add the bytes
+ *                  of A (or of K and V) they load from each tier.  The caller
+ *                  zeroes them.
+ * A NULL dak_launch_cfg* means all defaults. */
+typedef struct {
+  int32_t host_cus;
+  int32_t window;
+  int32_t flags;
+  int32_t reserved;
+  uint64_t* byte_counters;
+} dak_launch_cfg;
+
+#define DAK_FLAG_COUNT_BYTES 1
+
+/* ------------------------------------------------------------------------ */
+/* Split GEMM: y = x . A^T with A split by tile-rows across the two tiers      */
+/* ------------------------------------------------------------------------ */
+
+/* A weight matrix A (M x K, bf16, row-major, leading dimension K) cut along M
+ * into tile-rows of m rows; tile-rows [0, h) are in pinned host memory and
+ * [h, M/m) in HBM.  DAK paper §4.1 "Data Partition", Fig. 5a.
+ *   host  rows [0, h*m) of A, contiguous, in pinned host memory (may be NULL
+ *         when h == 0)
+ *   hbm   rows [h*m, M) of A, contiguous, in device memory (may be NULL when
+ *         h*m == M)
+ *   M, K  M >= 1 a multiple of m; K >= 8 a multiple of 8
+ *   m     tile-row height, a positive multiple of 16
+ *   h     host tile-rows, 0 <= h <= M/m
+ * Both pointers 16-byte aligned. */
+typedef struct {
+  const void* host;
+  const void* hbm;
+  int64_t M;
+  int64_t K;
+  int32_t m;
+  int32_t reserved;
+  int64_t h;
+} dak_split_matrix;
+
+/* y[n, r] = sum_k A[r, k] * x[n, k] for n < N, r < M (fp32 accumulation).
+ * DAK paper §4.1 "Kernel over Partitioned Memory": disjoint work-groups compute
+ * disjoint output rows; each work-group reads only one tier; a host tile-row
+ * is never split along N, so every host byte crosses the link once.
+ *   A   the split matrix (see dak_split_matrix)
+ *   x   bf16 [N, K] row-major in device memory, 16-byte aligned
+ *   N   1 <= N <= 256
+ *   y   fp32 [N, M] row-major in device memory, 16-byte aligned; fully written
+ *   cfg nullable launch configuration
+ * Errors: DAK_EINVAL for shapes/pointers outside the above; DAK_EUNSUPPORTED
+ * for N > 256; DAK_EHIP if the launch fails. */
+dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, float* y,
+                           const dak_launch_cfg* cfg, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Split decode attention: KV cache split along the batch                      */
+/* ------------------------------------------------------------------------ */
+
+/* KV caches of `batch` requests; requests [0, h) in pinned host memory and
+ * [h, batch) in HBM.  DAK paper §5 "Supporting FlashAttention": each request
+ * attends entirely within one tier.
+ *   k_host, v_host  bf16 [h, n_kv_heads, ctx, head_dim] row-major (NULL if h == 0)
+ *   k_hbm,  v_hbm   bf16 [batch - h, n_kv_heads, ctx, head_dim] (NULL if h == batch)
+ *   head_dim        128
+ *   ctx             >= 1 tokens per request, all valid (no mask)
+ * All pointers 16-byte aligned. */
+typedef struct {
+  const void* k_host;
+  const void* v_host;
+  const void* k_hbm;
+  const void* v_hbm;
+  int64_t batch;
+  int64_t h;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int64_t ctx;
+} dak_split_kv;
+
+/* Bytes of device workspace dak_splitk_decode_attn needs for these shapes
+ * (0 on invalid shapes). */
+size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads);
+
+/* out[b, j, :] = sum_t softmax_t(scale * q[b, j] . K[b, g, t]) V[b, g, t, :]
+ * with g = j / (n_q_heads / n_kv_heads) (grouped-query attention), one query
+ * token per request, fp32 accumulation, exact softmax.
+ *   q        bf16 [batch, n_q_heads, head_dim] in device memory
+ *   kv       the split KV cache
+ *   n_q_heads a multiple of n_kv_heads, group size 1, 2, 4 or 8
+ *   scale    finite softmax scale (e.g. 1/sqrt(head_dim))
+ *   out      fp32 [batch, n_q_heads, head_dim] in device memory; fully written
+ *   ws       device workspace of at least dak_decode_attn_workspace_bytes()
+ *   cfg      nullable launch configuration
+ * Errors: DAK_EINVAL for shapes/pointers outside the above, DAK_EUNSUPPORTED
+ * for head_dim != 128 or a group size other than 1, 2, 4, 8. */
+dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
+                                  float scale, float* out, void* ws, size_t ws_bytes,
+                                  const dak_launch_cfg* cfg, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Streaming-read probes (roofline bandwidths and the congestion sweep)        */
+/* ------------------------------------------------------------------------ */
+
+/* Streams `bytes` (a multiple of 16, >= 16) from `buf` (device memory or
+ * pinned host memory) with `workgroups` work-groups of 256 lanes, each lane
+ * keeping `window` 16-byte loads in flight (1, 2, 4, 8 or 16).  Runs one
+ * warm-up and `reps` (>= 1) timed launches on `stream`, synchronizing, and
+ * writes the median duration in milliseconds to *ms_out.
+ * DAK paper §4.3.1 (Fig. 7 microbenchmark). */
+dak_status dak_probe_read(const void* buf, size_t bytes, int32_t workgroups, int32_t window,
+                          int32_t reps, void* stream, float* ms_out);
+
+/* One launch in which `host_wgs` work-groups stream `host_bytes` of pinned
+ * host memory while `hbm_wgs` work-groups stream `hbm_bytes` of device memory
+ * (each role with its own window).  Per-role durations come from device
+ * timestamps (first start to last end of that role's work-groups), in ms.
+ * DAK paper §4.3.1, Fig. 7: host readers can slow down HBM readers. */
+dak_status dak_probe_read_concurrent(const void* hbm, size_t hbm_bytes, int32_t hbm_wgs,
+                                     int32_t hbm_window, const void* host, size_t host_bytes,
+                                     int32_t host_wgs, int32_t host_window, void* stream,
+                                     float* ms_total, float* ms_hbm, float* ms_host);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAK_H */

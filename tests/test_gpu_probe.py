@@ -1,0 +1,39 @@
+"""Streaming-read probes on the GPU: plausible bandwidths for both tiers and
+the concurrent (host + HBM) launch.  DAK paper §4.3.1, Fig. 7."""
+import pytest
+import torch
+
+import tiered_memory_offloading_amd as dak
+
+pytestmark = pytest.mark.gpu
+
+
+def test_probes_report_plausible_bandwidths():
+    assert torch.cuda.is_available()
+    g = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    ms = dak.probe_read(g, 1024, 1, reps=3)
+    bw_g = g.numel() / ms / 1e6
+    ms = dak.probe_read(h, 16, 4, reps=3)
+    bw_h = h.numel() / ms / 1e6
+    print(f"HBM {bw_g:.0f} GB/s, host {bw_h:.1f} GB/s")
+    assert 1000 < bw_g < 9000
+    assert 5 < bw_h < 80
+    t, mg, mh = dak.probe_read_concurrent(g, 1024, 4, h, 16, 4)
+    print(f"concurrent: total {t:.3f} ms, hbm {mg:.3f} ms, host {mh:.3f} ms")
+    assert 0 < mg <= t * 1.05 and 0 < mh <= t * 1.05
+
+
+def test_probe_argument_errors():
+    g = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dak.DakError):
+        dak.probe_read(g, 1, 3)
+    with pytest.raises(dak.DakError):
+        dak.probe_read(g, 0, 1)
+    # the library sees allocations, not tensors: torch carves small tensors out
+    # of larger segments, so overrun the whole segment
+    with pytest.raises(dak.DakError):
+        dak.probe_read(g, 1, 1, nbytes=1 << 30)
+    cpu = torch.empty(4096, dtype=torch.uint8)   # pageable
+    with pytest.raises(dak.DakError):
+        dak.probe_read(cpu, 1, 1)

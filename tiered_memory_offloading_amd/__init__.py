@@ -1,0 +1,282 @@
+"""Direct-access split operators over pinned host memory and HBM on MI355X.
+
+Python binding of libdak.so (include/dak.h).  Every step of the split operators
+runs in the library's HIP kernels; this module only marshals arguments and uses
+PyTorch to allocate device and pinned host memory and to name streams.
+
+Entry points (same names as the C ABI, without the ``dak_`` prefix):
+  min_offload_ratio, plan_offload, op_turning_points, host_workgroups,
+  splitk_gemm, decode_attn_workspace_bytes, splitk_decode_attn,
+  probe_read, probe_read_concurrent.
+Placement (DAK paper §4.1 "Data Partition"; §5 batch split of the KV cache):
+  place_matrix, place_kv.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "DakError", "LaunchConfig", "SplitMatrix", "SplitKV", "Op",
+    "min_offload_ratio", "plan_offload", "op_turning_points", "host_workgroups",
+    "place_matrix", "place_kv", "splitk_gemm", "decode_attn_workspace_bytes",
+    "splitk_decode_attn", "probe_read", "probe_read_concurrent", "library",
+]
+
+
+class DakError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"dak status {status}: {message}")
+        self.status = status
+
+
+def library() -> C.CDLL:
+    return L.load()
+
+
+def _check(status: int) -> None:
+    if status != L.DAK_OK:
+        lib = library()
+        raise DakError(status, lib.dak_last_error().decode(errors="replace"))
+
+
+def _stream_handle(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+# ----------------------------------------------------------------------------
+# Planning (CPU)
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Op:
+    units: int
+    unit_bytes: int
+    t_comp_s: float = 0.0
+
+
+def min_offload_ratio(footprint_bytes: int, hbm_bytes: int) -> float:
+    return library().dak_min_offload_ratio(int(footprint_bytes), int(hbm_bytes))
+
+
+def plan_offload(ops: Sequence[Op], b_hbm: float, b_host: float, x_global: float):
+    """(host units per op, modelled time in seconds)."""
+    lib = library()
+    arr = (L.OpDesc * len(ops))(*[L.OpDesc(o.units, o.unit_bytes, o.t_comp_s) for o in ops])
+    out = (C.c_uint64 * len(ops))()
+    t = C.c_double()
+    _check(lib.dak_plan_offload(arr, len(ops), float(b_hbm), float(b_host), float(x_global), out, C.byref(t)))
+    return [int(v) for v in out], t.value
+
+
+def op_turning_points(op: Op, b_hbm: float, b_host: float):
+    """(a, b, memory_bound) of one op."""
+    lib = library()
+    d = L.OpDesc(op.units, op.unit_bytes, op.t_comp_s)
+    a, b, mb = C.c_uint64(), C.c_uint64(), C.c_int32()
+    _check(lib.dak_op_turning_points(C.byref(d), float(b_hbm), float(b_host), C.byref(a), C.byref(b), C.byref(mb)))
+    return a.value, b.value, bool(mb.value)
+
+
+def host_workgroups(items: int, cap: int) -> int:
+    return library().dak_host_workgroups(int(items), int(cap))
+
+
+# ----------------------------------------------------------------------------
+# Launch configuration
+# ----------------------------------------------------------------------------
+@dataclass
+class LaunchConfig:
+    host_cus: int = 0              # 0 = library default
+    window: int = 0                # 0 = library default
+    byte_counters: Optional[torch.Tensor] = None   # int64 [2] on the GPU: host, HBM bytes loaded
+
+    def as_c(self) -> L.LaunchCfg:
+        flags = 0
+        ptr = None
+        if self.byte_counters is not None:
+            t = self.byte_counters
+            if t.dtype != torch.int64 or t.numel() < 2 or not t.is_cuda:
+                raise ValueError("byte_counters must be an int64 CUDA tensor of 2 elements")
+            flags |= L.DAK_FLAG_COUNT_BYTES
+            ptr = t.data_ptr()
+        return L.LaunchCfg(int(self.host_cus), int(self.window), flags, 0, ptr)
+
+
+def _cfg_ptr(cfg: Optional[LaunchConfig]):
+    if cfg is None:
+        return None, None
+    c = cfg.as_c()
+    return c, C.byref(c)
+
+
+# ----------------------------------------------------------------------------
+# Placement (tile-rows and requests across the two tiers)
+# ----------------------------------------------------------------------------
+@dataclass
+class SplitMatrix:
+    """A [M, K] bf16 weight matrix whose first h tile-rows (of m rows) live in
+    pinned host memory and the rest in HBM."""
+    host: Optional[torch.Tensor]   # [h*m, K] bf16, pinned CPU
+    hbm: Optional[torch.Tensor]    # [M - h*m, K] bf16, CUDA
+    M: int
+    K: int
+    m: int
+    h: int
+
+    def desc(self) -> L.SplitMatrixDesc:
+        hp = self.host.data_ptr() if self.host is not None and self.host.numel() else None
+        gp = self.hbm.data_ptr() if self.hbm is not None and self.hbm.numel() else None
+        return L.SplitMatrixDesc(hp, gp, self.M, self.K, self.m, 0, self.h)
+
+    @property
+    def host_bytes(self) -> int:
+        return self.h * self.m * self.K * 2
+
+
+def _pinned_like(n_rows: int, K: int) -> torch.Tensor:
+    return torch.empty((n_rows, K), dtype=torch.bfloat16, pin_memory=True)
+
+
+def place_matrix(A: torch.Tensor, m: int, h: int, device=None) -> SplitMatrix:
+    """Copy tile-rows [0, h) of A into pinned host memory and the rest into HBM."""
+    if A.dtype != torch.bfloat16 or A.dim() != 2:
+        raise ValueError("A must be a 2-D bf16 tensor")
+    M, K = A.shape
+    if M % m or not (0 <= h <= M // m):
+        raise ValueError("M must be a multiple of m and 0 <= h <= M/m")
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    rows = h * m
+    host = None
+    if rows:
+        host = _pinned_like(rows, K)
+        host.copy_(A[:rows])
+    hbm = None
+    if rows < M:
+        hbm = A[rows:].to(device, copy=True).contiguous()
+    return SplitMatrix(host, hbm, M, K, m, h)
+
+
+@dataclass
+class SplitKV:
+    """KV caches of `batch` requests; requests [0, h) in pinned host memory."""
+    k_host: Optional[torch.Tensor]   # [h, Hkv, ctx, D] bf16 pinned
+    v_host: Optional[torch.Tensor]
+    k_hbm: Optional[torch.Tensor]    # [batch - h, Hkv, ctx, D] bf16 CUDA
+    v_hbm: Optional[torch.Tensor]
+    batch: int
+    h: int
+    n_kv_heads: int
+    head_dim: int
+    ctx: int
+
+    def desc(self) -> L.SplitKVDesc:
+        def p(t):
+            return t.data_ptr() if t is not None and t.numel() else None
+        return L.SplitKVDesc(p(self.k_host), p(self.v_host), p(self.k_hbm), p(self.v_hbm), self.batch, self.h,
+                             self.n_kv_heads, self.head_dim, self.ctx)
+
+    @property
+    def host_bytes(self) -> int:
+        return 2 * self.h * self.n_kv_heads * self.ctx * self.head_dim * 2
+
+
+def place_kv(K: torch.Tensor, V: torch.Tensor, h: int, device=None) -> SplitKV:
+    """Copy requests [0, h) of K, V [B, Hkv, ctx, D] into pinned host memory, the rest into HBM."""
+    if K.shape != V.shape or K.dim() != 4 or K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise ValueError("K and V must be bf16 tensors of equal shape [B, Hkv, ctx, D]")
+    B, Hkv, ctx, D = K.shape
+    if not 0 <= h <= B:
+        raise ValueError("0 <= h <= batch")
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    kh = vh = kg = vg = None
+    if h:
+        kh = torch.empty((h, Hkv, ctx, D), dtype=torch.bfloat16, pin_memory=True)
+        vh = torch.empty((h, Hkv, ctx, D), dtype=torch.bfloat16, pin_memory=True)
+        kh.copy_(K[:h])
+        vh.copy_(V[:h])
+    if h < B:
+        kg = K[h:].to(device, copy=True).contiguous()
+        vg = V[h:].to(device, copy=True).contiguous()
+    return SplitKV(kh, vh, kg, vg, B, h, Hkv, D, ctx)
+
+
+# ----------------------------------------------------------------------------
+# Compute entry points
+# ----------------------------------------------------------------------------
+def splitk_gemm(A: SplitMatrix, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
+    """y[n, r] = sum_k A[r, k] x[n, k]; x bf16 [N, K] on the GPU, y fp32 [N, M]."""
+    lib = library()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
+    N = x.shape[0]
+    if y is None:
+        y = torch.empty((N, A.M), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (N, A.M):
+        raise ValueError("y must be a contiguous fp32 [N, M] tensor")
+    d = A.desc()
+    c, cp = _cfg_ptr(cfg)
+    _check(lib.dak_splitk_gemm(C.byref(d), x.data_ptr(), N, y.data_ptr(), cp, _stream_handle(stream)))
+    return y
+
+
+def decode_attn_workspace_bytes(kv: SplitKV, n_q_heads: int) -> int:
+    d = kv.desc()
+    return int(library().dak_decode_attn_workspace_bytes(C.byref(d), int(n_q_heads)))
+
+
+def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, cfg: Optional[LaunchConfig] = None,
+                       stream=None) -> torch.Tensor:
+    """out [B, Hq, D] fp32 from q bf16 [B, Hq, D] on the GPU."""
+    lib = library()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 CUDA tensor [B, Hq, D]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = decode_attn_workspace_bytes(kv, Hq)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    d = kv.desc()
+    c, cp = _cfg_ptr(cfg)
+    _check(lib.dak_splitk_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
+                                      ws.data_ptr(), ws.numel() * ws.element_size(), cp, _stream_handle(stream)))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Probes
+# ----------------------------------------------------------------------------
+def probe_read(buf: torch.Tensor, workgroups: int, window: int, reps: int = 5, nbytes: Optional[int] = None,
+               stream=None) -> float:
+    """Median milliseconds to stream `nbytes` (default: all of buf)."""
+    lib = library()
+    nb = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    ms = C.c_float()
+    _check(lib.dak_probe_read(buf.data_ptr(), nb, int(workgroups), int(window), int(reps), _stream_handle(stream),
+                              C.byref(ms)))
+    return ms.value
+
+
+def probe_read_concurrent(hbm: torch.Tensor, hbm_wgs: int, hbm_window: int, host: torch.Tensor, host_wgs: int,
+                          host_window: int, hbm_bytes: Optional[int] = None, host_bytes: Optional[int] = None,
+                          stream=None):
+    """(ms total, ms of the HBM role, ms of the host role) of one concurrent launch."""
+    lib = library()
+    gb = hbm.numel() * hbm.element_size() if hbm_bytes is None else int(hbm_bytes)
+    hb = host.numel() * host.element_size() if host_bytes is None else int(host_bytes)
+    t, g, h = C.c_float(), C.c_float(), C.c_float()
+    _check(lib.dak_probe_read_concurrent(hbm.data_ptr(), gb, int(hbm_wgs), int(hbm_window), host.data_ptr(), hb,
+                                         int(host_wgs), int(host_window), _stream_handle(stream), C.byref(t),
+                                         C.byref(g), C.byref(h)))
+    return t.value, g.value, h.value

@@ -1,0 +1,53 @@
+// Host-side runtime helpers of libdak that need the HIP runtime: validation of
+// caller pointers against the tier they are declared to live in.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+
+namespace dak {
+
+dak_status check_tier_ptr(const void* p, uint64_t bytes, Tier tier, const char* name, const void** dev) {
+  if (!p) return fail(DAK_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DAK_EINVAL, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the query's failure is not a launch error; clear it
+    return fail(DAK_EINVAL, "%s is not a pinned host or device allocation (hipPointerGetAttributes: %d)",
+                name, (int)e);
+  }
+  if (tier == Tier::kHost) {
+    if (attr.type != hipMemoryTypeHost)
+      return fail(DAK_EINVAL, "%s must be pinned host memory (memory type %d)", name, (int)attr.type);
+  } else {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail_hip((int)e, "hipGetDevice");
+    if (attr.type != hipMemoryTypeDevice || attr.device != cur)
+      return fail(DAK_EINVAL, "%s must be device memory on device %d (type %d, device %d)", name, cur,
+                  (int)attr.type, attr.device);
+  }
+  // Whole range inside the allocation that holds p.
+  hipDeviceptr_t start = nullptr;
+  size_t size = 0;
+  hipError_t e1 = hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, (hipDeviceptr_t)p);
+  hipError_t e2 = hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, (hipDeviceptr_t)p);
+  if (e1 != hipSuccess || e2 != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DAK_EINVAL, "%s: allocation range query failed (%d, %d)", name, (int)e1, (int)e2);
+  }
+  const uintptr_t s = reinterpret_cast<uintptr_t>(start), q = reinterpret_cast<uintptr_t>(p);
+  if (q < s || q - s > size || bytes > size - (q - s))
+    return fail(DAK_EINVAL, "%s: %llu bytes at offset %llu overrun its %llu-byte allocation", name,
+                (unsigned long long)bytes, (unsigned long long)(q - s), (unsigned long long)size);
+  if (tier == Tier::kHost && attr.devicePointer != attr.hostPointer) {
+    // Pinned host memory is mapped into the GPU's address space at the same
+    // virtual address; kernels dereference the caller's pointer as is.  Any
+    // other mapping is refused rather than translated.
+    return fail(DAK_EUNSUPPORTED, "%s: pinned memory is not mapped at its host address on the GPU", name);
+  }
+  *dev = p;
+  return DAK_OK;
+}
+
+}  // namespace dak

@@ -1,0 +1,417 @@
+// Split decode attention: grouped-query flash-decode over a KV cache split
+// along the batch between pinned host memory and HBM.
+//
+// DAK paper §5 "Supporting FlashAttention": the KV cache of a subset of the
+// requests lives in host memory and the rest in HBM; every request attends
+// entirely within one tier, so attention stays exact.  The walkthrough's
+// attention paragraph notes the split avoids merging one sequence's softmax
+// across tiers.  §4.1: one data path per compute unit; §4.3.1: the host role is
+// capped in work-groups and in-flight loads.
+//
+// CDNA4 design:
+//   * partial kernel, one work item per (request b, KV head g, chunk of 1024
+//     tokens).  The item's K and V rows are read once, for all query heads of
+//     the group (G = Hq / Hkv), so grouped heads never re-read KV;
+//   * wave w of the work-group walks tokens [256 w, 256 w + 256) of the chunk
+//     in tiles of 16 tokens.  Each tile is 4 fully coalesced 1 KiB loads of K
+//     and 4 of V: load i covers tokens t0 + 4 i + lane/16, dims 8 (lane % 16)..+7;
+//   * q . K is an fp32 dot over the lane's 8 dims, summed over the 16 lanes of
+//     a DPP row; scores carry scale * log2(e) so exp2 gives the softmax weights;
+//   * online softmax state (m, l, o) per lane group, merged across the four
+//     lane groups, then across the four waves in order, then written as the
+//     chunk's partial (m, l, o);
+//   * a combine kernel merges the chunks of each (b, head) in chunk order.
+// Work-groups [0, G_h) read host requests (static stride), the rest read HBM
+// requests, one item each.  Both roles run identical arithmetic, so results
+// are bit-identical whatever the number of host requests.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device_common.hpp"
+
+namespace dak {
+namespace {
+
+constexpr int kD = 128;                 // head_dim handled by this build
+constexpr int kChunk = 1024;            // tokens per work item
+constexpr int kAttnWaves = 4;
+constexpr int kWaveTokens = kChunk / kAttnWaves;
+constexpr int kTile = 16;               // tokens per tile (4 loads of K + 4 of V per lane)
+constexpr float kNegInf = -INFINITY;
+
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Merge softmax state (m2, l2, o2) into (m, l, o).
+template <int G>
+__device__ __forceinline__ void merge_state(float (&m)[G], float (&l)[G], float (&o)[G][8], const float (&m2)[G],
+                                            const float (&l2)[G], const float (&o2)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mn = fmaxf(m[h], m2[h]);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float a1 = exp2_fast(m[h] - ms), a2 = exp2_fast(m2[h] - ms);
+    const float t1 = l[h] * a1, t2 = l2[h] * a2;
+    l[h] = t1 + t2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float u1 = o[h][e] * a1, u2 = o2[h][e] * a2;
+      o[h][e] = u1 + u2;
+    }
+    m[h] = mn;
+  }
+}
+
+// Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the lane
+// group's online-softmax state.
+template <int G, int U, bool COUNT>
+__device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, const uint16_t* __restrict__ Vbg,
+                                            int64_t tb, int64_t te, const float (&qf)[G][8], float (&m)[G],
+                                            float (&l)[G], float (&o)[G][8], int lane, uint64_t& nbytes) {
+  const int grp = lane >> 4;
+  const int dq = (lane & 15) * 8;
+  const int64_t ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
+  for (int64_t t0 = 0; t0 < ntiles; t0 += U) {
+    uint4 kv[U][4], vv[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + (t0 + u) * kTile + 4 * i + grp;
+        const bool ok = (t0 + u < ntiles) && (t < te);
+        kv[u][i] = ok ? ld16(Kbg + t * kD + dq) : make_uint4(0, 0, 0, 0);
+        vv[u][i] = ok ? ld16(Vbg + t * kD + dq) : make_uint4(0, 0, 0, 0);
+        if (COUNT && ok) nbytes += 32;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u >= ntiles) break;   // uniform
+      float s[4][G];
+      float vf[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + (t0 + u) * kTile + 4 * i + grp;
+        const uint32_t kw[4] = {kv[u][i].x, kv[u][i].y, kv[u][i].z, kv[u][i].w};
+        const uint32_t vw[4] = {vv[u][i].x, vv[u][i].y, vv[u][i].z, vv[u][i].w};
+        float kf[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          kf[2 * q] = bf_lo(kw[q]);
+          kf[2 * q + 1] = bf_hi(kw[q]);
+          vf[i][2 * q] = bf_lo(vw[q]);
+          vf[i][2 * q + 1] = bf_hi(vw[q]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p = __builtin_fmaf(qf[h][e], kf[e], p);
+          p = row16_sum(p);
+          s[i][h] = (t < te) ? p : kNegInf;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mt = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+        const float mn = fmaxf(m[h], mt);
+        const float ms = (mn == kNegInf) ? 0.f : mn;
+        const float alpha = exp2_fast(m[h] - ms);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i][h] - ms);
+        // l and o take the same sequence of operations (o with an fma per
+        // token), so o is exactly c * l whenever every V row equals a power of
+        // two c.
+        float ls = l[h] * alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ls = ls + p[i];
+        l[h] = ls;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = o[h][e] * alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(p[i], vf[i][e], acc);
+          o[h][e] = acc;
+        }
+        m[h] = mn;
+      }
+    }
+  }
+}
+
+// One (b, g, chunk) item: every wave walks its 256 tokens, then the states are
+// merged (lane groups, then waves in order) and the chunk partial is written.
+template <int G, int U, bool COUNT>
+__device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kbg,
+                                          const uint16_t* __restrict__ Vbg, int64_t b, int g, int c, int64_t ctx,
+                                          int Hq, int C, float qscale, float* __restrict__ o_ws,
+                                          float* __restrict__ ml_ws, float* red_o, float* red_ml, int wave,
+                                          int lane, uint64_t& nbytes) {
+  const int dq = (lane & 15) * 8;
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 qv = ld16(q + ((b * Hq) + g * G + h) * kD + dq);
+    const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qf[h][2 * k] = bf_lo(w[k]) * qscale;
+      qf[h][2 * k + 1] = bf_hi(w[k]) * qscale;
+    }
+  }
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+  const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
+  const int64_t te = tb + kWaveTokens < ctx ? tb + kWaveTokens : ctx;
+  attn_tokens<G, U, COUNT>(Kbg, Vbg, tb, te, qf, m, l, o, lane, nbytes);
+
+  // Merge the four lane groups (xor 16, then xor 32).
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    float m2[G], l2[G], o2[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m2[h] = __shfl_xor(m[h], off, 64);
+      l2[h] = __shfl_xor(l[h], off, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[h][e] = __shfl_xor(o[h][e], off, 64);
+    }
+    merge_state<G>(m, l, o, m2, l2, o2);
+  }
+  // Lanes 0..15 hold the wave's state for dims 8*lane .. +7.
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[(wave * G + h) * kD + dq + e] = o[h][e];
+  }
+  if (lane < G) {
+    red_ml[(wave * G + lane) * 2 + 0] = m[lane];
+    red_ml[(wave * G + lane) * 2 + 1] = l[lane];
+  }
+  __syncthreads();
+  // Waves merged in order 0, 1, 2, 3; thread t handles (head, dim) pairs.
+  for (int idx = threadIdx.x; idx < G * kD; idx += kAttnWaves * 64) {
+    const int h = idx / kD, d = idx % kD;
+    float mm = red_ml[(0 * G + h) * 2 + 0], ll = red_ml[(0 * G + h) * 2 + 1];
+    float oo = red_o[(0 * G + h) * kD + d];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) {
+      const float m2 = red_ml[(w * G + h) * 2 + 0], l2 = red_ml[(w * G + h) * 2 + 1];
+      const float o2 = red_o[(w * G + h) * kD + d];
+      const float mn = fmaxf(mm, m2);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float a1 = exp2_fast(mm - ms), a2 = exp2_fast(m2 - ms);
+      const float t1 = ll * a1, t2 = l2 * a2;
+      ll = t1 + t2;
+      const float u1 = oo * a1, u2 = o2 * a2;
+      oo = u1 + u2;
+      mm = mn;
+    }
+    const int64_t rec = ((b * Hq) + g * G + h) * C + c;
+    o_ws[rec * kD + d] = oo;
+    if (d == 0) {
+      ml_ws[rec * 2 + 0] = mm;
+      ml_ws[rec * 2 + 1] = ll;
+    }
+  }
+  __syncthreads();   // LDS reused by the next item
+}
+
+template <int G, int UH, int UG, bool COUNT>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_host, const uint16_t* __restrict__ v_host,
+    const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t h_req, int Hkv, int Hq,
+    int64_t ctx, int C, float qscale, float* __restrict__ o_ws, float* __restrict__ ml_ws, int host_wgs,
+    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+  __shared__ float red_o[kAttnWaves * G * kD];
+  __shared__ float red_ml[kAttnWaves * G * 2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t nbytes = 0;
+  const bool host_role = (int)blockIdx.x < host_wgs;
+  const int64_t per_req = (int64_t)Hkv * C;
+  if (host_role) {
+    for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
+      const int64_t bl = it / per_req;
+      const int g = (int)((it / C) % Hkv), c = (int)(it % C);
+      const int64_t off = (bl * Hkv + g) * ctx * kD;
+      attn_item<G, UH, COUNT>(q, k_host + off, v_host + off, bl, g, c, ctx, Hq, C, qscale, o_ws, ml_ws, red_o,
+                              red_ml, wave, lane, nbytes);
+    }
+  } else {
+    const int64_t it = (int64_t)blockIdx.x - host_wgs;
+    if (it < hbm_items) {
+      const int64_t bl = it / per_req;
+      const int g = (int)((it / C) % Hkv), c = (int)(it % C);
+      const int64_t off = (bl * Hkv + g) * ctx * kD;
+      attn_item<G, UG, COUNT>(q, k_hbm + off, v_hbm + off, h_req + bl, g, c, ctx, Hq, C, qscale, o_ws, ml_ws,
+                              red_o, red_ml, wave, lane, nbytes);
+    }
+  }
+  if (COUNT) {
+    uint64_t v = nbytes;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&counters[host_role ? 0 : 1], (unsigned long long)v);
+  }
+}
+
+// out[row, :] = merge of the C chunk partials of row = b * Hq + j, in chunk order.
+__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ o_ws, const float* __restrict__ ml_ws,
+                                                   int C, float* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* ml = ml_ws + row * C * 2;
+  const float* ow = o_ws + row * C * kD;
+  float M = kNegInf;
+  for (int c = 0; c < C; ++c) M = fmaxf(M, ml[c * 2]);
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, O0 = 0.f, O1 = 0.f;
+  for (int c = 0; c < C; ++c) {
+    const float w = exp2_fast(ml[c * 2] - Ms);
+    const float lw = ml[c * 2 + 1] * w;
+    L = L + lw;
+    const float2 ov = *reinterpret_cast<const float2*>(ow + c * kD + 2 * lane);
+    const float a = ov.x * w, b = ov.y * w;
+    O0 = O0 + a;
+    O1 = O1 + b;
+  }
+  *reinterpret_cast<float2*>(out + row * kD + 2 * lane) = make_float2(O0 / L, O1 / L);
+}
+
+struct AttnArgs {
+  const uint16_t *q, *k_host, *v_host, *k_hbm, *v_hbm;
+  int64_t batch, h_req;
+  int Hkv, Hq;
+  int64_t ctx;
+  int C;
+  float qscale;
+  float *o_ws, *ml_ws, *out;
+  int host_wgs;
+  int64_t host_items, hbm_items;
+  unsigned long long* counters;
+  hipStream_t stream;
+};
+
+template <int G, int UH, bool COUNT>
+void launch_partial_g(const AttnArgs& a) {
+  constexpr int UG = G >= 8 ? 1 : 2;
+  constexpr int UHc = G >= 8 ? 1 : (G >= 4 && UH > 2 ? 2 : UH);
+  const int64_t grid = a.host_wgs + a.hbm_items;
+  hipLaunchKernelGGL((attn_partial_split<G, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0,
+                     a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_req, a.Hkv, a.Hq, a.ctx, a.C,
+                     a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
+}
+
+template <int UH, bool COUNT>
+void launch_partial(const AttnArgs& a, int G) {
+  switch (G) {
+    case 1: return launch_partial_g<1, UH, COUNT>(a);
+    case 2: return launch_partial_g<2, UH, COUNT>(a);
+    case 4: return launch_partial_g<4, UH, COUNT>(a);
+    default: return launch_partial_g<8, UH, COUNT>(a);
+  }
+}
+
+template <bool COUNT>
+void launch_partial_w(const AttnArgs& a, int G, int window) {
+  switch (window) {
+    case 1: return launch_partial<1, COUNT>(a, G);
+    case 2: return launch_partial<2, COUNT>(a, G);
+    case 8: return launch_partial<8, COUNT>(a, G);
+    default: return launch_partial<4, COUNT>(a, G);
+  }
+}
+
+bool attn_shapes_ok(const dak_split_kv* kv, int32_t n_q_heads) {
+  return kv && kv->batch >= 1 && kv->h >= 0 && kv->h <= kv->batch && kv->n_kv_heads >= 1 && kv->ctx >= 1 &&
+         n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0 && kv->head_dim == kD &&
+         kv->batch <= (int64_t(1) << 24) && kv->ctx <= (int64_t(1) << 31) && n_q_heads <= 4096;
+}
+
+}  // namespace
+}  // namespace dak
+
+extern "C" size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads) {
+  using namespace dak;
+  if (!attn_shapes_ok(kv, n_q_heads)) return 0;
+  const int64_t C = (kv->ctx + kChunk - 1) / kChunk;
+  return (size_t)(kv->batch * n_q_heads * C) * (kD + 2) * sizeof(float);
+}
+
+extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads, float scale,
+                                             float* out, void* ws, size_t ws_bytes, const dak_launch_cfg* cfg,
+                                             void* stream) {
+  using namespace dak;
+  clear_error();
+  if (!kv) return fail(DAK_EINVAL, "kv is NULL");
+  if (kv->head_dim != kD) return fail(DAK_EUNSUPPORTED, "head_dim %d (only 128 is built)", kv->head_dim);
+  if (!attn_shapes_ok(kv, n_q_heads))
+    return fail(DAK_EINVAL, "bad shapes: batch=%lld h=%lld Hkv=%d Hq=%d ctx=%lld", (long long)kv->batch,
+                (long long)kv->h, kv->n_kv_heads, n_q_heads, (long long)kv->ctx);
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(DAK_EUNSUPPORTED, "group size %d is not 1, 2, 4 or 8", G);
+  if (!std::isfinite(scale)) return fail(DAK_EINVAL, "scale must be finite");
+  LaunchCfg lc;
+  dak_status st = resolve_cfg(cfg, &lc);
+  if (st) return st;
+  const size_t need = dak_decode_attn_workspace_bytes(kv, n_q_heads);
+  if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+
+  const int64_t B = kv->batch, h = kv->h, Hkv = kv->n_kv_heads, ctx = kv->ctx;
+  const uint64_t per_req = (uint64_t)Hkv * ctx * kD * 2;
+  const void *dq = nullptr, *dkh = nullptr, *dvh = nullptr, *dkg = nullptr, *dvg = nullptr, *dout = nullptr,
+             *dws = nullptr;
+  if ((st = check_tier_ptr(q, (uint64_t)B * n_q_heads * kD * 2, Tier::kDevice, "q", &dq))) return st;
+  if (h > 0) {
+    if ((st = check_tier_ptr(kv->k_host, per_req * h, Tier::kHost, "k_host", &dkh))) return st;
+    if ((st = check_tier_ptr(kv->v_host, per_req * h, Tier::kHost, "v_host", &dvh))) return st;
+  }
+  if (h < B) {
+    if ((st = check_tier_ptr(kv->k_hbm, per_req * (B - h), Tier::kDevice, "k_hbm", &dkg))) return st;
+    if ((st = check_tier_ptr(kv->v_hbm, per_req * (B - h), Tier::kDevice, "v_hbm", &dvg))) return st;
+  }
+  if ((st = check_tier_ptr(out, (uint64_t)B * n_q_heads * kD * 4, Tier::kDevice, "out", &dout))) return st;
+  if ((st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws))) return st;
+
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(dq);
+  a.k_host = static_cast<const uint16_t*>(dkh);
+  a.v_host = static_cast<const uint16_t*>(dvh);
+  a.k_hbm = static_cast<const uint16_t*>(dkg);
+  a.v_hbm = static_cast<const uint16_t*>(dvg);
+  a.batch = B;
+  a.h_req = h;
+  a.Hkv = (int)Hkv;
+  a.Hq = n_q_heads;
+  a.ctx = ctx;
+  a.C = (int)((ctx + kChunk - 1) / kChunk);
+  a.qscale = scale * 1.4426950408889634f;   // scores in log2 units: exp2 gives e^(scale * q.k)
+  a.o_ws = static_cast<float*>(ws);
+  a.ml_ws = a.o_ws + (size_t)B * n_q_heads * a.C * kD;
+  a.out = out;
+  a.host_items = h * Hkv * a.C;
+  a.hbm_items = (B - h) * Hkv * a.C;
+  a.host_wgs = (int)host_workgroups(a.host_items, lc.host_cus);
+  a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+  a.stream = static_cast<hipStream_t>(stream);
+  if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
+  if (lc.flags & DAK_FLAG_COUNT_BYTES)
+    launch_partial_w<true>(a, G, lc.window);
+  else
+    launch_partial_w<false>(a, G, lc.window);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(64), 0, a.stream, a.o_ws, a.ml_ws, a.C,
+                     out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");
+  return DAK_OK;
+}

@@ -1,0 +1,324 @@
+"""Benchmark of the direct-access split operators on one MI355X.
+
+A step is the split-operator work of one Llama-8B-shaped decoder layer at
+batch 16: the QKV (6144x4096), O (4096x4096), gate+up (28672x4096) and down
+(4096x14336) split GEMMs with N = 16 activations, and split-KV grouped-query
+decode attention over 16 requests x 32768 tokens (32 query heads on 8 KV heads,
+head_dim 128).  A fraction x of every weight matrix's 64-row tile-rows and of
+the requests' KV caches lives in pinned host memory and is read in place by the
+kernels; the rest is in HBM.  The headline is x = 0.25.
+
+Metric: effective bandwidth = bytes of weights and KV touched (both tiers, each
+byte once) / step time, and its fraction of the two-tier roofline
+max((1 - x) C / B_hbm, x C / B_host) summed over the ops, with B_hbm and B_host
+measured by the library's streaming-read probes in the same run.
+
+Inputs are seeded synthetic tensors drawn with the recipe of synth.py (std
+0.02 weights, std 1 activations and KV), generated on the GPU.  Weights and KV
+are held in both tiers, so every ratio of the sweep is a different descriptor
+over the same buffers.
+
+Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+M_TILE = 64
+BATCH = 16
+HQ, HKV, HD, CTX = 32, 8, 128, 32768
+PCIE_GEN5_X16_GBPS = 64.0      # published per-direction host link peak
+HBM_PEAK_GBPS = 8000.0         # published MI355X HBM3E peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def host_units(k, den, n):
+    return -(-k * n // den)
+
+
+class Workload:
+    """Weights and KV in both tiers, plus outputs and workspace."""
+
+    def __init__(self, torch, dak, seed=0):
+        self.torch, self.dak = torch, dak
+        dev = torch.device("cuda")
+        self.lin = []
+        for i, (name, M, K) in enumerate(synth.LLAMA8B_LINEARS):
+            A, X = synth.gemm_inputs(M, K, BATCH, seed=seed + i, device="cuda")
+            A_host = torch.empty((M, K), dtype=torch.bfloat16, pin_memory=True)
+            A_host.copy_(A)
+            y = torch.empty((BATCH, M), dtype=torch.float32, device=dev)
+            self.lin.append(dict(name=name, M=M, K=K, A_dev=A, A_host=A_host, x=X.contiguous(), y=y))
+        q, K, V = synth.attn_inputs(BATCH, HQ, HKV, HD, CTX, seed=seed + 10, device="cuda")
+        self.q, self.K_dev, self.V_dev = q, K, V
+        self.K_host = torch.empty(K.shape, dtype=torch.bfloat16, pin_memory=True)
+        self.V_host = torch.empty(V.shape, dtype=torch.bfloat16, pin_memory=True)
+        self.K_host.copy_(K)
+        self.V_host.copy_(V)
+        self.out = torch.empty((BATCH, HQ, HD), dtype=torch.float32, device=dev)
+        kv0 = self.kv_desc(0)
+        self.ws = torch.empty((dak.decode_attn_workspace_bytes(kv0, HQ),), dtype=torch.uint8, device=dev)
+        self.scale = 1.0 / math.sqrt(HD)
+        torch.cuda.synchronize()
+
+    def mat_desc(self, L, h):
+        rows = h * M_TILE
+        return self.dak.SplitMatrix(L["A_host"] if rows else None, L["A_dev"][rows:] if rows < L["M"] else None,
+                                    L["M"], L["K"], M_TILE, h)
+
+    def kv_desc(self, h):
+        d = self.dak
+        return d.SplitKV(self.K_host if h else None, self.V_host if h else None,
+                         self.K_dev[h:] if h < BATCH else None, self.V_dev[h:] if h < BATCH else None,
+                         BATCH, h, HKV, HD, CTX)
+
+    def plan(self, k, den=20):
+        """Descriptors for x = k/den (host units rounded up per op)."""
+        mats = [(L, self.mat_desc(L, host_units(k, den, L["M"] // M_TILE))) for L in self.lin]
+        kv = self.kv_desc(host_units(k, den, BATCH))
+        return mats, kv
+
+    def op_bytes(self):
+        """(name, total bytes C, units n) per op in step order."""
+        ops = []
+        for L in self.lin:
+            ops.append((L["name"], L["M"] * L["K"] * 2, L["M"] // M_TILE))
+        kvb = 2 * BATCH * HKV * CTX * HD * 2
+        # attention runs after QKV
+        return [ops[0], ("attn", kvb, BATCH)] + ops[1:]
+
+
+def run_step(wl, plan, cfg=None, events=None):
+    """One pass of the hot path: QKV, attention, O, gate+up, down."""
+    dak = wl.dak
+    mats, kv = plan
+    seq = [("gemm", mats[0]), ("attn", kv), ("gemm", mats[1]), ("gemm", mats[2]), ("gemm", mats[3])]
+    for i, (kind, obj) in enumerate(seq):
+        if events is not None:
+            events[i][0].record()
+        if kind == "gemm":
+            L, S = obj
+            dak.splitk_gemm(S, L["x"], y=L["y"], cfg=cfg)
+        else:
+            dak.splitk_decode_attn(wl.q, obj, wl.scale, out=wl.out, ws=wl.ws, cfg=cfg)
+        if events is not None:
+            events[i][1].record()
+
+
+def measure_bandwidths(torch, dak):
+    """B_hbm (4 GiB device buffer) and B_host (1 GiB pinned) from the probes, GB/s."""
+    g = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    best_g = 0.0
+    for wg, w in ((256, 8), (512, 4), (1024, 1), (2048, 1), (1024, 2)):
+        ms = dak.probe_read(g, wg, w, reps=5)
+        best_g = max(best_g, g.numel() / ms / 1e6)
+    del g
+    h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    best_h = 0.0
+    for wg, w in ((16, 4), (32, 4), (8, 8), (64, 2)):
+        ms = dak.probe_read(h, wg, w, reps=3)
+        best_h = max(best_h, h.numel() / ms / 1e6)
+    del h
+    torch.cuda.empty_cache()
+    return best_g, best_h
+
+
+def two_tier_roofline_ms(wl, k, den, b_hbm, b_host):
+    t = 0.0
+    for name, C, n in wl.op_bytes():
+        h = host_units(k, den, n)
+        x = h / n
+        t += max((1 - x) * C / (b_hbm * 1e9), x * C / (b_host * 1e9))
+    return t * 1e3
+
+
+def host_bytes(wl, k, den):
+    tot = 0
+    for name, C, n in wl.op_bytes():
+        tot += host_units(k, den, n) * (C // n)
+    return tot
+
+
+def time_steps(torch, wl, plan, steps, warmup, per_op=True):
+    for _ in range(warmup):
+        run_step(wl, plan)
+    torch.cuda.synchronize()
+    evs = None
+    if per_op:
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+               for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run_step(wl, plan, events=evs[s] if evs else None)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    op_ms = None
+    if evs:
+        op_ms = [statistics.mean(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) for i in range(5)]
+    return dt * 1e3, op_ms
+
+
+def cpu_baseline(seed=0):
+    """The oracle, as it stands, on a bounded sample of the step: the O linear
+    (4096x4096, N = 16) and two (request, KV head) attention pairs, timed on the
+    host CPU and scaled by bytes to the whole step."""
+    import numpy as np
+    import torch
+    from oracle import attention as oa
+    from oracle import gemm as og
+
+    t0 = time.perf_counter()
+    A, X = synth.gemm_inputs(4096, 4096, BATCH, seed=seed)
+    t_gen = time.perf_counter()
+    og.gemm(og.to_f64(A), og.to_f64(X))
+    t_lin = time.perf_counter() - t_gen
+    gen = torch.Generator().manual_seed(seed + 10)
+    pairs = 2
+    t_att = 0.0
+    for _ in range(pairs):
+        q = synth.normal_bf16((4, HD), 1.0, gen)
+        Kb = synth.normal_bf16((CTX, HD), 1.0, gen)
+        Vb = synth.normal_bf16((CTX, HD), 1.0, gen)
+        t1 = time.perf_counter()
+        qf, Kf, Vf = og.to_f64(q), og.to_f64(Kb), og.to_f64(Vb)
+        for j in range(4):
+            oa.attend_one(qf[j], Kf, Vf, 1.0 / math.sqrt(HD))
+        t_att += time.perf_counter() - t1
+    lin_bytes = sum(M * K * 2 for _, M, K in synth.LLAMA8B_LINEARS)
+    kv_bytes = 2 * BATCH * HKV * CTX * HD * 2
+    t_step = t_lin * lin_bytes / (4096 * 4096 * 2) + t_att / pairs * (BATCH * HKV)
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": round((lin_bytes + kv_bytes) / t_step / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: O linear 4096x4096 at N=16 ({t_lin:.2f} s) and {pairs} (request, kv-head) "
+                   f"attention pairs x 4 query heads over 32768 tokens ({t_att:.2f} s), scaled by bytes to one "
+                   f"step ({t_step:.1f} s per step); input generation excluded"),
+        "wall_s": round(time.perf_counter() - t0, 2),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--x-num", type=int, default=5, help="headline ratio numerator over 20 (5 -> 0.25)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=5)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no collectives or sharding); use --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import tiered_memory_offloading_amd as dak
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dak.library()
+
+    log("measuring B_hbm / B_host with the streaming-read probes")
+    b_hbm, b_host = measure_bandwidths(torch, dak)
+    log(f"B_hbm {b_hbm:.0f} GB/s, B_host {b_host:.2f} GB/s")
+    log("building the workload on the GPU")
+    wl = Workload(torch, dak)
+    ops = wl.op_bytes()
+    step_bytes = sum(C for _, C, _ in ops)
+    den = 20
+    k = args.x_num
+    plan = wl.plan(k, den)
+    log(f"timing {args.steps} steps at x = {k}/{den}")
+    ms, op_ms = time_steps(torch, wl, plan, args.steps, args.warmup)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    t_roof = two_tier_roofline_ms(wl, k, den, b_hbm, b_host)
+    names = [n for n, _, _ in ops]
+
+    # dominant kernel: the op with the largest measured time
+    i_dom = max(range(5), key=lambda i: op_ms[i])
+    dom_name, dom_C, dom_n = ops[i_dom]
+    dom_h = host_units(k, den, dom_n)
+    dom_host_bytes = dom_h * (dom_C // dom_n)
+    dom_ms = op_ms[i_dom]
+    if dom_h > 0:
+        ach = dom_host_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "host-link", "kernel": dom_name, "achieved": round(ach, 3), "peak": PCIE_GEN5_X16_GBPS,
+                "unit": "GB/s", "frac": round(ach / PCIE_GEN5_X16_GBPS, 4), "traffic": None,
+                "bytes_per_launch": dom_host_bytes, "ms_per_launch": round(dom_ms, 4),
+                "note": "host-tier bytes of the op (read once) / its average duration; peak = PCIe Gen5 x16 "
+                        "per-direction published rate"}
+    else:
+        ach = dom_C / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": dom_C,
+                "ms_per_launch": round(dom_ms, 4)}
+
+    result = {
+        "metric": "effective GB/s (HBM+host) and % of two-tier roofline vs offload ratio x",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU; Llama-8B shapes, random weights)",
+        "config": {"workload": "Llama-8B decode layer split operators, batch 16: QKV/O/gate+up/down split GEMMs "
+                               "(N=16, 64-row tile-rows) + split-KV GQA decode attention (32q/8kv heads, hd 128, "
+                               "32768 ctx/request)",
+                   "x": k / den, "global_batch": BATCH, "seq_len": CTX, "parallelism": "none (1 GPU)",
+                   "step_bytes": step_bytes, "host_bytes": host_bytes(wl, k, den)},
+        "two_tier": {"b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3),
+                     "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_host_GBps": PCIE_GEN5_X16_GBPS,
+                     "t_roof_ms": round(t_roof, 4), "frac": round(t_roof / ms, 4),
+                     "op_ms": {n: round(t, 4) for n, t in zip(names, op_ms)}},
+        "roofline": roof,
+    }
+
+    if not args.no_sweep:
+        sweep = []
+        for kk in range(0, 11):
+            p = wl.plan(kk, den)
+            sms, sop = time_steps(torch, wl, p, args.sweep_steps, 1)
+            tr = two_tier_roofline_ms(wl, kk, den, b_hbm, b_host)
+            sweep.append({"x": kk / den, "GBps": round(step_bytes / (sms * 1e-3) / 1e9, 2),
+                          "frac_two_tier": round(tr / sms, 4), "ms": round(sms, 4),
+                          "op_ms": [round(t, 4) for t in sop]})
+            log(f"sweep x={kk / den:.2f}: {sweep[-1]['GBps']} GB/s, {sweep[-1]['frac_two_tier']:.3f} of roofline")
+        result["sweep"] = sweep
+        x0 = sweep[0]
+        i0 = max(range(5), key=lambda i: x0["op_ms"][i])
+        ach0 = ops[i0][1] / (x0["op_ms"][i0] * 1e-3) / 1e9
+        result["roofline_x0"] = {"bound": "hbm", "kernel": ops[i0][0], "achieved": round(ach0, 1),
+                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach0 / HBM_PEAK_GBPS, 4),
+                                 "frac_of_measured_b_hbm": round(ach0 / b_hbm, 4)}
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

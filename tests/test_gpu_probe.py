@@ -37,3 +37,15 @@ def test_probe_argument_errors():
     cpu = torch.empty(4096, dtype=torch.uint8)   # pageable
     with pytest.raises(dak.DakError):
         dak.probe_read(cpu, 1, 1)
+
+
+def test_allocations_of_4_gib_and_more_validate():
+    # The range check must see the full size of large allocations (a 32-bit
+    # size would make a 4 GiB buffer look empty and a 5 GiB one look 1 GiB).
+    g = torch.empty((5 << 30) // 2, dtype=torch.bfloat16, device="cuda")
+    ms = dak.probe_read(g, 1024, 1, reps=1, nbytes=(5 << 30) - 4096)
+    assert ms > 0
+    h = torch.empty((5 << 30) // 2, dtype=torch.bfloat16, pin_memory=True)
+    ms = dak.probe_read(h, 16, 4, reps=1, nbytes=(5 << 30) - 4096)
+    assert ms > 0
+    del g, h

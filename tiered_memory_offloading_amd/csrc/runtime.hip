@@ -27,14 +27,15 @@ dak_status check_tier_ptr(const void* p, uint64_t bytes, Tier tier, const char* 
       return fail(DAK_EINVAL, "%s must be device memory on device %d (type %d, device %d)", name, cur,
                   (int)attr.type, attr.device);
   }
-  // Whole range inside the allocation that holds p.
+  // Whole range inside the allocation that holds p.  (The pointer-attribute
+  // range-size query returns only 32 bits, so allocations of 4 GiB and more
+  // would read as short; hipMemGetAddressRange reports the full size.)
   hipDeviceptr_t start = nullptr;
   size_t size = 0;
-  hipError_t e1 = hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, (hipDeviceptr_t)p);
-  hipError_t e2 = hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, (hipDeviceptr_t)p);
-  if (e1 != hipSuccess || e2 != hipSuccess) {
+  e = hipMemGetAddressRange(&start, &size, (hipDeviceptr_t)p);
+  if (e != hipSuccess) {
     (void)hipGetLastError();
-    return fail(DAK_EINVAL, "%s: allocation range query failed (%d, %d)", name, (int)e1, (int)e2);
+    return fail(DAK_EINVAL, "%s: allocation range query failed (%d)", name, (int)e);
   }
   const uintptr_t s = reinterpret_cast<uintptr_t>(start), q = reinterpret_cast<uintptr_t>(p);
   if (q < s || q - s > size || bytes > size - (q - s))

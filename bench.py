@@ -103,12 +103,17 @@ class Workload:
         return [ops[0], ("attn", kvb, BATCH)] + ops[1:]
 
 
-def run_step(wl, plan, cfg=None, events=None):
-    """One pass of the hot path: QKV, attention, O, gate+up, down."""
+OP_ORDER = ("qkv", "attn", "o", "gate_up", "down")
+
+
+def run_step(wl, plan, cfg=None, events=None, only=None):
+    """One pass of the hot path: QKV, attention, O, gate+up, down (or one of them)."""
     dak = wl.dak
     mats, kv = plan
     seq = [("gemm", mats[0]), ("attn", kv), ("gemm", mats[1]), ("gemm", mats[2]), ("gemm", mats[3])]
     for i, (kind, obj) in enumerate(seq):
+        if only is not None and OP_ORDER[i] != only:
+            continue
         if events is not None:
             events[i][0].record()
         if kind == "gemm":
@@ -154,9 +159,9 @@ def host_bytes(wl, k, den):
     return tot
 
 
-def time_steps(torch, wl, plan, steps, warmup, per_op=True):
+def time_steps(torch, wl, plan, steps, warmup, per_op=True, only=None):
     for _ in range(warmup):
-        run_step(wl, plan)
+        run_step(wl, plan, only=only)
     torch.cuda.synchronize()
     evs = None
     if per_op:
@@ -164,12 +169,15 @@ def time_steps(torch, wl, plan, steps, warmup, per_op=True):
                for _ in range(steps)]
     t0 = time.perf_counter()
     for s in range(steps):
-        run_step(wl, plan, events=evs[s] if evs else None)
+        run_step(wl, plan, events=evs[s] if evs else None, only=only)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
     op_ms = None
     if evs:
-        op_ms = [statistics.mean(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) for i in range(5)]
+        idx = range(5) if only is None else [OP_ORDER.index(only)]
+        op_ms = [0.0] * 5
+        for i in idx:
+            op_ms[i] = statistics.mean(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps))
     return dt * 1e3, op_ms
 
 
@@ -224,6 +232,8 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--only", choices=OP_ORDER, default=None,
+                    help="time one operator of the step (for profiling); the JSON then covers that op only")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no collectives or sharding); use --gpus 1",
@@ -246,6 +256,15 @@ def main(argv=None):
     k = args.x_num
     plan = wl.plan(k, den)
     log(f"timing {args.steps} steps at x = {k}/{den}")
+    if args.only is not None:
+        ms, op_ms = time_steps(torch, wl, plan, args.steps, args.warmup, only=args.only)
+        i = OP_ORDER.index(args.only)
+        name, C, n = ops[i]
+        h = host_units(k, den, n)
+        print(json.dumps({"only": name, "x": k / den, "ms_per_launch": op_ms[i], "bytes": C,
+                          "host_bytes": h * (C // n), "GBps": C / (op_ms[i] * 1e-3) / 1e9,
+                          "b_hbm_GBps": b_hbm, "b_host_GBps": b_host}), flush=True)
+        return 0
     ms, op_ms = time_steps(torch, wl, plan, args.steps, args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
     t_roof = two_tier_roofline_ms(wl, k, den, b_hbm, b_host)

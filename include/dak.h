@@ -118,9 +118,15 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  * of compute units reading the host and the requests each keeps in flight are
  * capped; both come from an offline sweep.
  *   host_cus       cap on work-groups (one per CU) that read host memory;
- *                  0 = library default (16)
- *   window         host in-flight window: 16-byte loads per lane issued ahead
- *                  of use in the host role; one of 1, 2, 4, 8; 0 = default (4)
+ *                  0 = per-operator default (split GEMM N <= 4: 8; split
+ *                  GEMM N > 4: 16; split attention: 8), the fewest that reach
+ *                  the full link rate in the library's sweep on MI355X
+ *   window         host in-flight window: loop steps whose loads a host-role
+ *                  wave issues before consuming the first; one of 1, 2, 4, 8;
+ *                  0 = per-operator default (2, 1, 1).  A step is 512 k of
+ *                  the wave's 4 rows (GEMM, N <= 4), a 256-k chunk of its 16
+ *                  rows (GEMM, N > 4; at most 2 chunks) or 16 tokens of K and
+ *                  V (attention; clamped to what registers allow)
  *   flags          bit-or of DAK_FLAG_*
  *   byte_counters  device pointer to 2 uint64 (host bytes, HBM bytes), used
  *                  only with DAK_FLAG_COUNT_BYTES: the kernels add the bytes

@@ -18,8 +18,16 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kDefaultHostCus = 16;
-constexpr int kDefaultWindow = 4;
+// Host-role defaults per operator class, from the offline sweep on MI355X
+// (fewest host work-groups that reach the link's full rate, then the smallest
+// window; a deep window also slows concurrent HBM readers the most).
+struct HostDefaults {
+  int host_cus;
+  int window;
+};
+constexpr HostDefaults kGemmFmaDefaults{8, 2};    // split GEMM, N <= 4
+constexpr HostDefaults kGemmMfmaDefaults{16, 1};  // split GEMM, N > 4
+constexpr HostDefaults kAttnDefaults{8, 1};       // split decode attention
 
 // Resolved launch configuration.
 struct LaunchCfg {
@@ -28,7 +36,7 @@ struct LaunchCfg {
   int flags;
   uint64_t* byte_counters;
 };
-dak_status resolve_cfg(const dak_launch_cfg* cfg, LaunchCfg* out);
+dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* out);
 
 // Host work-group count under a cap (fewest waves, then fewest groups).
 int64_t host_workgroups(int64_t items, int32_t cap);

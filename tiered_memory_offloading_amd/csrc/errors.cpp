@@ -32,9 +32,9 @@ void clear_error() {
   g_hip = 0;
 }
 
-dak_status resolve_cfg(const dak_launch_cfg* cfg, LaunchCfg* out) {
-  out->host_cus = kDefaultHostCus;
-  out->window = kDefaultWindow;
+dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* out) {
+  out->host_cus = def.host_cus;
+  out->window = def.window;
   out->flags = 0;
   out->byte_counters = nullptr;
   if (!cfg) return DAK_OK;

@@ -360,7 +360,7 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(DAK_EUNSUPPORTED, "group size %d is not 1, 2, 4 or 8", G);
   if (!std::isfinite(scale)) return fail(DAK_EINVAL, "scale must be finite");
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, &lc);
+  dak_status st = resolve_cfg(cfg, kAttnDefaults, &lc);
   if (st) return st;
   const size_t need = dak_decode_attn_workspace_bytes(kv, n_q_heads);
   if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);

@@ -147,18 +147,49 @@ __global__ __launch_bounds__(kThreads) void gemm_fma_split(
 // ---------------------------------------------------------------------------
 // MFMA path (4 < N <= 256)
 // ---------------------------------------------------------------------------
-// A work item is 16*RBW rows; wave w (w = 0..3) computes all of them over the
-// w-th K-slice.  K is walked in steps of 32; the T = ceil(K/32) steps are split
-// into four slices of ceil(T/4) consecutive steps.
+// Every row is computed the same way: K is walked in steps of 32, the
+// T = ceil(K/32) steps are split into four slices of ceil(T/4) consecutive
+// steps, wave w of the work-group accumulates slice w with one MFMA per step
+// and column block, and the four slice sums are added in slice order.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (wave64):
 //   A-operand: lane l holds A[i = l%16][k = 8*(l/16) .. +7]
 //   B-operand: lane l holds B[k = 8*(l/16) .. +7][j = l%16]
 //   result   : lane l holds D[i = 4*(l/16) + 0..3][j = l%16]
+//
+// The two roles fetch A differently, never computing differently:
+//   * HBM role: fragments are loaded straight from HBM (each row's 4 lanes
+//     read one 64-byte piece), U steps ahead;
+//   * host role: rows are read in 256-k chunks, each row's 512 bytes by 32
+//     consecutive lanes (host memory is not cached by the GPU, so short
+//     pieces would each cross the link as a small request), staged in the
+//     wave's LDS tile and read back as fragments.
+constexpr int kChunkSteps = 8;                  // host chunk: 8 steps = 256 k
+constexpr int kStageRow = 256 * 2 + 16;         // bytes per staged row; the pad spreads rows over banks
+constexpr int kStageWave = 16 * kStageRow;      // bytes per wave
+
+template <int NB>
+__device__ __forceinline__ void load_x_frags(const uint16_t* __restrict__ x, int64_t N, int64_t K, int64_t k,
+                                             bool ok, int i16, uint4 (&xv)[NB]) {
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int64_t n = 16 * cb + i16;
+    xv[cb] = (ok && n < N) ? ld16(x + n * K + k) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void mfma_step(f32x4_t (&acc)[NB], uint4 a, const uint4 (&xv)[NB]) {
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xv[cb]), acc[cb], 0, 0, 0);
+}
+
+// HBM role: 16*RBW rows over steps [step_beg, step_end), U steps loaded ahead.
 template <int NB, int RBW, int U, bool COUNT>
-__device__ __forceinline__ void mfma_rows(const uint16_t* __restrict__ a, int64_t K, int64_t step_beg,
-                                          int64_t step_end, const uint16_t* __restrict__ x, int64_t N,
-                                          f32x4_t (&acc)[RBW][NB], int lane, uint64_t& nbytes) {
+__device__ __forceinline__ void mfma_rows_direct(const uint16_t* __restrict__ a, int64_t K, int64_t step_beg,
+                                                 int64_t step_end, const uint16_t* __restrict__ x, int64_t N,
+                                                 f32x4_t (&acc)[RBW][NB], int lane, uint64_t& nbytes) {
   const int i16 = lane & 15;
   const int kq = (lane >> 4) * 8;
   for (int64_t s0 = step_beg; s0 < step_end; s0 += U) {
@@ -171,22 +202,70 @@ __device__ __forceinline__ void mfma_rows(const uint16_t* __restrict__ a, int64_
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb)
         av[u][rb] = ok ? ld16(a + (int64_t)(16 * rb + i16) * K + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int64_t n = 16 * cb + i16;
-        xv[u][cb] = (ok && n < N) ? ld16(x + n * K + k) : make_uint4(0, 0, 0, 0);
-      }
+      load_x_frags<NB>(x, N, K, k, ok, i16, xv[u]);
       if (COUNT && ok) nbytes += 16 * RBW;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + u >= step_end) break;   // uniform
+      if (s0 + u < step_end) {   // uniform
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
+        for (int rb = 0; rb < RBW; ++rb) mfma_step<NB>(acc[rb], av[u][rb], xv[u]);
+      }
+    }
+  }
+}
+
+// Host role: 16 rows over steps [step_beg, step_end), U chunks loaded ahead.
+template <int NB, int U, bool COUNT>
+__device__ __forceinline__ void mfma_rows_staged(const uint16_t* __restrict__ a, int64_t K, int64_t step_beg,
+                                                 int64_t step_end, const uint16_t* __restrict__ x, int64_t N,
+                                                 f32x4_t (&acc)[1][NB], unsigned char* stage, int lane,
+                                                 uint64_t& nbytes) {
+  const int i16 = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const int half = lane >> 5, l32 = lane & 31;
+  constexpr bool kPreloadX = NB <= 2;   // x for a whole chunk fits in registers
+  for (int64_t c0 = step_beg; c0 < step_end; c0 += kChunkSteps * U) {
+    uint4 av[U][8];
+    uint4 xv[U][kPreloadX ? kChunkSteps : 1][NB];
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][rb]), as_bf16x8(xv[u][cb]),
-                                                                 acc[rb][cb], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int64_t cs = c0 + u * kChunkSteps;
+      const int64_t k = (cs << 5) + l32 * 8;
+      const bool ok = (cs + (l32 >> 2) < step_end) && (k < K);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[u][j] = ok ? ld16(a + (int64_t)(2 * j + half) * K + k) : make_uint4(0, 0, 0, 0);
+        if (COUNT && ok) nbytes += 16;
+      }
+      if constexpr (kPreloadX) {
+#pragma unroll
+        for (int s = 0; s < kChunkSteps; ++s) {
+          const int64_t kx = ((cs + s) << 5) + kq;
+          load_x_frags<NB>(x, N, K, kx, (cs + s < step_end) && (kx < K), i16, xv[u][s]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cs = c0 + u * kChunkSteps;
+      if (cs >= step_end) break;   // uniform
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint4*>(stage + (2 * j + half) * kStageRow + l32 * 16) = av[u][j];
+#pragma unroll
+      for (int s = 0; s < kChunkSteps; ++s) {
+        if (cs + s >= step_end) break;   // uniform
+        const uint4 af = *reinterpret_cast<const uint4*>(stage + i16 * kStageRow + (s * 32 + kq) * 2);
+        if constexpr (kPreloadX) {
+          mfma_step<NB>(acc[0], af, xv[u][s]);
+        } else {
+          uint4 xs[NB];
+          const int64_t kx = ((cs + s) << 5) + kq;
+          load_x_frags<NB>(x, N, K, kx, kx < K, i16, xs);
+          mfma_step<NB>(acc[0], af, xs);
+        }
+      }
     }
   }
 }
@@ -196,6 +275,7 @@ __device__ __forceinline__ void mfma_rows(const uint16_t* __restrict__ a, int64_
 template <int NB, int RBW>
 __device__ __forceinline__ void mfma_reduce_store(f32x4_t (&acc)[RBW][NB], f32x4_t* part, float* __restrict__ y,
                                                   int64_t M, int64_t N, int64_t row0, int wave, int lane) {
+  __syncthreads();   // staging tiles alias `part`
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -219,40 +299,47 @@ __device__ __forceinline__ void mfma_reduce_store(f32x4_t (&acc)[RBW][NB], f32x4
   __syncthreads();   // LDS is reused by the next item
 }
 
+template <int NB, int RBW>
+constexpr int mfma_lds_bytes() {
+  constexpr int stage = kWaves * kStageWave;
+  constexpr int part = kWaves * RBW * NB * 64 * 16;
+  return stage > part ? stage : part;
+}
+
+// Host items are 16 rows (RBW = 1); HBM items are 16*RBW rows.
 template <int NB, int RBW, int UH, int UG, bool COUNT>
 __global__ __launch_bounds__(kThreads) void gemm_mfma_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
     int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
-  __shared__ f32x4_t part[kWaves * RBW * NB * 64];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[mfma_lds_bytes<NB, RBW>()];
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t T = (K + 31) >> 5;
   const int64_t per = (T + kWaves - 1) / kWaves;
   const int64_t sb = std::min<int64_t>(T, wave * per), se = std::min<int64_t>(T, sb + per);
-  constexpr int ROWS = 16 * RBW;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
   if (host_role) {
+    unsigned char* stage = lds + wave * kStageWave;
     for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
-      const int64_t row = it * ROWS;
-      f32x4_t acc[RBW][NB];
+      const int64_t row = it * 16;
+      f32x4_t acc[1][NB];
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<NB, RBW, UH, COUNT>(a_host + row * K, K, sb, se, x, N, acc, lane, nbytes);
-      mfma_reduce_store<NB, RBW>(acc, part, y, M, N, row, wave, lane);
+      for (int cb = 0; cb < NB; ++cb) acc[0][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      mfma_rows_staged<NB, UH, COUNT>(a_host + row * K, K, sb, se, x, N, acc, stage, lane, nbytes);
+      mfma_reduce_store<NB, 1>(acc, part, y, M, N, row, wave, lane);
     }
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
     if (it < hbm_items) {
-      const int64_t lrow = it * ROWS;
+      const int64_t lrow = it * 16 * RBW;
       f32x4_t acc[RBW][NB];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mfma_rows<NB, RBW, UG, COUNT>(a_hbm + lrow * K, K, sb, se, x, N, acc, lane, nbytes);
+      mfma_rows_direct<NB, RBW, UG, COUNT>(a_hbm + lrow * K, K, sb, se, x, N, acc, lane, nbytes);
       mfma_reduce_store<NB, RBW>(acc, part, y, M, N, host_rows + lrow, wave, lane);
     }
   }
@@ -299,38 +386,32 @@ void launch_fma(const GemmArgs& g) {
   }
 }
 
+// HBM window: as many steps ahead as ~32 16-byte loads per lane allow.
+template <int NB, int RBW>
+constexpr int hbm_window() {
+  constexpr int w = 32 / (RBW + NB);
+  return w >= 16 ? 16 : w >= 8 ? 8 : w >= 4 ? 4 : w >= 2 ? 2 : 1;
+}
+
 template <int NB, int RBW, int UH, bool COUNT>
 void launch_mfma_nb(const GemmArgs& g) {
-  constexpr int UG = (NB >= 8) ? 1 : 2;
+  constexpr int UG = hbm_window<NB, RBW>();
+  constexpr int UHc = NB >= 8 ? 1 : (UH > 2 ? 2 : UH);   // chunks in flight (64 VGPRs each)
   const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_mfma_split<NB, RBW, UH, UG, COUNT>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_mfma_split<NB, RBW, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(kThreads), 0,
                      g.stream, g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items,
                      g.hbm_items, g.counters);
 }
 
 template <int UH, bool COUNT>
 void launch_mfma(const GemmArgs& g, int nb, int rbw) {
-  // Host windows above 2 steps only for narrow N (register budget).
-  if (nb == 1) {
-    if (rbw == 4) return launch_mfma_nb<1, 4, UH, COUNT>(g);
-    if (rbw == 2) return launch_mfma_nb<1, 2, UH, COUNT>(g);
-    return launch_mfma_nb<1, 1, UH, COUNT>(g);
+  switch (nb) {
+    case 1: return rbw == 2 ? launch_mfma_nb<1, 2, UH, COUNT>(g) : launch_mfma_nb<1, 1, UH, COUNT>(g);
+    case 2: return rbw == 2 ? launch_mfma_nb<2, 2, UH, COUNT>(g) : launch_mfma_nb<2, 1, UH, COUNT>(g);
+    case 4: return rbw == 2 ? launch_mfma_nb<4, 2, UH, COUNT>(g) : launch_mfma_nb<4, 1, UH, COUNT>(g);
+    case 8: return launch_mfma_nb<8, 1, UH, COUNT>(g);
+    default: return launch_mfma_nb<16, 1, UH, COUNT>(g);
   }
-  if (nb == 2) {
-    if (rbw == 4) return launch_mfma_nb<2, 4, (UH > 4 ? 4 : UH), COUNT>(g);
-    if (rbw == 2) return launch_mfma_nb<2, 2, UH, COUNT>(g);
-    return launch_mfma_nb<2, 1, UH, COUNT>(g);
-  }
-  if (nb == 4) {
-    if (rbw == 4) return launch_mfma_nb<4, 4, (UH > 2 ? 2 : UH), COUNT>(g);
-    if (rbw == 2) return launch_mfma_nb<4, 2, (UH > 4 ? 4 : UH), COUNT>(g);
-    return launch_mfma_nb<4, 1, UH, COUNT>(g);
-  }
-  if (nb == 8) {
-    if (rbw == 2) return launch_mfma_nb<8, 2, (UH > 2 ? 2 : UH), COUNT>(g);
-    return launch_mfma_nb<8, 1, (UH > 4 ? 4 : UH), COUNT>(g);
-  }
-  return launch_mfma_nb<16, 1, (UH > 2 ? 2 : UH), COUNT>(g);
 }
 
 template <bool COUNT>
@@ -369,8 +450,9 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
   if (N > 256) return fail(DAK_EUNSUPPORTED, "N=%lld > 256 (large-N path not built)", (long long)N);
   if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
+  const bool fma = N <= 4;
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, &lc);
+  dak_status st = resolve_cfg(cfg, fma ? kGemmFmaDefaults : kGemmMfmaDefaults, &lc);
   if (st) return st;
 
   const int64_t host_rows = h * m;
@@ -384,19 +466,17 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   if ((st = check_tier_ptr(x, (uint64_t)N * K * 2, Tier::kDevice, "x", &dx))) return st;
   if ((st = check_tier_ptr(y, (uint64_t)N * M * 4, Tier::kDevice, "y", &dy))) return st;
 
-  const bool fma = N <= 4;
   int nb = 1, rbw = 1;
-  int64_t item_rows;
+  int64_t host_item_rows, hbm_item_rows;
   if (fma) {
-    item_rows = kFmaItemRows;
+    host_item_rows = hbm_item_rows = kFmaItemRows;
   } else {
     nb = N <= 16 ? 1 : N <= 32 ? 2 : N <= 64 ? 4 : N <= 128 ? 8 : 16;
-    // Largest row group that keeps >= 512 items and the accumulators small;
-    // it never changes the arithmetic of a row.
-    const int maxr = nb <= 1 ? 4 : nb == 2 ? 4 : nb == 4 ? 4 : nb == 8 ? 2 : 1;
-    for (int r = maxr; r >= 1; r >>= 1)
-      if (m % (16 * r) == 0 && (M / (16 * r) >= 512 || r == 1)) { rbw = r; break; }
-    item_rows = 16 * rbw;
+    // HBM items of 32 rows halve the re-reads of x where the matrix still
+    // gives >= 2 items per CU; the grouping never changes a row's arithmetic.
+    rbw = (nb <= 4 && m % 32 == 0 && M / 32 >= 512) ? 2 : 1;
+    host_item_rows = 16;
+    hbm_item_rows = 16 * rbw;
   }
   GemmArgs g;
   g.a_host = static_cast<const uint16_t*>(dh);
@@ -407,8 +487,8 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   g.x = static_cast<const uint16_t*>(dx);
   g.N = N;
   g.y = y;
-  g.host_items = host_rows / item_rows;
-  g.hbm_items = (M - host_rows) / item_rows;
+  g.host_items = host_rows / host_item_rows;
+  g.hbm_items = (M - host_rows) / hbm_item_rows;
   g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
   g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   g.stream = static_cast<hipStream_t>(stream);

@@ -23,12 +23,24 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 // Sum over the 16 lanes of a DPP row; every lane of the row ends with the same
 // bits (each step adds a lane to its mirror image, and fp addition commutes).
+// Every source lane of these patterns lies inside the row, so bound_ctrl only
+// lets the compiler fold each move into the add (v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row_mirror
+  v = dpp_add<0xB1>(v);   // quad_perm 1,0,3,2
+  v = dpp_add<0x4E>(v);   // quad_perm 2,3,0,1
+  v = dpp_add<0x141>(v);  // row_half_mirror
+  v = dpp_add<0x140>(v);  // row_mirror
   return v;
+}
+
+// Dot product of two bf16 pairs accumulated into fp32 (v_dot2c_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // Sum over all 64 lanes by a fixed xor butterfly; all lanes end with equal bits.

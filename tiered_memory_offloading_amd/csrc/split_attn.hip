@@ -15,8 +15,9 @@
 //   * wave w of the work-group walks tokens [256 w, 256 w + 256) of the chunk
 //     in tiles of 16 tokens.  Each tile is 4 fully coalesced 1 KiB loads of K
 //     and 4 of V: load i covers tokens t0 + 4 i + lane/16, dims 8 (lane % 16)..+7;
-//   * q . K is an fp32 dot over the lane's 8 dims, summed over the 16 lanes of
-//     a DPP row; scores carry scale * log2(e) so exp2 gives the softmax weights;
+//   * q . K takes the lane's 8 dims as four bf16-pair dot products into fp32
+//     (v_dot2c_f32_bf16), summed over the 16 lanes of a DPP row, then scaled by
+//     scale * log2(e) so exp2 gives the softmax weights;
 //   * online softmax state (m, l, o) per lane group, merged across the four
 //     lane groups, then across the four waves in order, then written as the
 //     chunk's partial (m, l, o);
@@ -63,11 +64,13 @@ __device__ __forceinline__ void merge_state(float (&m)[G], float (&l)[G], float 
 }
 
 // Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the lane
-// group's online-softmax state.
+// group's online-softmax state.  qb holds the lane's 8 query dims per head as
+// bf16 pairs (unscaled); qscale = scale * log2(e).
 template <int G, int U, bool COUNT>
 __device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, const uint16_t* __restrict__ Vbg,
-                                            int64_t tb, int64_t te, const float (&qf)[G][8], float (&m)[G],
-                                            float (&l)[G], float (&o)[G][8], int lane, uint64_t& nbytes) {
+                                            int64_t tb, int64_t te, const uint32_t (&qb)[G][4], float qscale,
+                                            float (&m)[G], float (&l)[G], float (&o)[G][8], int lane,
+                                            uint64_t& nbytes) {
   const int grp = lane >> 4;
   const int dq = (lane & 15) * 8;
   const int64_t ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
@@ -86,55 +89,63 @@ __device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, co
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (t0 + u >= ntiles) break;   // uniform
-      float s[4][G];
-      float vf[4][8];
+      if (t0 + u < ntiles) {   // uniform
+        float s[4][G];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = tb + (t0 + u) * kTile + 4 * i + grp;
-        const uint32_t kw[4] = {kv[u][i].x, kv[u][i].y, kv[u][i].z, kv[u][i].w};
-        const uint32_t vw[4] = {vv[u][i].x, vv[u][i].y, vv[u][i].z, vv[u][i].w};
-        float kf[8];
+        for (int i = 0; i < 4; ++i) {
+          const int64_t t = tb + (t0 + u) * kTile + 4 * i + grp;
+          const uint32_t kw[4] = {kv[u][i].x, kv[u][i].y, kv[u][i].z, kv[u][i].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          kf[2 * q] = bf_lo(kw[q]);
-          kf[2 * q + 1] = bf_hi(kw[q]);
-          vf[i][2 * q] = bf_lo(vw[q]);
-          vf[i][2 * q + 1] = bf_hi(vw[q]);
+          for (int h = 0; h < G; ++h) {
+            float p = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p = dot2_bf16(kw[q], qb[h][q], p);
+            p = row16_sum(p) * qscale;
+            s[i][h] = (t < te) ? p : kNegInf;
+          }
+        }
+        float vf[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t vw[4] = {vv[u][i].x, vv[u][i].y, vv[u][i].z, vv[u][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            vf[i][2 * q] = bf_lo(vw[q]);
+            vf[i][2 * q + 1] = bf_hi(vw[q]);
+          }
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float p = 0.f;
+          const float mt = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+          const float mn = fmaxf(m[h], mt);
+          const float ms = (mn == kNegInf) ? 0.f : mn;
+          // Rescale only when some lane group's running max grew; elsewhere
+          // the factor is exp2(0) = 1 and the multiply would not change a bit.
+          float ls = l[h];
+          if (__any(mn > m[h])) {
+            const float alpha = exp2_fast(m[h] - ms);
+            ls = ls * alpha;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p = __builtin_fmaf(qf[h][e], kf[e], p);
-          p = row16_sum(p);
-          s[i][h] = (t < te) ? p : kNegInf;
+            for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * alpha;
+          }
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i][h] - ms);
+          // l and o take the same sequence of operations (o with an fma per
+          // token), so o is exactly c * l whenever every V row equals a power of
+          // two c.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ls = ls + p[i];
+          l[h] = ls;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float acc = o[h][e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(p[i], vf[i][e], acc);
+            o[h][e] = acc;
+          }
+          m[h] = mn;
         }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mt = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-        const float mn = fmaxf(m[h], mt);
-        const float ms = (mn == kNegInf) ? 0.f : mn;
-        const float alpha = exp2_fast(m[h] - ms);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i][h] - ms);
-        // l and o take the same sequence of operations (o with an fma per
-        // token), so o is exactly c * l whenever every V row equals a power of
-        // two c.
-        float ls = l[h] * alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ls = ls + p[i];
-        l[h] = ls;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float acc = o[h][e] * alpha;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(p[i], vf[i][e], acc);
-          o[h][e] = acc;
-        }
-        m[h] = mn;
       }
     }
   }
@@ -149,16 +160,14 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
                                           float* __restrict__ ml_ws, float* red_o, float* red_ml, int wave,
                                           int lane, uint64_t& nbytes) {
   const int dq = (lane & 15) * 8;
-  float qf[G][8];
+  uint32_t qb[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const uint4 qv = ld16(q + ((b * Hq) + g * G + h) * kD + dq);
-    const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      qf[h][2 * k] = bf_lo(w[k]) * qscale;
-      qf[h][2 * k + 1] = bf_hi(w[k]) * qscale;
-    }
+    qb[h][0] = qv.x;
+    qb[h][1] = qv.y;
+    qb[h][2] = qv.z;
+    qb[h][3] = qv.w;
   }
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -170,7 +179,7 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
   }
   const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
   const int64_t te = tb + kWaveTokens < ctx ? tb + kWaveTokens : ctx;
-  attn_tokens<G, U, COUNT>(Kbg, Vbg, tb, te, qf, m, l, o, lane, nbytes);
+  attn_tokens<G, U, COUNT>(Kbg, Vbg, tb, te, qb, qscale, m, l, o, lane, nbytes);
 
   // Merge the four lane groups (xor 16, then xor 32).
 #pragma unroll

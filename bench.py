@@ -54,15 +54,15 @@ def host_units(k, den, n):
 class Workload:
     """Weights and KV in both tiers, plus outputs and workspace."""
 
-    def __init__(self, torch, dak, seed=0):
+    def __init__(self, torch, dak, seed=0, n_act=BATCH):
         self.torch, self.dak = torch, dak
         dev = torch.device("cuda")
         self.lin = []
         for i, (name, M, K) in enumerate(synth.LLAMA8B_LINEARS):
-            A, X = synth.gemm_inputs(M, K, BATCH, seed=seed + i, device="cuda")
+            A, X = synth.gemm_inputs(M, K, n_act, seed=seed + i, device="cuda")
             A_host = torch.empty((M, K), dtype=torch.bfloat16, pin_memory=True)
             A_host.copy_(A)
-            y = torch.empty((BATCH, M), dtype=torch.float32, device=dev)
+            y = torch.empty((n_act, M), dtype=torch.float32, device=dev)
             self.lin.append(dict(name=name, M=M, K=K, A_dev=A, A_host=A_host, x=X.contiguous(), y=y))
         q, K, V = synth.attn_inputs(BATCH, HQ, HKV, HD, CTX, seed=seed + 10, device="cuda")
         self.q, self.K_dev, self.V_dev = q, K, V
@@ -232,6 +232,8 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--n-act", type=int, default=BATCH,
+                    help="activation rows N of the split GEMMs (config sweeps use 1, 16, 64)")
     ap.add_argument("--only", choices=OP_ORDER, default=None,
                     help="time one operator of the step (for profiling); the JSON then covers that op only")
     args = ap.parse_args(argv)
@@ -249,7 +251,7 @@ def main(argv=None):
     b_hbm, b_host = measure_bandwidths(torch, dak)
     log(f"B_hbm {b_hbm:.0f} GB/s, B_host {b_host:.2f} GB/s")
     log("building the workload on the GPU")
-    wl = Workload(torch, dak)
+    wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()
     step_bytes = sum(C for _, C, _ in ops)
     den = 20

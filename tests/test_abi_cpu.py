@@ -146,8 +146,8 @@ def test_attention_shape_errors_are_reported_before_any_launch():
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 32, C.c_float(float("inf")), None, None, 0, None, None) == L.DAK_EINVAL
     # workspace too small is caught before pointers are looked at
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 32, C.c_float(0.1), None, None, 16, None, None) == L.DAK_EINVAL
-    # workspace size: B * Hq * chunks * (D + 2) fp32
+    # workspace size: B * Hq * chunks * (D + 2) fp32, chunks of 2048 tokens
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 32) == 16 * 32 * 1 * 130 * 4
     kv2 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768)
-    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 32 * 130 * 4
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 16 * 130 * 4   # 2048-token chunks
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 30) == 0

@@ -172,3 +172,17 @@ def test_pointer_validation_rejects_wrong_tiers():
     y = torch.empty((1, 128), dtype=torch.float32, device="cuda")
     assert lib.dak_splitk_gemm(C.byref(d), X.data_ptr(), 1, y.data_ptr(), None, None) == -1
     assert b"x" in lib.dak_last_error()
+
+
+@pytest.mark.parametrize("N", [16, 33, 64])
+def test_wide_hbm_row_groups_with_ragged_k(N):
+    # M = 12288 selects HBM items of 32 or 64 rows (the row-group size depends
+    # on M and N only); K = 1000 is ragged.  Every split must give the same bits.
+    M, K = 12288, 1000
+    A, X = synth.gemm_inputs(M, K, N, seed=70 + N)
+    g = torch.Generator().manual_seed(71)
+    rows = torch.randint(0, M, (64,), generator=g).tolist() + [0, M - 1]
+    ref = og.gemm_rows(og.to_f64(A[rows]), og.to_f64(X))
+    outs = [run(A, X, 64, h) for h in (0, 7, M // 64)]
+    assert og.normwise_error(outs[0][:, rows].numpy(), ref) <= TOL
+    assert torch.equal(outs[1], outs[0]) and torch.equal(outs[2], outs[0])

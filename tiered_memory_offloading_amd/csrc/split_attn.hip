@@ -9,10 +9,10 @@
 // capped in work-groups and in-flight loads.
 //
 // CDNA4 design:
-//   * partial kernel, one work item per (request b, KV head g, chunk of 1024
+//   * partial kernel, one work item per (request b, KV head g, chunk of 2048
 //     tokens).  The item's K and V rows are read once, for all query heads of
 //     the group (G = Hq / Hkv), so grouped heads never re-read KV;
-//   * wave w of the work-group walks tokens [256 w, 256 w + 256) of the chunk
+//   * wave w of the work-group walks tokens [512 w, 512 w + 512) of the chunk
 //     in tiles of 16 tokens.  Each tile is 4 fully coalesced 1 KiB loads of K
 //     and 4 of V: load i covers tokens t0 + 4 i + lane/16, dims 8 (lane % 16)..+7;
 //   * q . K takes the lane's 8 dims as four bf16-pair dot products into fp32
@@ -35,7 +35,7 @@ namespace dak {
 namespace {
 
 constexpr int kD = 128;                 // head_dim handled by this build
-constexpr int kChunk = 1024;            // tokens per work item
+constexpr int kChunk = 2048;            // tokens per work item
 constexpr int kAttnWaves = 4;
 constexpr int kWaveTokens = kChunk / kAttnWaves;
 constexpr int kTile = 16;               // tokens per tile (4 loads of K + 4 of V per lane)
@@ -272,27 +272,44 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
   }
 }
 
-// out[row, :] = merge of the C chunk partials of row = b * Hq + j, in chunk order.
-__global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ o_ws, const float* __restrict__ ml_ws,
+// out[row, :] = merge of the C chunk partials of row = b * Hq + j.  One
+// work-group of kD threads per row: the chunk maxima and weights are computed
+// from LDS in chunk order (identically by every thread), then thread d sums its
+// dimension over the chunks in chunk order; the chunk loads are independent, so
+// many are in flight at once.
+__global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_ws, const float* __restrict__ ml_ws,
                                                    int C, float* __restrict__ out) {
+  __shared__ float sm[2 * 256];
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int d = threadIdx.x;
   const float* ml = ml_ws + row * C * 2;
   const float* ow = o_ws + row * C * kD;
+  float O = 0.f, L = 0.f;
+  // Chunks in groups of 256 (C is at most ctx / kChunk).
   float M = kNegInf;
-  for (int c = 0; c < C; ++c) M = fmaxf(M, ml[c * 2]);
-  const float Ms = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, O0 = 0.f, O1 = 0.f;
-  for (int c = 0; c < C; ++c) {
-    const float w = exp2_fast(ml[c * 2] - Ms);
-    const float lw = ml[c * 2 + 1] * w;
-    L = L + lw;
-    const float2 ov = *reinterpret_cast<const float2*>(ow + c * kD + 2 * lane);
-    const float a = ov.x * w, b = ov.y * w;
-    O0 = O0 + a;
-    O1 = O1 + b;
+  for (int c0 = 0; c0 < C; c0 += 256) {
+    const int n = C - c0 < 256 ? C - c0 : 256;
+    __syncthreads();
+    for (int i = d; i < 2 * n; i += kD) sm[i] = ml[(int64_t)c0 * 2 + i];
+    __syncthreads();
+    for (int c = 0; c < n; ++c) M = fmaxf(M, sm[2 * c]);
   }
-  *reinterpret_cast<float2*>(out + row * kD + 2 * lane) = make_float2(O0 / L, O1 / L);
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  for (int c0 = 0; c0 < C; c0 += 256) {
+    const int n = C - c0 < 256 ? C - c0 : 256;
+    __syncthreads();
+    for (int i = d; i < 2 * n; i += kD) sm[i] = ml[(int64_t)c0 * 2 + i];
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < n; ++c) {
+      const float w = exp2_fast(sm[2 * c] - Ms);
+      const float lw = sm[2 * c + 1] * w;
+      L = L + lw;
+      const float a = ow[(int64_t)(c0 + c) * kD + d] * w;
+      O = O + a;
+    }
+  }
+  out[row * kD + d] = O / L;
 }
 
 struct AttnArgs {
@@ -418,7 +435,7 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
     launch_partial_w<false>(a, G, lc.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(64), 0, a.stream, a.o_ws, a.ml_ws, a.C,
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
                      out);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");

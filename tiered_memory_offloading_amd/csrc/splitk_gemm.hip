@@ -406,8 +406,12 @@ void launch_mfma_nb(const GemmArgs& g) {
 template <int UH, bool COUNT>
 void launch_mfma(const GemmArgs& g, int nb, int rbw) {
   switch (nb) {
-    case 1: return rbw == 2 ? launch_mfma_nb<1, 2, UH, COUNT>(g) : launch_mfma_nb<1, 1, UH, COUNT>(g);
-    case 2: return rbw == 2 ? launch_mfma_nb<2, 2, UH, COUNT>(g) : launch_mfma_nb<2, 1, UH, COUNT>(g);
+    case 1:
+      return rbw == 4 ? launch_mfma_nb<1, 4, UH, COUNT>(g)
+                      : rbw == 2 ? launch_mfma_nb<1, 2, UH, COUNT>(g) : launch_mfma_nb<1, 1, UH, COUNT>(g);
+    case 2:
+      return rbw == 4 ? launch_mfma_nb<2, 4, UH, COUNT>(g)
+                      : rbw == 2 ? launch_mfma_nb<2, 2, UH, COUNT>(g) : launch_mfma_nb<2, 1, UH, COUNT>(g);
     case 4: return rbw == 2 ? launch_mfma_nb<4, 2, UH, COUNT>(g) : launch_mfma_nb<4, 1, UH, COUNT>(g);
     case 8: return launch_mfma_nb<8, 1, UH, COUNT>(g);
     default: return launch_mfma_nb<16, 1, UH, COUNT>(g);
@@ -472,9 +476,14 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     host_item_rows = hbm_item_rows = kFmaItemRows;
   } else {
     nb = N <= 16 ? 1 : N <= 32 ? 2 : N <= 64 ? 4 : N <= 128 ? 8 : 16;
-    // HBM items of 32 rows halve the re-reads of x where the matrix still
-    // gives >= 2 items per CU; the grouping never changes a row's arithmetic.
-    rbw = (nb <= 4 && m % 32 == 0 && M / 32 >= 512) ? 2 : 1;
+    // HBM items of 16*rbw rows: a wave reuses each x fragment for rbw row
+    // blocks, so larger groups cut x re-reads, as long as at least 192 items
+    // remain to spread over the CUs (measured on the Llama-8B linears).  The
+    // grouping never changes a row's arithmetic.
+    const int maxr = nb <= 2 ? 4 : nb == 4 ? 2 : 1;
+    rbw = 1;
+    for (int r = maxr; r >= 2; r >>= 1)
+      if (m % (16 * r) == 0 && M / (16 * r) >= 192) { rbw = r; break; }
     host_item_rows = 16;
     hbm_item_rows = 16 * rbw;
   }

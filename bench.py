@@ -181,46 +181,99 @@ def time_steps(torch, wl, plan, steps, warmup, per_op=True, only=None):
     return dt * 1e3, op_ms
 
 
-def cpu_baseline(seed=0):
-    """The oracle, as it stands, on a bounded sample of the step: the O linear
-    (4096x4096, N = 16) and two (request, KV head) attention pairs, timed on the
-    host CPU and scaled by bytes to the whole step."""
-    import numpy as np
-    import torch
+def cpu_baseline(wl, reps=5):
+    """The oracle, as it stands, on the whole step at x = 0 (the result does
+    not depend on x): the four split-GEMM oracles at N = 16 and the attention
+    oracle over all 16 requests x 32 query heads, on the host CPU, from the
+    same tensors the GPU step reads (copied to the host first, untimed)."""
+    import numpy as np  # noqa: F401
     from oracle import attention as oa
     from oracle import gemm as og
 
     t0 = time.perf_counter()
-    A, X = synth.gemm_inputs(4096, 4096, BATCH, seed=seed)
-    t_gen = time.perf_counter()
-    og.gemm(og.to_f64(A), og.to_f64(X))
-    t_lin = time.perf_counter() - t_gen
-    gen = torch.Generator().manual_seed(seed + 10)
-    pairs = 2
-    t_att = 0.0
-    for _ in range(pairs):
-        q = synth.normal_bf16((4, HD), 1.0, gen)
-        Kb = synth.normal_bf16((CTX, HD), 1.0, gen)
-        Vb = synth.normal_bf16((CTX, HD), 1.0, gen)
+    lin = [(L["A_dev"].cpu(), L["x"].cpu()) for L in wl.lin]
+    q, K, V = wl.q.cpu(), wl.K_dev.cpu(), wl.V_dev.cpu()
+    t_copy = time.perf_counter() - t0
+    runs = []
+    for _ in range(reps):
         t1 = time.perf_counter()
-        qf, Kf, Vf = og.to_f64(q), og.to_f64(Kb), og.to_f64(Vb)
-        for j in range(4):
-            oa.attend_one(qf[j], Kf, Vf, 1.0 / math.sqrt(HD))
-        t_att += time.perf_counter() - t1
-    lin_bytes = sum(M * K * 2 for _, M, K in synth.LLAMA8B_LINEARS)
-    kv_bytes = 2 * BATCH * HKV * CTX * HD * 2
-    t_step = t_lin * lin_bytes / (4096 * 4096 * 2) + t_att / pairs * (BATCH * HKV)
-    cores = len(os.sched_getaffinity(0))
+        for A, X in lin:
+            og.gemm(og.to_f64(A), og.to_f64(X))
+        t_lin = time.perf_counter() - t1
+        t2 = time.perf_counter()
+        for b in range(BATCH):
+            oa.decode_attention(og.to_f64(q[b:b + 1]), og.to_f64(K[b:b + 1]), og.to_f64(V[b:b + 1]), wl.scale)
+        t_att = time.perf_counter() - t2
+        runs.append((t_lin + t_att, t_lin, t_att))
+    runs.sort()
+    t_step, t_lin, t_att = runs[len(runs) // 2]
+    step_bytes = sum(C for _, C, _ in wl.op_bytes())
     return {
-        "value": round((lin_bytes + kv_bytes) / t_step / 1e9, 4),
+        "value": round(step_bytes / t_step / 1e9, 4),
         "unit": "GB/s",
-        "cores": cores,
+        "cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: O linear 4096x4096 at N=16 ({t_lin:.2f} s) and {pairs} (request, kv-head) "
-                   f"attention pairs x 4 query heads over 32768 tokens ({t_att:.2f} s), scaled by bytes to one "
-                   f"step ({t_step:.1f} s per step); input generation excluded"),
-        "wall_s": round(time.perf_counter() - t0, 2),
+        "sample": (f"the whole step, median of {reps} runs: fp64 numpy oracle of the four split GEMMs at N=16 "
+                   f"({t_lin:.2f} s) and of the split-KV attention over 16 requests x 32 query heads x 32768 tokens "
+                   f"({t_att:.2f} s), on the same inputs as the GPU step (copied to the host first, {t_copy:.1f} s, "
+                   f"untimed)"),
+        "seconds_per_step": round(t_step, 3),
     }
+
+
+def run_llama70b(torch, dak, args, b_hbm, b_host):
+    """70B-shaped decode step (80 layers, hidden 8192, GQA 64/8, hd 128, FFN
+    28672, batch 16 x 32768 tokens): the planner spreads the ~309 GB footprint
+    over HBM and pinned host memory; the step is timed against its model."""
+    from tiered_memory_offloading_amd.model import LLAMA70B, DecodeModel
+
+    free, total = torch.cuda.mem_get_info()
+    reserve = int(args.hbm_reserve_gib * (1 << 30))
+    H = free - reserve
+    log(f"HBM free {free / 2**30:.2f} GiB of {total / 2**30:.2f} GiB; planning with H = {H / 2**30:.2f} GiB")
+    model = DecodeModel(LLAMA70B, 16, 32768, b_hbm * 1e9, b_host * 1e9, H, log=log)
+    for _ in range(args.warmup):
+        model.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        model.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    n = len(model.slots)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    model.step(events=evs)
+    torch.cuda.synchronize()
+    per_kind = {}
+    for i, o in enumerate(model.slots):
+        d = per_kind.setdefault(o.kind, {"measured_ms": 0.0, "modeled_ms": 0.0, "host_units": 0, "units": 0,
+                                         "host_bytes": 0, "bytes": 0})
+        d["measured_ms"] += evs[i][0].elapsed_time(evs[i][1])
+        d["modeled_ms"] += model.op_model_s(i) * 1e3
+        d["host_units"] += o.host_units
+        d["units"] += o.units
+        d["host_bytes"] += o.host_units * o.unit_bytes
+        d["bytes"] += o.bytes
+    for d in per_kind.values():
+        d["measured_ms"] = round(d["measured_ms"], 3)
+        d["modeled_ms"] = round(d["modeled_ms"], 3)
+    ops_with_host = sum(1 for o in model.slots if o.host_units)
+    res = {
+        "metric": "effective GB/s (HBM+host) of a 70B-shaped decode step at the planned ratios",
+        "value": round(model.footprint / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "Llama-70B-shaped decode step: 80 layers x {QKV 10240x8192, split-KV attention "
+                               "64q/8kv hd128, O 8192x8192, gate+up 57344x8192, down 8192x28672}, batch 16, "
+                               "32768 ctx/request", "footprint_bytes": model.footprint,
+                   "hbm_budget_bytes": H, "hbm_reserve_bytes": reserve},
+        "x_global": round(model.x_global, 6), "host_bytes": model.host_bytes, "ops": n,
+        "ops_with_host_units": ops_with_host, "modeled_ms": round(model.modeled_s * 1e3, 3),
+        "frac_of_model": round(model.modeled_s * 1e3 / ms, 4),
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "per_kind": per_kind,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def main(argv=None):
@@ -232,6 +285,10 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b"), default="llama8b-layer",
+                    help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios (own JSON line)")
+    ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,
+                    help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,
                     help="activation rows N of the split GEMMs (config sweeps use 1, 16, 64)")
     ap.add_argument("--only", choices=OP_ORDER, default=None,
@@ -250,6 +307,8 @@ def main(argv=None):
     log("measuring B_hbm / B_host with the streaming-read probes")
     b_hbm, b_host = measure_bandwidths(torch, dak)
     log(f"B_hbm {b_hbm:.0f} GB/s, B_host {b_host:.2f} GB/s")
+    if args.workload == "llama70b":
+        return run_llama70b(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()
@@ -336,7 +395,7 @@ def main(argv=None):
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -122,11 +122,13 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  *                  GEMM N > 4: 16; split attention: 8), the fewest that reach
  *                  the full link rate in the library's sweep on MI355X
  *   window         host in-flight window: loop steps whose loads a host-role
- *                  wave issues before consuming the first; one of 1, 2, 4, 8;
- *                  0 = per-operator default (2, 1, 1).  A step is 512 k of
- *                  the wave's 4 rows (GEMM, N <= 4), a 256-k chunk of its 16
- *                  rows (GEMM, N > 4; at most 2 chunks) or 16 tokens of K and
- *                  V (attention; clamped to what registers allow)
+ *                  wave issues before consuming the first; one of 1, 2, 4, 8.
+ *                  0 = sized so that all host work-groups together keep about
+ *                  256 KiB in flight (the link's bandwidth-delay product).  A
+ *                  step is 512 k of the wave's 4 rows (GEMM, N <= 4), a 256-k
+ *                  chunk of its 16 rows (GEMM, N > 4; at most 2 chunks) or 16
+ *                  tokens of K and V (attention; clamped to what registers
+ *                  allow)
  *   flags          bit-or of DAK_FLAG_*
  *   byte_counters  device pointer to 2 uint64 (host bytes, HBM bytes), used
  *                  only with DAK_FLAG_COUNT_BYTES: the kernels add the bytes

@@ -119,3 +119,21 @@ def test_attention_pointer_validation():
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(dak.DakError):
         dak.splitk_decode_attn(q.cuda(), kv, 0.1, ws=small)
+
+
+def test_llama70b_attention_full_size():
+    # 64 query heads on 8 KV heads (groups of 8), 16 requests x 32768 tokens,
+    # generated on the GPU; sampled (request, head) pairs against the oracle and
+    # bit-identity between 0 and 4 requests on the host.
+    B, Hq, Hkv, D, ctx = 16, 64, 8, 128, 32768
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=9, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    out4 = run(q, K, V, 4, scale)
+    out0 = run(q, K, V, 0, scale)
+    assert torch.equal(out4, out0)
+    for b, j in [(0, 0), (3, 63), (4, 7), (15, 8), (9, 40)]:
+        gk = oa.kv_group(j, Hq, Hkv)
+        ref = oa.attend_one(to_f64(q[b, j]), to_f64(K[b, gk]), to_f64(V[b, gk]), scale)
+        assert normwise_error(out4[b, j].numpy(), ref) <= TOL, (b, j)
+    del K, V
+    torch.cuda.empty_cache()

@@ -18,16 +18,30 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Host-role defaults per operator class, from the offline sweep on MI355X
-// (fewest host work-groups that reach the link's full rate, then the smallest
-// window; a deep window also slows concurrent HBM readers the most).
+// Host-role work-group caps per operator class, from the offline sweep on
+// MI355X: the fewest host work-groups that reach the link's full rate.
 struct HostDefaults {
   int host_cus;
-  int window;
 };
-constexpr HostDefaults kGemmFmaDefaults{8, 2};    // split GEMM, N <= 4
-constexpr HostDefaults kGemmMfmaDefaults{16, 1};  // split GEMM, N > 4
-constexpr HostDefaults kAttnDefaults{8, 1};       // split decode attention
+constexpr HostDefaults kGemmFmaDefaults{8};    // split GEMM, N <= 4
+constexpr HostDefaults kGemmMfmaDefaults{16};  // split GEMM, N > 4
+constexpr HostDefaults kAttnDefaults{8};       // split decode attention
+
+// Congestion window when the caller leaves it at 0: the host role as a whole
+// keeps about this many bytes in flight, roughly the link's bandwidth-delay
+// product (57.5 GB/s x ~4.5 us under load).  Fewer host work-groups (small
+// host parts) get deeper windows; many get shallow ones, which also slows
+// concurrent HBM readers the least.
+constexpr uint64_t kHostInflightBytes = 256u << 10;
+
+// Smallest window in {1, 2, 4, ..., max_window} with
+// host_wgs * bytes_per_step_per_wg * window >= kHostInflightBytes.
+inline int auto_window(int64_t host_wgs, uint64_t bytes_per_step_per_wg, int max_window) {
+  int w = 1;
+  while (w < max_window && (uint64_t)(host_wgs > 0 ? host_wgs : 1) * bytes_per_step_per_wg * w < kHostInflightBytes)
+    w <<= 1;
+  return w;
+}
 
 // Resolved launch configuration.
 struct LaunchCfg {

@@ -34,7 +34,7 @@ void clear_error() {
 
 dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* out) {
   out->host_cus = def.host_cus;
-  out->window = def.window;
+  out->window = 0;   // 0: sized by the operator from kHostInflightBytes
   out->flags = 0;
   out->byte_counters = nullptr;
   if (!cfg) return DAK_OK;

@@ -429,10 +429,12 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   a.stream = static_cast<hipStream_t>(stream);
   if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
+  // Host window: one tile is 4 waves x 16 tokens x (K + V) = 32 KiB per work-group.
+  const int window = lc.window ? lc.window : auto_window(a.host_wgs, 32u << 10, G >= 8 ? 1 : G >= 4 ? 2 : 8);
   if (lc.flags & DAK_FLAG_COUNT_BYTES)
-    launch_partial_w<true>(a, G, lc.window);
+    launch_partial_w<true>(a, G, window);
   else
-    launch_partial_w<false>(a, G, lc.window);
+    launch_partial_w<false>(a, G, window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,

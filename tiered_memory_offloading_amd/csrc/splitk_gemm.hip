@@ -164,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fma_split(
 //     consecutive lanes (host memory is not cached by the GPU, so short
 //     pieces would each cross the link as a small request), staged in the
 //     wave's LDS tile and read back as fragments.
+constexpr int kMfmaSlices = 4;                  // K-slices (and waves) per work-group
 constexpr int kChunkSteps = 8;                  // host chunk: 8 steps = 256 k
 constexpr int kStageRow = 256 * 2 + 16;         // bytes per staged row; the pad spreads rows over banks
 constexpr int kStageWave = 16 * kStageRow;      // bytes per wave
@@ -270,9 +271,9 @@ __device__ __forceinline__ void mfma_rows_staged(const uint16_t* __restrict__ a,
   }
 }
 
-// Sum the four K-slice partials in slice order and store y.  `part` is LDS of
-// kWaves * RBW * NB * 64 f32x4.  Waves share the (rb, cb) blocks round-robin.
-template <int NB, int RBW>
+// Sum the S K-slice partials in slice order and store y.  `part` is LDS of
+// S * RBW * NB * 64 f32x4.  Waves share the (rb, cb) blocks round-robin.
+template <int NB, int RBW, int S>
 __device__ __forceinline__ void mfma_reduce_store(f32x4_t (&acc)[RBW][NB], f32x4_t* part, float* __restrict__ y,
                                                   int64_t M, int64_t N, int64_t row0, int wave, int lane) {
   __syncthreads();   // staging tiles alias `part`
@@ -281,11 +282,11 @@ __device__ __forceinline__ void mfma_reduce_store(f32x4_t (&acc)[RBW][NB], f32x4
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) part[((wave * RBW + rb) * NB + cb) * 64 + lane] = acc[rb][cb];
   __syncthreads();
-  for (int blk = wave; blk < RBW * NB; blk += kWaves) {
+  for (int blk = wave; blk < RBW * NB; blk += S) {
     const int rb = blk / NB, cb = blk % NB;
     f32x4_t t = part[((0 * RBW + rb) * NB + cb) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 1; w < S; ++w) {
       const f32x4_t p = part[((w * RBW + rb) * NB + cb) * 64 + lane];
       t[0] += p[0];
       t[1] += p[1];
@@ -299,24 +300,25 @@ __device__ __forceinline__ void mfma_reduce_store(f32x4_t (&acc)[RBW][NB], f32x4
   __syncthreads();   // LDS is reused by the next item
 }
 
-template <int NB, int RBW>
+template <int NB, int RBW, int S>
 constexpr int mfma_lds_bytes() {
-  constexpr int stage = kWaves * kStageWave;
-  constexpr int part = kWaves * RBW * NB * 64 * 16;
+  constexpr int stage = S * kStageWave;
+  constexpr int part = S * RBW * NB * 64 * 16;
   return stage > part ? stage : part;
 }
 
-// Host items are 16 rows (RBW = 1); HBM items are 16*RBW rows.
-template <int NB, int RBW, int UH, int UG, bool COUNT>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_split(
+// S waves per work-group, wave w owning K-slice w.  Host items are 16 rows
+// (RBW = 1); HBM items are 16*RBW rows.
+template <int NB, int RBW, int S, int UH, int UG, bool COUNT>
+__global__ __launch_bounds__(64 * S) void gemm_mfma_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
     int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[mfma_lds_bytes<NB, RBW>()];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[mfma_lds_bytes<NB, RBW, S>()];
   f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t T = (K + 31) >> 5;
-  const int64_t per = (T + kWaves - 1) / kWaves;
+  const int64_t per = (T + S - 1) / S;
   const int64_t sb = std::min<int64_t>(T, wave * per), se = std::min<int64_t>(T, sb + per);
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_split(
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) acc[0][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       mfma_rows_staged<NB, UH, COUNT>(a_host + row * K, K, sb, se, x, N, acc, stage, lane, nbytes);
-      mfma_reduce_store<NB, 1>(acc, part, y, M, N, row, wave, lane);
+      mfma_reduce_store<NB, 1, S>(acc, part, y, M, N, row, wave, lane);
     }
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_split(
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       mfma_rows_direct<NB, RBW, UG, COUNT>(a_hbm + lrow * K, K, sb, se, x, N, acc, lane, nbytes);
-      mfma_reduce_store<NB, RBW>(acc, part, y, M, N, host_rows + lrow, wave, lane);
+      mfma_reduce_store<NB, RBW, S>(acc, part, y, M, N, host_rows + lrow, wave, lane);
     }
   }
   if (COUNT) {
@@ -397,8 +399,9 @@ template <int NB, int RBW, int UH, bool COUNT>
 void launch_mfma_nb(const GemmArgs& g) {
   constexpr int UG = hbm_window<NB, RBW>();
   constexpr int UHc = NB >= 8 ? 1 : (UH > 2 ? 2 : UH);   // chunks in flight (64 VGPRs each)
+  constexpr int S = kMfmaSlices;
   const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_mfma_split<NB, RBW, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_mfma_split<NB, RBW, S, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(64 * S), 0,
                      g.stream, g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items,
                      g.hbm_items, g.counters);
 }
@@ -503,10 +506,14 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   g.stream = static_cast<hipStream_t>(stream);
   if (g.host_wgs + g.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
   if (g.host_wgs + g.hbm_items == 0) return DAK_OK;
+  // Host window: bytes one host work-group loads per step are 4 waves x 4 rows
+  // x 1 KiB (FMA path) or 4 waves x 16 rows x 512 B (MFMA path, at most 2).
+  const int window = lc.window ? lc.window
+                               : (fma ? auto_window(g.host_wgs, 16u << 10, 8) : auto_window(g.host_wgs, 32u << 10, 2));
   if (lc.flags & DAK_FLAG_COUNT_BYTES)
-    launch_any<true>(g, lc.window, fma, nb, rbw);
+    launch_any<true>(g, window, fma, nb, rbw);
   else
-    launch_any<false>(g, lc.window, fma, nb, rbw);
+    launch_any<false>(g, window, fma, nb, rbw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "gemm kernel launch");
   return DAK_OK;

@@ -1,0 +1,185 @@
+"""A decoder's split operators placed across pinned host memory and HBM by the
+planner, and one decode step over them.
+
+DAK paper §3 (Overview, Fig. 4): the global offload ratio follows from the
+footprint and the HBM capacity; the planner of §4.2.2 turns it into per-op
+ratios; each op's weights (tile-rows) or KV cache (requests) are then stored
+across the two tiers and the split kernels run over them.  The walkthrough's
+capacity section gives x_global >= max(0, (M - H) / M).
+
+Per layer the step runs QKV (split GEMM), decode attention (split KV), O,
+gate+up and down (split GEMMs) with N = batch activations.  Norms, rotary
+embeddings, activation functions and residual adds are not part of the split
+operators and are left out; every op reads fixed synthetic activations of its
+shape (the layers are not chained), so the step measures exactly the bytes the
+split operators read.
+
+Weights ~ N(0, 0.02) and KV ~ N(0, 1) are generated on the GPU with a seeded
+device generator, in chunks (HBM is nearly full): fp32 normals, scaled, rounded
+to bf16.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import Op, SplitKV, SplitMatrix, plan_offload, min_offload_ratio, splitk_decode_attn, splitk_gemm
+from . import decode_attn_workspace_bytes
+
+
+@dataclass(frozen=True)
+class DecoderShape:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    layers: int
+
+    def linears(self):
+        """(name, M, K) of the decode linears (QKV and gate+up fused)."""
+        qkv = (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+        return [("qkv", qkv, self.hidden), ("o", self.hidden, self.n_q_heads * self.head_dim),
+                ("gate_up", 2 * self.ffn, self.hidden), ("down", self.hidden, self.ffn)]
+
+
+LLAMA70B = DecoderShape(hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, layers=80)
+LLAMA8B = DecoderShape(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=14336, layers=32)
+
+
+@dataclass
+class OpSlot:
+    layer: int
+    kind: str              # qkv, attn, o, gate_up, down
+    units: int
+    unit_bytes: int
+    host_units: int = 0
+    tensors: dict = field(default_factory=dict)
+    desc: object = None
+
+    @property
+    def bytes(self):
+        return self.units * self.unit_bytes
+
+
+def _fill_normal_(t: torch.Tensor, std: float, gen: torch.Generator, stage: torch.Tensor):
+    """Fill a bf16 tensor (device or pinned host) with std * N(0, 1), one
+    staging-buffer chunk at a time (fp32 normals drawn into `stage`, scaled,
+    rounded to bf16 by the copy)."""
+    flat = t.view(-1)
+    n = flat.numel()
+    chunk = stage.numel()
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        v = stage[:m]
+        torch.randn((m,), generator=gen, out=v)
+        if std != 1.0:
+            v.mul_(std)
+        flat[i:i + m].copy_(v)
+
+
+class DecodeModel:
+    """Weights and KV of a decoder spread over two tiers by the greedy planner."""
+
+    def __init__(self, shape: DecoderShape, batch: int, ctx: int, b_hbm: float, b_host: float,
+                 hbm_bytes: int, m: int = 64, seed: int = 0, t_comp=None, log=print):
+        self.shape, self.batch, self.ctx, self.m = shape, batch, ctx, m
+        self.b_hbm, self.b_host = b_hbm, b_host
+        s = shape
+        kv_unit = 2 * s.n_kv_heads * ctx * s.head_dim * 2      # K and V of one request, one layer
+        self.slots: List[OpSlot] = []
+        lin = s.linears()
+        for layer in range(s.layers):
+            for name, M, K in lin:
+                if name == "o":
+                    self.slots.append(OpSlot(layer, "attn", batch, kv_unit))
+                self.slots.append(OpSlot(layer, name, M // m, m * K * 2))
+        # order within a layer: qkv, attn, o, gate_up, down
+        self.footprint = sum(o.bytes for o in self.slots)
+        self.hbm_bytes = hbm_bytes
+        self.x_global = min_offload_ratio(self.footprint, hbm_bytes)
+        tc = t_comp or (lambda slot: 0.0)
+        ops = [Op(o.units, o.unit_bytes, float(tc(o))) for o in self.slots]
+        self.host_units, self.modeled_s = plan_offload(ops, b_hbm, b_host, self.x_global)
+        for o, h in zip(self.slots, self.host_units):
+            o.host_units = h
+        self.host_bytes = sum(o.host_units * o.unit_bytes for o in self.slots)
+        log(f"footprint {self.footprint / 2**30:.2f} GiB, HBM budget {hbm_bytes / 2**30:.2f} GiB, "
+            f"x_global {self.x_global:.5f}, host {self.host_bytes / 2**30:.3f} GiB, "
+            f"modelled step {self.modeled_s * 1e3:.3f} ms")
+        self._allocate(seed, log)
+
+    # ------------------------------------------------------------------
+    def _allocate(self, seed: int, log):
+        """Allocate every op's two tiers first, then fill them through one
+        staging buffer (interleaving temporaries with the large allocations
+        fragments a nearly full HBM)."""
+        s = self.shape
+        dev = torch.device("cuda")
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        stage = torch.empty((1 << 26,), dtype=torch.float32, device=dev)
+        lin = {name: (M, K) for name, M, K in s.linears()}
+        fills = []
+        for i, o in enumerate(self.slots):
+            if o.kind == "attn":
+                shp = (s.n_kv_heads, self.ctx, s.head_dim)
+                h = o.host_units
+                kh = vh = kg = vg = None
+                if h:
+                    kh = torch.empty((h,) + shp, dtype=torch.bfloat16, pin_memory=True)
+                    vh = torch.empty((h,) + shp, dtype=torch.bfloat16, pin_memory=True)
+                if h < self.batch:
+                    kg = torch.empty((self.batch - h,) + shp, dtype=torch.bfloat16, device=dev)
+                    vg = torch.empty((self.batch - h,) + shp, dtype=torch.bfloat16, device=dev)
+                fills += [(t, 1.0) for t in (kh, vh, kg, vg) if t is not None]
+                o.desc = SplitKV(kh, vh, kg, vg, self.batch, h, s.n_kv_heads, s.head_dim, self.ctx)
+            else:
+                M, K = lin[o.kind]
+                rows = o.host_units * self.m
+                ah = ag = None
+                if rows:
+                    ah = torch.empty((rows, K), dtype=torch.bfloat16, pin_memory=True)
+                if rows < M:
+                    ag = torch.empty((M - rows, K), dtype=torch.bfloat16, device=dev)
+                fills += [(t, 0.02) for t in (ah, ag) if t is not None]
+                o.desc = SplitMatrix(ah, ag, M, K, self.m, o.host_units)
+        log(f"  allocated {len(self.slots)} ops; filling {len(fills)} tensors")
+        for i, (t, std) in enumerate(fills):
+            _fill_normal_(t, std, gen, stage)
+            if i % 100 == 0:
+                log(f"  filled {i + 1}/{len(fills)} tensors")
+        del stage
+        # activations, outputs and workspace shared by all layers
+        self.x = {}
+        self.y = {}
+        for name, (M, K) in lin.items():
+            self.x[name] = (torch.randn((self.batch, K), generator=gen, device=dev) * 1.0).to(torch.bfloat16)
+            self.y[name] = torch.empty((self.batch, M), dtype=torch.float32, device=dev)
+        self.q = torch.randn((self.batch, s.n_q_heads, s.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        self.out = torch.empty((self.batch, s.n_q_heads, s.head_dim), dtype=torch.float32, device=dev)
+        attn0 = next(o for o in self.slots if o.kind == "attn")
+        self.ws = torch.empty((decode_attn_workspace_bytes(attn0.desc, s.n_q_heads),), dtype=torch.uint8,
+                              device=dev)
+        self.scale = 1.0 / math.sqrt(s.head_dim)
+        torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------
+    def step(self, events=None):
+        """One decode step: every layer's five split operators, in order."""
+        for i, o in enumerate(self.slots):
+            if events is not None:
+                events[i][0].record()
+            if o.kind == "attn":
+                splitk_decode_attn(self.q, o.desc, self.scale, out=self.out, ws=self.ws)
+            else:
+                splitk_gemm(o.desc, self.x[o.kind], y=self.y[o.kind])
+            if events is not None:
+                events[i][1].record()
+
+    def op_model_s(self, i: int) -> float:
+        """Modelled time of op i: max((n - h) u / B_hbm, h u / B_host) (T_comp = 0)."""
+        o = self.slots[i]
+        return max((o.units - o.host_units) * o.unit_bytes / self.b_hbm, o.host_units * o.unit_bytes / self.b_host)

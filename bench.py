@@ -276,6 +276,88 @@ def run_llama70b(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+MFMA_BF16_DENSE_TFLOPS = 2500.0   # published MI355X dense bf16 matrix peak
+
+
+def run_prefill(torch, dak, args, b_hbm, b_host):
+    """Compute-bound split GEMM: A 28672x8192 ~N(0, 0.02), B 8192x2048 ~N(0, 1)
+    (x holds B^T, N = 2048), 64-row tile-rows.  The op's compute time at x = 0
+    gives the planner's turning point b (DAK paper §4.2.1: host reads hide
+    behind compute while x C / B_host <= T_comp); the kernel is timed at x = 0,
+    at b / n and on a sweep of x up to 0.75, and its MFMA utilisation reported."""
+    M, K, N = 28672, 8192, 2048
+    n = M // M_TILE
+    C = M * K * 2
+    flops = 2 * M * K * N
+    A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
+    hmax = host_units(3, 4, n)
+    A_host = torch.empty((hmax * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+    A_host.copy_(A[:hmax * M_TILE])
+    y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+
+    def desc(h):
+        return dak.SplitMatrix(A_host[:h * M_TILE] if h else None, A[h * M_TILE:] if h < n else None,
+                               M, K, M_TILE, h)
+
+    def time_h(h, reps):
+        S = desc(h)
+        for _ in range(args.warmup):
+            dak.splitk_gemm(S, X, y=y)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            dak.splitk_gemm(S, X, y=y)
+            e1.record()
+        torch.cuda.synchronize()
+        return statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev)
+
+    reps = max(args.steps, 5)
+    t0 = time_h(0, reps)
+    a, b, mb = dak.op_turning_points(dak.Op(n, C // n, t0 * 1e-3), b_hbm * 1e9, b_host * 1e9)
+    log(f"x=0: {t0:.3f} ms, {flops / t0 / 1e9:.1f} TFLOP/s; turning points a={a} b={b} of n={n}")
+    xs = sorted({(0, 1), (b, n)} | {(kk, 20) for kk in (1, 2, 3, 4, 6, 10, 15)})
+    sweep = []
+    for num, den in xs:
+        h = host_units(num, den, n) if den != n else num
+        t = t0 if h == 0 else time_h(h, reps)
+        model = max(t0, h * (C // n) / (b_host * 1e9) * 1e3)
+        sweep.append({"x": round(h / n, 5), "h": h, "ms": round(t, 4), "TFLOPs": round(flops / t / 1e9, 1),
+                      "slowdown_vs_x0": round(t / t0, 4), "model_ms": round(model, 4),
+                      "frac_of_model": round(model / t, 4)})
+        log(f"x={h / n:.4f} (h={h}): {t:.3f} ms, slowdown {t / t0:.3f}, model {model:.3f} ms")
+    # a library GEMM of the same shape, all in HBM, as context for the MFMA rate
+    Bt = X.t()
+    for _ in range(args.warmup):
+        torch.matmul(A, Bt)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        torch.matmul(A, Bt)
+        e1.record()
+    torch.cuda.synchronize()
+    t_lib = statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev)
+    at_b = next(r for r in sweep if r["h"] == b)
+    tf0 = flops / t0 / 1e9
+    res = {
+        "metric": "TFLOP/s of the compute-bound split GEMM and its slowdown at the planner's host share",
+        "value": round(flops / at_b["ms"] / 1e9, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": at_b["ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "prefill split GEMM A 28672x8192 . B 8192x2048, 64-row tile-rows",
+                   "x": at_b["x"], "h": b, "n": n},
+        "turning_points": {"a": a, "b": b, "memory_bound": mb, "t_comp_ms": round(t0, 4)},
+        "roofline": {"bound": "mfma", "kernel": "gemm_tiled_split", "achieved": round(tf0, 1),
+                     "peak": MFMA_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf0 / MFMA_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                     "ms_per_launch": round(t0, 4), "flops_per_launch": flops},
+        "library_gemm_all_hbm": {"ms": round(t_lib, 4), "TFLOPs": round(flops / t_lib / 1e9, 1),
+                                 "what": "torch.matmul (hipBLASLt) of the same bf16 shape, all operands in HBM"},
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "sweep": sweep,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,8 +367,9 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
-    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b"), default="llama8b-layer",
-                    help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios (own JSON line)")
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill"), default="llama8b-layer",
+                    help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
+                         "the compute-bound 28672x8192x2048 split GEMM (each prints its own JSON line)")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,
                     help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,
@@ -309,6 +392,8 @@ def main(argv=None):
     log(f"B_hbm {b_hbm:.0f} GB/s, B_host {b_host:.2f} GB/s")
     if args.workload == "llama70b":
         return run_llama70b(torch, dak, args, b_hbm, b_host)
+    if args.workload == "prefill":
+        return run_prefill(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

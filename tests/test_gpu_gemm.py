@@ -204,3 +204,87 @@ def test_llama70b_linears_full_size(name, M, K):
     assert torch.equal(y1, y0)
     del A
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Wide activations (N > 256): the tiled MFMA kernel of the compute-bound regime
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N", [257, 300, 512, 1000, 2048])
+def test_wide_n_small_shapes_ragged_all_splits_bit_identical(N):
+    # M = 320 leaves a partial 256-row HBM tile for every split, N is ragged
+    # against the 256-column tile and K = 1000 against the 64-k chunk.
+    M, K, m = 320, 1000, 64
+    A, X = synth.gemm_inputs(M, K, N, seed=100 + N)
+    ref = ref_of(A, X)
+    outs = [run(A, X, m, h) for h in range(M // m + 1)]
+    err = og.normwise_error(outs[0].numpy(), ref)
+    print(f"N={N} normwise error {err:.3e}")
+    assert err <= TOL
+    for h, y in enumerate(outs[1:], 1):
+        assert torch.equal(y, outs[0]), f"h={h} differs from h=0"
+
+
+@pytest.mark.parametrize("M,K,m,N", [(32, 8, 32, 257), (96, 40, 32, 600), (512, 4104, 128, 1536)])
+def test_wide_n_edge_shapes(M, K, m, N):
+    A, X = synth.gemm_inputs(M, K, N, seed=M + K + N)
+    ref = ref_of(A, X)
+    y = run(A, X, m, M // m)             # everything on the host
+    assert og.normwise_error(y.numpy(), ref) <= TOL
+    assert torch.equal(y, run(A, X, m, 0))
+
+
+def test_wide_n_host_bytes_are_read_exactly_once():
+    M, K, N, h = 1024, 1024, 512, 7
+    A, X = synth.gemm_inputs(M, K, N, seed=110)
+    S = dak.place_matrix(A, 64, h)
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    dak.splitk_gemm(S, X.cuda(), cfg=dak.LaunchConfig(byte_counters=cnt))
+    torch.cuda.synchronize()
+    host_b, hbm_b = cnt.tolist()
+    assert host_b == h * 64 * K * 2
+    # HBM tiles are 256 x 256 output blocks: each A panel is loaded once per
+    # 256-column block of the output (from L2 or HBM), host rows exactly once.
+    assert hbm_b == -(-N // 256) * (M - h * 64) * K * 2
+
+
+def test_wide_n_integer_inputs_are_exact():
+    M, K, N = 256, 4096, 512
+    A = synth.int_valued_bf16((M, K), -2, 2, seed=111)
+    X = synth.int_valued_bf16((N, K), -2, 2, seed=112)
+    ref = ref_of(A, X)
+    for h in (0, 2, 4):
+        assert np.array_equal(run(A, X, 64, h).numpy().astype(np.float64), ref)
+
+
+def test_wide_n_windows_and_host_caps_do_not_change_bits():
+    M, K, N = 1024, 3072, 512
+    A, X = synth.gemm_inputs(M, K, N, seed=113)
+    base = run(A, X, 64, 8)
+    for hc in (1, 3, 16, 64):
+        for w in (1, 2):
+            y = run(A, X, 64, 8, cfg=dak.LaunchConfig(host_cus=hc, window=w))
+            assert torch.equal(y, base), (hc, w)
+
+
+def test_compute_bound_prefill_gemm_full_size():
+    # A 28672 x 8192 ~N(0, 0.02), B 8192 x 2048 ~N(0, 1) (x holds B^T, N = 2048),
+    # m = 64.  Sampled rows against the oracle; the whole output bit-identical
+    # for host shares 0, 1/20 and 3/4 of the tile-rows.
+    M, K, N = 28672, 8192, 2048
+    A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
+    g = torch.Generator().manual_seed(9)
+    rows = torch.randint(0, M, (40,), generator=g).tolist() + [0, 31, 32, 255, 256, M - 1]
+    ref = og.gemm_rows(og.to_f64(A[rows]), og.to_f64(X))
+    x = X.contiguous()
+    outs = []
+    for frac in ((0, 1), (1, 20), (3, 4)):
+        S = dak.place_matrix(A, 64, og.host_units(frac, M // 64))
+        outs.append(dak.splitk_gemm(S, x))
+        torch.cuda.synchronize()
+        del S
+    err = og.normwise_error(outs[0][:, rows].cpu().numpy(), ref)
+    print(f"prefill GEMM sampled normwise error {err:.3e}")
+    assert err <= TOL
+    assert torch.equal(outs[1], outs[0]) and torch.equal(outs[2], outs[0])
+    del A, outs
+    torch.cuda.empty_cache()

@@ -26,6 +26,7 @@ struct HostDefaults {
 constexpr HostDefaults kGemmFmaDefaults{8};    // split GEMM, N <= 4
 constexpr HostDefaults kGemmMfmaDefaults{16};  // split GEMM, N > 4
 constexpr HostDefaults kAttnDefaults{8};       // split decode attention
+constexpr HostDefaults kGemmTiledDefaults{32}; // split GEMM, N > 256 (x re-reads limit each host WG)
 
 // Congestion window when the caller leaves it at 0: the host role as a whole
 // keeps about this many bytes in flight, roughly the link's bandwidth-delay

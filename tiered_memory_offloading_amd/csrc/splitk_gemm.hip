@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "device_common.hpp"
+#include "gemm_tiled.hpp"
 
 namespace dak {
 namespace {
@@ -455,11 +456,18 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   const int64_t n_units = M / m;
   if (h < 0 || h > n_units) return fail(DAK_EINVAL, "h=%lld outside [0, %lld]", (long long)h, (long long)n_units);
   if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
-  if (N > 256) return fail(DAK_EUNSUPPORTED, "N=%lld > 256 (large-N path not built)", (long long)N);
+  if (N > tiled_max_n()) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld", (long long)N, (long long)tiled_max_n());
+  if (N > 256 && (m % tiled_host_item_rows()))
+    return fail(DAK_EUNSUPPORTED, "N > 256 needs a tile-row height m that is a multiple of %lld",
+                (long long)tiled_host_item_rows());
   if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
+  // The wide-N kernel addresses 16-row blocks of x with 32-bit byte offsets.
+  if (N > 256 && K >= (int64_t(1) << 25))
+    return fail(DAK_EUNSUPPORTED, "N > 256 needs K < 2^25 (K=%lld)", (long long)K);
   const bool fma = N <= 4;
+  const bool tiled = N > 256;
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, fma ? kGemmFmaDefaults : kGemmMfmaDefaults, &lc);
+  dak_status st = resolve_cfg(cfg, tiled ? kGemmTiledDefaults : fma ? kGemmFmaDefaults : kGemmMfmaDefaults, &lc);
   if (st) return st;
 
   const int64_t host_rows = h * m;
@@ -473,6 +481,27 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   if ((st = check_tier_ptr(x, (uint64_t)N * K * 2, Tier::kDevice, "x", &dx))) return st;
   if ((st = check_tier_ptr(y, (uint64_t)N * M * 4, Tier::kDevice, "y", &dy))) return st;
 
+  if (tiled) {
+    TiledArgs t;
+    t.a_host = static_cast<const uint16_t*>(dh);
+    t.a_hbm = static_cast<const uint16_t*>(dg);
+    t.M = M;
+    t.K = K;
+    t.host_rows = host_rows;
+    t.x = static_cast<const uint16_t*>(dx);
+    t.N = N;
+    t.y = y;
+    t.host_items = host_rows / tiled_host_item_rows();
+    t.host_wgs = (int)host_workgroups(t.host_items, lc.host_cus);
+    t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+    t.stream = static_cast<hipStream_t>(stream);
+    // Host window: one chunk is 32 rows x 512 B = 16 KiB per work-group.
+    const int window = lc.window ? std::min(lc.window, 2) : auto_window(t.host_wgs, 16u << 10, 2);
+    launch_gemm_tiled(t, window, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip((int)e, "tiled gemm kernel launch");
+    return DAK_OK;
+  }
   int nb = 1, rbw = 1;
   int64_t host_item_rows, hbm_item_rows;
   if (fma) {

@@ -1,0 +1,35 @@
+// Interface between the split-GEMM entry point and its LDS-staged MFMA kernel
+// (activations 4 < N <= 64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dak {
+
+struct StagedArgs {
+  const uint16_t* a_host;
+  const uint16_t* a_hbm;
+  int64_t M, K, host_rows;
+  const uint16_t* x;
+  int64_t N;
+  float* y;
+  int host_wgs;
+  int64_t host_items, hbm_items;
+  unsigned long long* counters;
+  hipStream_t stream;
+};
+
+// Largest N the staged kernel takes.
+constexpr int64_t kStagedMaxN = 64;
+// Row blocks (16 rows each) per work item for an M x K matrix with tile-row
+// height m: depends on the shape only, never on the host/HBM split.
+int staged_row_blocks(int64_t M, int64_t m, int64_t N);
+// Default host work-group cap: enough groups that their in-flight chunks
+// cover the host link's bandwidth-delay product.
+int staged_host_cus(int64_t N, int row_blocks);
+// Launch (the ring depth is fixed by the shape).
+void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count);
+
+}  // namespace dak

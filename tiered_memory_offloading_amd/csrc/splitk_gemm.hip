@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "device_common.hpp"
+#include "gemm_staged.hpp"
 #include "gemm_tiled.hpp"
 
 namespace dak {
@@ -466,8 +467,14 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     return fail(DAK_EUNSUPPORTED, "N > 256 needs K < 2^25 (K=%lld)", (long long)K);
   const bool fma = N <= 4;
   const bool tiled = N > 256;
+  const bool staged = !fma && N <= kStagedMaxN;
+  const int staged_rbw = staged ? staged_row_blocks(M, m, N) : 1;
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, tiled ? kGemmTiledDefaults : fma ? kGemmFmaDefaults : kGemmMfmaDefaults, &lc);
+  const HostDefaults def = tiled ? kGemmTiledDefaults
+                           : fma ? kGemmFmaDefaults
+                           : staged ? HostDefaults{staged_host_cus(N, staged_rbw)}
+                                    : kGemmMfmaDefaults;
+  dak_status st = resolve_cfg(cfg, def, &lc);
   if (st) return st;
 
   const int64_t host_rows = h * m;
@@ -500,6 +507,30 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     launch_gemm_tiled(t, window, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail_hip((int)e, "tiled gemm kernel launch");
+    return DAK_OK;
+  }
+  if (staged) {
+    StagedArgs t;
+    t.a_host = static_cast<const uint16_t*>(dh);
+    t.a_hbm = static_cast<const uint16_t*>(dg);
+    t.M = M;
+    t.K = K;
+    t.host_rows = host_rows;
+    t.x = static_cast<const uint16_t*>(dx);
+    t.N = N;
+    t.y = y;
+    const int rbw = staged_rbw;
+    const int64_t item_rows = 16 * rbw;
+    t.host_items = host_rows / item_rows;
+    t.hbm_items = (M - host_rows) / item_rows;
+    t.host_wgs = (int)host_workgroups(t.host_items, lc.host_cus);
+    t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+    t.stream = static_cast<hipStream_t>(stream);
+    if (t.host_wgs + t.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
+    if (t.host_wgs + t.hbm_items == 0) return DAK_OK;
+    launch_gemm_staged(t, rbw, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip((int)e, "staged gemm kernel launch");
     return DAK_OK;
   }
   int nb = 1, rbw = 1;

@@ -1,0 +1,287 @@
+// Split GEMM for skinny activations (4 < N <= 64): y = x . A^T with A's first
+// h tile-rows in pinned host memory, the rest in HBM.
+//
+// DAK paper §4.1 "DAK Design": disjoint work-groups compute disjoint output
+// rows and each reads one tier (Fig. 5b); §4.3.2: a host tile is fetched by one
+// consumer only, so one work-group covers every output column of its rows.
+// The pages stage tiles through shared memory with a TMA producer; on CDNA4
+// the same role is played by the LDS-DMA form of the global load
+// (global_load_lds_dwordx4), which moves 16 bytes per lane straight into LDS
+// without passing through registers.
+//
+// Work item: R = 16 * RB rows x all K x all N.  K is read in chunks of 256
+// (512 contiguous bytes per row: the host link needs long row pieces, and HBM
+// streams them at full rate).  Each chunk of A rows and of the N activation
+// rows is DMA-ed into one slot of an LDS ring of STAGES slots; STAGES - 1
+// chunks are in flight while one is consumed.  The ring depth depends on the
+// shape only (the window of the launch configuration does not apply here); the
+// host role's bytes in flight are set by its work-group count.
+//
+// Arithmetic of one output element y[n][r], identical in both roles:
+//   * K is walked in steps of 32 (step t covers k in [32 t, 32 t + 32));
+//   * the P = 4 / RB waves that share r's 16-row block each accumulate the
+//     steps t with t % P == p (their phase), in increasing t, one
+//     v_mfma_f32_16x16x32_bf16 per step, from 0;
+//   * the P phase sums are added in phase order.
+// Host and HBM work-groups differ only in the base pointer, so outputs are
+// bit-identical for every host/HBM split, host work-group count and window.
+//
+// LDS slots hold rows of 512 bytes with the 16-byte pieces of row r XOR-
+// swizzled by (r & 15), so the 16 lanes that read one MFMA fragment (16 rows,
+// same piece) hit 16 different bank groups.  The DMA writes each instruction's
+// 64 x 16 bytes contiguously; the swizzle is applied by choosing which global
+// piece each lane fetches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device_common.hpp"
+#include "gemm_staged.hpp"
+
+namespace dak {
+namespace {
+
+constexpr int kSWaves = 4;
+constexpr int kSThreads = 64 * kSWaves;
+constexpr int kKC = 256;                 // k per chunk
+constexpr int kRowB = kKC * 2;           // bytes per staged row
+constexpr int kStepsPerChunk = kKC / 32;
+
+template <int NB, int RB>
+struct StagedShape {
+  static constexpr int R = 16 * RB;                 // A rows per item
+  static constexpr int ROWS = R + 16 * NB;          // staged rows per chunk (A, then x)
+  static constexpr int SLOT = ROWS * kRowB;         // bytes per LDS slot
+  static constexpr int INSTR = SLOT / 1024;         // 1 KiB DMA instructions per slot
+  static constexpr int PER_WAVE = INSTR / kSWaves;  // per wave per chunk
+  static constexpr int P = kSWaves / RB;            // k-phases
+  static_assert(INSTR % kSWaves == 0, "every wave issues the same number of DMA instructions");
+  static_assert(PER_WAVE * 2 <= 63, "vmcnt range");
+};
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  Issued
+// through inline assembly so that the compiler adds no conservative waits for
+// the pending LDS writes; the kernel's own vmcnt waits and barriers order them.
+__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+
+// Wait until at most N vector-memory instructions of this wave are pending.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int NB, int RB, bool COUNT>
+struct StagedItem {
+  using S = StagedShape<NB, RB>;
+
+  // DMA chunk c of the item whose first A row is `a` into `slot`.  Pieces past
+  // K and activation rows past N are fetched from an in-bounds address and
+  // masked (K) or never stored (N).
+  static __device__ __forceinline__ void issue(unsigned char* slot, int64_t c, const uint16_t* __restrict__ a,
+                                               const uint16_t* __restrict__ x, int64_t N, int64_t K, int wave,
+                                               int lane, uint64_t& nbytes) {
+#pragma unroll
+    for (int j = 0; j < S::PER_WAVE; ++j) {
+      const int ins = wave * S::PER_WAVE + j;
+      const int r = 2 * ins + (lane >> 5);
+      const int piece = (lane & 31) ^ (r & 15);
+      const int64_t k = c * kKC + piece * 8;
+      const int64_t kk = k < K ? k : 0;
+      const uint16_t* src;
+      if (r < S::R) {
+        src = a + (int64_t)r * K + kk;
+        if (COUNT && k < K) nbytes += 16;
+      } else {
+        const int64_t n = r - S::R;
+        src = x + (n < N ? n : 0) * K + kk;
+      }
+      dma16(src, slot + ins * 1024);
+    }
+  }
+
+  // The steps of chunk c that belong to this wave's phase.
+  static __device__ __forceinline__ void compute(const unsigned char* slot, int64_t c, int64_t K, int rb, int phase,
+                                                 int lane, f32x4_t (&acc)[NB]) {
+    const int i16 = lane & 15, g = lane >> 4;
+    const int ra = 16 * rb + i16;
+#pragma unroll
+    for (int t = 0; t < kStepsPerChunk; ++t) {
+      if (t % S::P != phase) continue;   // uniform
+      const bool kok = c * kKC + 32 * t + 8 * g < K;
+      const int pc = 4 * t + g;
+      uint4 af = *reinterpret_cast<const uint4*>(slot + ra * kRowB + ((pc ^ (ra & 15)) << 4));
+      if (!kok) af = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int rx = S::R + 16 * cb + i16;
+        uint4 xf = *reinterpret_cast<const uint4*>(slot + rx * kRowB + ((pc ^ (rx & 15)) << 4));
+        if (!kok) xf = make_uint4(0, 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc[cb], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int NB, int RB, int STAGES, bool COUNT>
+__global__ __launch_bounds__(kSThreads) void gemm_staged_split(
+    const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
+    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
+    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+  using S = StagedShape<NB, RB>;
+  using I = StagedItem<NB, RB, COUNT>;
+  // One array per slot: the slot a wave reads is then a different object from
+  // the slots being filled, which keeps the compiler's alias reasoning exact.
+  __shared__ __attribute__((aligned(16))) unsigned char s0[S::SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char s1[S::SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char s2[STAGES > 2 ? S::SLOT : 16];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rb = wave % RB, phase = wave / RB;
+  const int64_t nch = (K + kKC - 1) / kKC;
+  uint64_t nbytes = 0;
+  const bool host_role = (int)blockIdx.x < host_wgs;
+  int64_t it = host_role ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - host_wgs;
+  const int64_t items = host_role ? host_items : hbm_items;
+  const int64_t stride = host_role ? host_wgs : items;   // HBM work-groups take one item
+  for (; it < items; it += stride) {
+    const int64_t lrow = it * S::R;
+    const uint16_t* a = (host_role ? a_host : a_hbm) + lrow * K;
+    const int64_t yrow = host_role ? lrow : host_rows + lrow;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    I::issue(s0, 0, a, x, N, K, wave, lane, nbytes);
+    if (STAGES > 2 && nch > 1) I::issue(s1, 1, a, x, N, K, wave, lane, nbytes);
+    // Step for chunk c = c0 + IDX: wait for its DMA (all waves, via the
+    // barrier, which also retires every read of the slot about to be refilled),
+    // refill that slot with chunk c + STAGES - 1, then consume chunk c.
+#define DAK_STAGED_STEP(IDX, RD, WR)                                                             \
+  {                                                                                              \
+    const int64_t c = c0 + IDX;                                                                  \
+    if (c < nch) {                                                                               \
+      const int64_t later = std::min<int64_t>(nch - 1 - c, STAGES - 2);                          \
+      if (later >= 2) vm_wait<2 * S::PER_WAVE>();                                                \
+      else if (later == 1) vm_wait<S::PER_WAVE>();                                               \
+      else vm_wait<0>();                                                                         \
+      __builtin_amdgcn_s_barrier();                                                              \
+      if (c + STAGES - 1 < nch) I::issue(WR, c + STAGES - 1, a, x, N, K, wave, lane, nbytes);    \
+      I::compute(RD, c, K, rb, phase, lane, acc);                                                \
+    }                                                                                            \
+  }
+    for (int64_t c0 = 0; c0 < nch; c0 += STAGES) {
+      if constexpr (STAGES == 2) {
+        DAK_STAGED_STEP(0, s0, s1)
+        DAK_STAGED_STEP(1, s1, s0)
+      } else {
+        DAK_STAGED_STEP(0, s0, s2)
+        DAK_STAGED_STEP(1, s1, s0)
+        DAK_STAGED_STEP(2, s2, s1)
+      }
+    }
+#undef DAK_STAGED_STEP
+    const int i16 = lane & 15, g = lane >> 4;
+    if constexpr (S::P == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t n = 16 * cb + i16;
+        if (n < N) *reinterpret_cast<f32x4_t*>(y + n * M + yrow + 16 * rb + 4 * g) = acc[cb];
+      }
+    } else {
+      // Phase partials through slot 0 (every DMA has landed and every read of
+      // the ring has retired once all waves pass the barrier).
+      __syncthreads();
+      f32x4_t* part = reinterpret_cast<f32x4_t*>(s0);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) part[(wave * NB + cb) * 64 + lane] = acc[cb];
+      __syncthreads();
+      if (phase == 0) {
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          f32x4_t t = acc[cb];
+#pragma unroll
+          for (int p = 1; p < S::P; ++p) {
+            const f32x4_t q = part[((p * RB + rb) * NB + cb) * 64 + lane];
+            t[0] += q[0];
+            t[1] += q[1];
+            t[2] += q[2];
+            t[3] += q[3];
+          }
+          const int64_t n = 16 * cb + i16;
+          if (n < N) *reinterpret_cast<f32x4_t*>(y + n * M + yrow + 16 * rb + 4 * g) = t;
+        }
+      }
+    }
+    __syncthreads();   // the ring is reused by the next item
+  }
+  if (COUNT) {
+    uint64_t v = nbytes;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&counters[host_role ? 0 : 1], (unsigned long long)v);
+  }
+}
+
+// Ring depth: three slots when they fit in half of the CU's LDS (two resident
+// work-groups per CU), else two.  A function of the shape only.
+constexpr int stages_for(int nb, int rb) { return 3 * (16 * rb + 16 * nb) * kRowB <= (80 << 10) ? 3 : 2; }
+
+template <int NB, int RB, bool COUNT>
+void launch_nb_rb(const StagedArgs& g) {
+  constexpr int ST = stages_for(NB, RB);
+  const int64_t grid = g.host_wgs + g.hbm_items;
+  hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items, g.hbm_items,
+                     g.counters);
+}
+
+template <int NB, bool COUNT>
+void launch_nb(const StagedArgs& g, int rbw) {
+  switch (rbw) {
+    case 4: return launch_nb_rb<NB, NB >= 4 ? 2 : 4, COUNT>(g);   // NB = 4 never selects 4
+    case 2: return launch_nb_rb<NB, 2, COUNT>(g);
+    default: return launch_nb_rb<NB, 1, COUNT>(g);
+  }
+}
+
+int nb_of(int64_t N) { return N <= 16 ? 1 : N <= 32 ? 2 : 4; }
+
+template <bool COUNT>
+void launch(const StagedArgs& g, int rbw) {
+  switch (nb_of(g.N)) {
+    case 1: return launch_nb<1, COUNT>(g, rbw);
+    case 2: return launch_nb<2, COUNT>(g, rbw);
+    default: return launch_nb<4, COUNT>(g, rbw);
+  }
+}
+
+}  // namespace
+
+int staged_row_blocks(int64_t M, int64_t m, int64_t N) {
+  // Tall items share each staged activation chunk over more rows; keep at
+  // least 384 items so that the HBM role still spreads over every CU, and a
+  // three-slot ring within the 160 KiB of LDS.
+  for (int r = N > 32 ? 2 : 4; r >= 2; r >>= 1)
+    if (m % (16 * r) == 0 && M / (16 * r) >= 384) return r;
+  return 1;
+}
+
+int staged_host_cus(int64_t N, int row_blocks) {
+  // Enough host work-groups that the chunks they have in flight cover the
+  // link's bandwidth-delay product.
+  const uint64_t inflight = (uint64_t)(stages_for(nb_of(N), row_blocks) - 1) * 16 * row_blocks * kRowB;
+  const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
+  return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
+}
+
+void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count) {
+  if (count)
+    launch<true>(g, row_blocks);
+  else
+    launch<false>(g, row_blocks);
+}
+
+}  // namespace dak

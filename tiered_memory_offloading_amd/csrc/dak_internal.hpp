@@ -26,7 +26,11 @@ struct HostDefaults {
 constexpr HostDefaults kGemmFmaDefaults{8};    // split GEMM, N <= 4
 constexpr HostDefaults kGemmMfmaDefaults{16};  // split GEMM, N > 4
 constexpr HostDefaults kAttnDefaults{8};       // split decode attention
-constexpr HostDefaults kGemmTiledDefaults{32}; // split GEMM, N > 256 (x re-reads limit each host WG)
+// Split GEMM, N > 256: a host item (32 rows x all N) streams all of x through
+// one CU, so it takes several times longer than an HBM tile of the same flops;
+// the host role is given one work-group per item (up to 192) so that it keeps
+// pace with the HBM role.
+constexpr HostDefaults kGemmTiledDefaults{192};
 
 // Congestion window when the caller leaves it at 0: the host role as a whole
 // keeps about this many bytes in flight, roughly the link's bandwidth-delay

@@ -194,29 +194,41 @@ __device__ __forceinline__ void host_item(const uint16_t* __restrict__ a, int64_
 #pragma unroll
         for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(lds + (r + 16 * h) * kHRowB + l32 * 16) = hv[u][h];
         __syncthreads();
-        for (int s = 0; s < kHChunkSteps; ++s) {
-          if (cs + s >= T) break;   // uniform
-          const uint4 a0 = *reinterpret_cast<const uint4*>(lds + i16 * kHRowB + (s * 32 + kq) * 2);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(lds + (16 + i16) * kHRowB + (s * 32 + kq) * 2);
-          const int64_t kx = ((cs + s) << 5) + kq;
+        // The chunk's 8 k-steps in quarter steps of 4 column blocks; the x
+        // fragments of quarter u + 2 are requested before quarter u is
+        // multiplied, so two quarters of loads are in flight behind the MFMAs.
+        constexpr int kQ = kHChunkSteps * 4;
+        uint4 xb[3][4];
+        auto xload = [&](int u, uint4(&dst)[4]) {
+          const int st = u >> 2, qq = u & 3;
+          const int64_t kx = ((cs + st) << 5) + kq;
           // Offset of this lane's fragment inside a 16-row block of x; past K
           // it points beyond every block's extent and the load returns zeros.
-          const int xoff = kx < K ? (int)((i16 * K + kx) * 2) : oob;
-          // x fragments in two halves of kCBW / 2 (register budget).
+          const int xoff = (cs + st < T && kx < K) ? (int)((i16 * K + kx) * 2) : oob;
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            uint4 xv[kCBW / 2];
+          for (int j = 0; j < 4; ++j) {
+            const int cb = 4 * qq + j;
+            dst[j] = cb < cbw ? ld_block(x, N, K, (nb0 + cb) * 16, xoff) : make_uint4(0, 0, 0, 0);
+          }
+        };
+        xload(0, xb[0]);
+        xload(1, xb[1]);
+        uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < kCBW / 2; ++q) {
-              const int cb = half * (kCBW / 2) + q;
-              xv[q] = cb < cbw ? ld_block(x, N, K, (nb0 + cb) * 16, xoff) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kQ; ++u) {
+          if (u + 2 < kQ) xload(u + 2, xb[(u + 2) % 3]);
+          const int st = u >> 2, qq = u & 3;
+          if (cs + st < T) {   // uniform
+            if (qq == 0) {
+              a0 = *reinterpret_cast<const uint4*>(lds + i16 * kHRowB + (st * 32 + kq) * 2);
+              a1 = *reinterpret_cast<const uint4*>(lds + (16 + i16) * kHRowB + (st * 32 + kq) * 2);
             }
 #pragma unroll
-            for (int q = 0; q < kCBW / 2; ++q) {
-              const int cb = half * (kCBW / 2) + q;
+            for (int j = 0; j < 4; ++j) {
+              const int cb = 4 * qq + j;
               if (cb < cbw) {   // uniform
-                acc[0][cb] = mfma(a0, xv[q], acc[0][cb]);
-                acc[1][cb] = mfma(a1, xv[q], acc[1][cb]);
+                acc[0][cb] = mfma(a0, xb[u % 3][j], acc[0][cb]);
+                acc[1][cb] = mfma(a1, xb[u % 3][j], acc[1][cb]);
               }
             }
           }

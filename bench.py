@@ -125,6 +125,35 @@ def run_step(wl, plan, cfg=None, events=None, only=None):
             events[i][1].record()
 
 
+def kernel_traffic(kernel_src: str, key: str):
+    """Per-launch DRAM/link traffic of a kernel from the committed rocprofv3
+    counter summary (profiles/traffic.json), or None when the kernel's source
+    has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f).get(key)
+        with open(os.path.join(ROOT, "tiered_memory_offloading_amd", "csrc", kernel_src), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def calibrate_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, so that a counter run can
+    scale FETCH_SIZE and WRITE_SIZE to bytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def measure_bandwidths(torch, dak):
     """B_hbm (4 GiB device buffer) and B_host (1 GiB pinned) from the probes, GB/s."""
     g = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
@@ -374,6 +403,8 @@ def main(argv=None):
                     help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,
                     help="activation rows N of the split GEMMs (config sweeps use 1, 16, 64)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (scale reference for counter runs)")
     ap.add_argument("--only", choices=OP_ORDER, default=None,
                     help="time one operator of the step (for profiling); the JSON then covers that op only")
     args = ap.parse_args(argv)
@@ -387,6 +418,8 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dak.library()
 
+    if args.calibrate_copy:
+        calibrate_copy(torch)
     log("measuring B_hbm / B_host with the streaming-read probes")
     b_hbm, b_host = measure_bandwidths(torch, dak)
     log(f"B_hbm {b_hbm:.0f} GB/s, B_host {b_host:.2f} GB/s")
@@ -422,19 +455,23 @@ def main(argv=None):
     dom_h = host_units(k, den, dom_n)
     dom_host_bytes = dom_h * (dom_C // dom_n)
     dom_ms = op_ms[i_dom]
+    tr = kernel_traffic("split_attn.hip", f"attn_partial_x{k}_{den}") if dom_name == "attn" else None
+    traffic = tr["bytes_per_launch"] if tr else None
     if dom_h > 0:
         ach = dom_host_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "host-link", "kernel": dom_name, "achieved": round(ach, 3), "peak": PCIE_GEN5_X16_GBPS,
-                "unit": "GB/s", "frac": round(ach / PCIE_GEN5_X16_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / PCIE_GEN5_X16_GBPS, 4), "traffic": traffic,
                 "bytes_per_launch": dom_host_bytes, "ms_per_launch": round(dom_ms, 4),
                 "note": "host-tier bytes of the op (read once) / its average duration; peak = PCIe Gen5 x16 "
                         "per-direction published rate"}
     else:
         ach = dom_C / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": dom_C,
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic, "bytes_per_launch": dom_C,
                 "ms_per_launch": round(dom_ms, 4)}
 
+    if tr:
+        roof["traffic_note"] = tr.get("note", "")
     result = {
         "metric": "effective GB/s (HBM+host) and % of two-tier roofline vs offload ratio x",
         "value": round(value, 3),

@@ -33,18 +33,20 @@ namespace {
 
 constexpr int kTW = 8;                       // waves per work-group
 constexpr int kTT = 64 * kTW;                // threads per work-group
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kRowB = kBK * 2 + 16;          // LDS row stride (bytes): pad spreads rows over banks
-constexpr int kTileA = kBM * kRowB;
-constexpr int kTileB = kBN * kRowB;
-constexpr int kStage = kTileA + kTileB;
-constexpr int kLds = 2 * kStage;             // 144 KiB
+constexpr int kBM = 256, kBN = 256;
+constexpr int kSlotRow = 64;                 // bytes per staged row: one 32-k step
+constexpr int kSlotA = kBM * kSlotRow;       // 16 KiB of A rows
+constexpr int kSlot = kSlotA + kBN * kSlotRow;   // + 16 KiB of x rows
+constexpr int kStages = 4;                   // ring slots: three steps in flight behind the one consumed
+constexpr int kDmaPerWave = kSlot / 1024 / kTW;  // 1 KiB DMA instructions per wave per step
 
 constexpr int kHRows = 32;                   // host item rows
 constexpr int kHChunkSteps = 8;              // host chunk: 8 steps = 256 k
 constexpr int kHRowB = kHChunkSteps * 32 * 2 + 16;
 constexpr int kCBW = 16;                     // max column blocks per wave (N <= 8 * 16 * 16)
-static_assert(kHRows * kHRowB <= kLds, "host staging must fit");
+constexpr int kLds = kStages * kSlot > kHRows * kHRowB ? kStages * kSlot : kHRows * kHRowB;   // 128 KiB
+static_assert(kDmaPerWave * kTW * 1024 == kSlot, "the waves split a slot's DMA evenly");
+static_assert((kStages & (kStages - 1)) == 0, "ring depth is a power of two");
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -53,58 +55,100 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // ---------------------------------------------------------------------------
 // HBM role
 // ---------------------------------------------------------------------------
-// Thread t moves row (t >> 3) + 64 i, 16-byte piece (t & 7) of the A and x
-// tiles (i = 0..3): every row's 128 bytes come from 8 consecutive lanes.
-template <bool COUNT>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
-                                          const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
-                                          int64_t k0, int tid, uint4 (&ra)[4], uint4 (&rb)[4], uint64_t& nbytes) {
-  const int r = tid >> 3, c = tid & 7;
-  const int64_t k = k0 + 8 * c;
-  const bool kok = k < K;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + r + 64 * i;
-    const bool aok = kok && row < P;
-    ra[i] = aok ? ld16(a + row * K + k) : make_uint4(0, 0, 0, 0);
-    if (COUNT && aok) nbytes += 16;
-    const int64_t n = col0 + r + 64 * i;
-    rb[i] = (kok && n < N) ? ld16(x + n * K + k) : make_uint4(0, 0, 0, 0);
-  }
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the DMA
+// form of the load), issued through inline assembly so that the compiler adds
+// no conservative waits for the pending LDS writes; the tile loop's own vmcnt
+// waits and barriers order them.
+__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
 }
 
-__device__ __forceinline__ void store_tile(unsigned char* st, int tid, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
-  const int r = tid >> 3, c = tid & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<uint4*>(st + (r + 64 * i) * kRowB + c * 16) = ra[i];
-    *reinterpret_cast<uint4*>(st + kTileA + (r + 64 * i) * kRowB + c * 16) = rb[i];
-  }
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Steps s0, s0 + 1 (those below T) of the staged chunk for wave (wm, wn).
-__device__ __forceinline__ void mma_chunk(const unsigned char* st, int wm, int wn, int lane, int64_t s0, int64_t T,
-                                          f32x4_t (&acc)[8][4]) {
-  const int i16 = lane & 15, kq = (lane >> 4) * 8;
+// Slot layout: row r (A rows 0..255, then x rows 0..255) holds the step's 32
+// k values as four 16-byte pieces, piece p at position p ^ ((r >> 2) & 3): the
+// 16 lanes that read one MFMA fragment (16 consecutive rows, one piece) then
+// hit 16 different bank groups.
+__device__ __forceinline__ int slot_pos(int r, int piece) { return r * kSlotRow + ((piece ^ ((r >> 2) & 3)) << 4); }
+
+// Per-lane source of this wave's DMA instructions.  Instruction j of wave w
+// moves slot rows 16 (4 (w & 3) + j) .. +15 of A (waves 0-3) or of x (waves
+// 4-7); lane l writes row + l / 4, position l & 3, i.e. global piece
+// (l & 3) ^ ((row >> 2) & 3).  Rows past the matrix read row 0 of the tile
+// (never stored).
+struct TileDma {
+  const uint16_t* src[kDmaPerWave];
+  int piece[kDmaPerWave];
+  bool counted[kDmaPerWave];
+};
+
+__device__ __forceinline__ TileDma tile_dma(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+                                            const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
+                                            int wave, int lane) {
+  TileDma d;
+  const bool is_a = wave < 4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (s0 + j < T) {   // uniform
-      uint4 bf[4];
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int r = 16 * (4 * (wave & 3) + j) + (lane >> 2);
+    d.piece[j] = (lane & 3) ^ ((r >> 2) & 3);
+    const int64_t g = (is_a ? row0 : col0) + r;
+    const bool in = g < (is_a ? P : N);
+    d.src[j] = (is_a ? a : x) + (in ? g : (is_a ? row0 : col0)) * K + d.piece[j] * 8;
+    d.counted[j] = is_a && in;
+  }
+  return d;
+}
+
+// DMA step s (k in [32 s, 32 s + 32)) of the tile into `slot`.  Pieces at or
+// past K (only in a partial last step) are fetched from column 0 (in bounds)
+// and zeroed where they are read.
+template <bool COUNT, bool RAGGED>
+__device__ __forceinline__ void tile_issue(const TileDma& d, int64_t s, int64_t K, unsigned char* slot, int wave,
+                                           uint64_t& nbytes) {
+  unsigned char* base = slot + (wave < 4 ? 0 : kSlotA) + (16 * 4 * (wave & 3)) * kSlotRow;
+  if (!RAGGED || 32 * (s + 1) <= K) {   // uniform: a full step
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        bf[cb] = *reinterpret_cast<const uint4*>(st + kTileA + (wn * 64 + cb * 16 + i16) * kRowB + (32 * j + kq) * 2);
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      dma16(d.src[j] + 32 * s, base + 16 * j * kSlotRow);
+      if (COUNT && d.counted[j]) nbytes += 16;
+    }
+  } else {
 #pragma unroll
-      for (int rb = 0; rb < 8; ++rb) {
-        const uint4 af =
-            *reinterpret_cast<const uint4*>(st + (wm * 128 + rb * 16 + i16) * kRowB + (32 * j + kq) * 2);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
-      }
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const bool kin = 32 * s + 8 * d.piece[j] < K;
+      dma16(d.src[j] + (kin ? 32 * s : -8 * d.piece[j]), base + 16 * j * kSlotRow);
+      if (COUNT && kin && d.counted[j]) nbytes += 16;
     }
   }
 }
 
-template <bool COUNT>
+// One k-step from `slot` for wave (wm, wn): 8 x 4 MFMA blocks.  MASK zeroes
+// the fragments of k at or past K (a partial last step).
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const unsigned char* slot, int wm, int wn, int lane, bool kok,
+                                          f32x4_t (&acc)[8][4]) {
+  const int i16 = lane & 15, g = lane >> 4;
+  uint4 bf[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    bf[cb] = *reinterpret_cast<const uint4*>(slot + kSlotA + slot_pos(wn * 64 + cb * 16 + i16, g));
+    if (MASK && !kok) bf[cb] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) {
+    uint4 af = *reinterpret_cast<const uint4*>(slot + slot_pos(wm * 128 + rb * 16 + i16, g));
+    if (MASK && !kok) af = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
+  }
+}
+
+// RAGGED: K is not a multiple of 32, so the last step is partial.
+template <bool COUNT, bool RAGGED>
 __device__ __forceinline__ void hbm_tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
                                          const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
                                          int64_t M, int64_t host_rows, float* __restrict__ y, unsigned char* lds,
@@ -117,17 +161,27 @@ __device__ __forceinline__ void hbm_tile(const uint16_t* __restrict__ a, int64_t
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t T = (K + 31) >> 5;
-  const int64_t nch = (K + kBK - 1) / kBK;
-  uint4 ra[4], rb[4];
-  load_tile<COUNT>(a, P, row0, x, N, col0, K, 0, tid, ra, rb, nbytes);
-  store_tile(lds, tid, ra, rb);
-  __syncthreads();
-  for (int64_t c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) load_tile<COUNT>(a, P, row0, x, N, col0, K, (c + 1) * kBK, tid, ra, rb, nbytes);
-    mma_chunk(lds + (c & 1) * kStage, wm, wn, lane, 2 * c, T, acc);
-    if (more) store_tile(lds + ((c + 1) & 1) * kStage, tid, ra, rb);
-    __syncthreads();
+  const TileDma d = tile_dma(a, P, row0, x, N, col0, K, wave, lane);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, lds + s * kSlot, wave, nbytes);
+  // Step s: wait for its DMA (every wave's part, via the barrier, which also
+  // retires every read of the slot refilled next), refill that slot with step
+  // s + 3, then consume step s.
+  for (int64_t s = 0; s < T; ++s) {
+    const int64_t later = T - 1 - s;
+    if (later >= kStages - 2)
+      vm_wait<(kStages - 2) * kDmaPerWave>();
+    else if (later == 1)
+      vm_wait<kDmaPerWave>();
+    else
+      vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    const int slot = (int)(s & (kStages - 1));
+    if (s + kStages - 1 < T)
+      tile_issue<COUNT, RAGGED>(d, s + kStages - 1, K, lds + ((slot + kStages - 1) & (kStages - 1)) * kSlot, wave,
+                                nbytes);
+    tile_step<RAGGED>(lds + slot * kSlot, wm, wn, lane, 32 * s + 8 * (lane >> 4) < K, acc);
   }
   const int i16 = lane & 15, r4 = 4 * (lane >> 4);
 #pragma unroll
@@ -247,7 +301,7 @@ __device__ __forceinline__ void host_item(const uint16_t* __restrict__ a, int64_
   __syncthreads();   // LDS is reused by the next item
 }
 
-template <int UH, bool COUNT>
+template <int UH, bool COUNT, bool RAGGED>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
@@ -266,7 +320,7 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const int64_t t = (g % 8) * per_slot + g / 8;
     if (t < tiles_m * tiles_n) {
       const int64_t tm = t / tiles_n, tn = t % tiles_n;
-      hbm_tile<COUNT>(a_hbm, M - host_rows, tm * kBM, x, N, tn * kBN, K, M, host_rows, y, lds, nbytes);
+      hbm_tile<COUNT, RAGGED>(a_hbm, M - host_rows, tm * kBM, x, N, tn * kBN, K, M, host_rows, y, lds, nbytes);
     }
   }
   if (COUNT) {
@@ -281,13 +335,15 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
 template <bool COUNT>
 void launch(const TiledArgs& g, int window) {
   const int64_t grid = g.host_wgs + 8 * g.per_slot;
-#define DAK_TILED(U)                                                                                            \
-  hipLaunchKernelGGL((gemm_tiled_split<U, COUNT>), dim3((unsigned)grid), dim3(kTT), 0, g.stream, g.a_host,     \
+  const bool ragged = (g.K & 31) != 0;
+#define DAK_TILED(U, R)                                                                                         \
+  hipLaunchKernelGGL((gemm_tiled_split<U, COUNT, R>), dim3((unsigned)grid), dim3(kTT), 0, g.stream, g.a_host,  \
                      g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items, g.tiles_m,         \
                      g.tiles_n, g.per_slot, g.cbw, g.counters)
-  switch (window) {
-    case 1: DAK_TILED(1); break;
-    default: DAK_TILED(2); break;
+  if (window == 1) {
+    if (ragged) DAK_TILED(1, true); else DAK_TILED(1, false);
+  } else {
+    if (ragged) DAK_TILED(2, true); else DAK_TILED(2, false);
   }
 #undef DAK_TILED
 }

@@ -265,6 +265,17 @@ dak_status dak_probe_read_concurrent(const void* hbm, size_t hbm_bytes, int32_t 
                                      int32_t host_wgs, int32_t host_window, void* stream,
                                      float* ms_total, float* ms_hbm, float* ms_host);
 
+/* Matrix-core peak probe, the compute roof of the compute-bound split GEMM
+ * (DAK paper §4.2.1 prices such ops by T_comp): `workgroups` work-groups of 4
+ * waves each run 8 independent chains of `iters` v_mfma_f32_16x16x32_bf16 on
+ * register operands.  Median of `reps` event-timed launches in *ms_out; the
+ * bf16 dense rate it implies in *tflops_out (nullable), at whatever clock the
+ * chip holds under that load.  Synchronizes the stream.  DAK_EINVAL for
+ * workgroups outside [1, 65536], iters outside [1, 2^24], reps outside
+ * [1, 1000] or a NULL ms_out. */
+dak_status dak_probe_mfma(int32_t workgroups, int64_t iters, int32_t reps, void* stream, float* ms_out,
+                          double* tflops_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,12 @@ def test_attention_shape_errors_are_reported_before_any_launch():
     kv2 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768)
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 16 * 130 * 4   # 2048-token chunks
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 30) == 0
+
+
+def test_mfma_probe_argument_errors_before_any_launch():
+    lib = dak.library()
+    ms, tf = C.c_float(), C.c_double()
+    assert lib.dak_probe_mfma(0, 16, 1, None, C.byref(ms), C.byref(tf)) == L.DAK_EINVAL
+    assert lib.dak_probe_mfma(4, 0, 1, None, C.byref(ms), C.byref(tf)) == L.DAK_EINVAL
+    assert lib.dak_probe_mfma(4, 16, 0, None, C.byref(ms), C.byref(tf)) == L.DAK_EINVAL
+    assert lib.dak_probe_mfma(4, 16, 1, None, None, None) == L.DAK_EINVAL

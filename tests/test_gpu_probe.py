@@ -49,3 +49,14 @@ def test_allocations_of_4_gib_and_more_validate():
     ms = dak.probe_read(h, 16, 4, reps=1, nbytes=(5 << 30) - 4096)
     assert ms > 0
     del g, h
+
+
+def test_mfma_probe_is_plausible():
+    # 8 independent MFMA chains per wave on every SIMD: the rate must lie
+    # between a third of MI355X's published dense bf16 peak (2.5 PFLOP/s) and
+    # that peak, and scale with the work.
+    ms1, tf1 = dak.probe_mfma(workgroups=1024, iters=2048, reps=3)
+    ms2, tf2 = dak.probe_mfma(workgroups=1024, iters=4096, reps=3)
+    print(f"MFMA probe {tf1:.0f} / {tf2:.0f} TFLOP/s")
+    assert 800 < tf2 < 2600
+    assert 1.6 < ms2 / ms1 < 2.4

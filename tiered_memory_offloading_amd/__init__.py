@@ -268,6 +268,15 @@ def probe_read(buf: torch.Tensor, workgroups: int, window: int, reps: int = 5, n
     return ms.value
 
 
+def probe_mfma(workgroups: int = 1024, iters: int = 4096, reps: int = 5, stream=None):
+    """(median ms, TFLOP/s) of the matrix-core peak probe."""
+    lib = library()
+    ms, tf = C.c_float(), C.c_double()
+    _check(lib.dak_probe_mfma(int(workgroups), int(iters), int(reps), _stream_handle(stream), C.byref(ms),
+                              C.byref(tf)))
+    return ms.value, tf.value
+
+
 def probe_read_concurrent(hbm: torch.Tensor, hbm_wgs: int, hbm_window: int, host: torch.Tensor, host_wgs: int,
                           host_window: int, hbm_bytes: Optional[int] = None, host_bytes: Optional[int] = None,
                           stream=None):

@@ -57,6 +57,8 @@ SIGNATURES = [
     ("dak_probe_read_concurrent", C.c_int32, [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
                                               C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
                                               C.POINTER(C.c_float), C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    ("dak_probe_mfma", C.c_int32, [C.c_int32, C.c_int64, C.c_int32, C.c_void_p, C.POINTER(C.c_float),
+                                   C.POINTER(C.c_double)]),
 ]
 
 _lib = None

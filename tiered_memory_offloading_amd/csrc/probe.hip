@@ -52,6 +52,29 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read(const uint4* __restr
   stream_words<U>(p, n16, blockIdx.x, gridDim.x);
 }
 
+// Matrix-core peak: every wave runs kMfmaChains independent accumulation
+// chains of v_mfma_f32_16x16x32_bf16 on register operands (no memory traffic),
+// `iters` MFMAs per chain; the sums feed a store that never happens.
+constexpr int kMfmaChains = 8;
+typedef __bf16 probe_bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma(int64_t iters) {
+  const uint32_t l = threadIdx.x & 63;
+  const uint4 av = make_uint4(0x3f803f80u ^ l, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  const uint4 bv = make_uint4(0x3f003f00u, 0x3f003f00u ^ l, 0x3f003f00u, 0x3f003f00u);
+  const probe_bf16x8_t a = __builtin_bit_cast(probe_bf16x8_t, av), b = __builtin_bit_cast(probe_bf16x8_t, bv);
+  f32x4_t acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, (float)c};
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) t += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (t == 1.2345e-38f) g_probe_sink[threadIdx.x] = __float_as_uint(t);
+}
+
 // Work-groups [0, host_wgs) stream the host buffer, the rest the HBM buffer;
 // each records its first and last timestamp.
 template <int UH, int UG>
@@ -214,5 +237,40 @@ extern "C" dak_status dak_probe_read_concurrent(const void* hbm, size_t hbm_byte
   *ms_total = ms;
   *ms_host = span(0, host_wgs);
   *ms_hbm = span(host_wgs, grid);
+  return DAK_OK;
+}
+
+extern "C" dak_status dak_probe_mfma(int32_t workgroups, int64_t iters, int32_t reps, void* stream, float* ms_out,
+                                     double* tflops_out) {
+  using namespace dak;
+  clear_error();
+  if (!ms_out) return fail(DAK_EINVAL, "ms_out is NULL");
+  if (workgroups < 1 || workgroups > 65536) return fail(DAK_EINVAL, "workgroups outside [1, 65536]");
+  if (iters < 1 || iters > (int64_t(1) << 24)) return fail(DAK_EINVAL, "iters outside [1, 2^24]");
+  if (reps < 1 || reps > 1000) return fail(DAK_EINVAL, "reps outside [1, 1000]");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Events ev;
+  hipError_t e;
+  if ((e = hipEventCreate(&ev.a)) != hipSuccess || (e = hipEventCreate(&ev.b)) != hipSuccess)
+    return fail_hip((int)e, "hipEventCreate");
+  hipLaunchKernelGGL(probe_mfma, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, s, iters);
+  if ((e = hipGetLastError()) != hipSuccess) return fail_hip((int)e, "probe launch");
+  std::vector<float> ts;
+  for (int r = 0; r < reps; ++r) {
+    if ((e = hipEventRecord(ev.a, s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+    hipLaunchKernelGGL(probe_mfma, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, s, iters);
+    if ((e = hipGetLastError()) != hipSuccess) return fail_hip((int)e, "probe launch");
+    if ((e = hipEventRecord(ev.b, s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+    if ((e = hipEventSynchronize(ev.b)) != hipSuccess) return fail_hip((int)e, "hipEventSynchronize");
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, ev.a, ev.b)) != hipSuccess) return fail_hip((int)e, "hipEventElapsedTime");
+    ts.push_back(ms);
+  }
+  std::sort(ts.begin(), ts.end());
+  *ms_out = ts[ts.size() / 2];
+  if (tflops_out) {
+    const double flops = (double)workgroups * (kProbeThreads / 64) * (double)iters * kMfmaChains * 2.0 * 16 * 16 * 32;
+    *tflops_out = flops / (*ms_out * 1e-3) / 1e12;
+  }
   return DAK_OK;
 }

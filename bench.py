@@ -188,26 +188,63 @@ def host_bytes(wl, k, den):
     return tot
 
 
-def time_steps(torch, wl, plan, steps, warmup, per_op=True, only=None):
-    for _ in range(warmup):
-        run_step(wl, plan, only=only)
-    torch.cuda.synchronize()
-    evs = None
+def capture_step(torch, wl, plan):
+    """The step's launches recorded in one HIP graph (a decode step is replayed
+    this way in serving), or None if capture fails.  The library's entry points
+    allocate nothing and only launch kernels on the given stream, so they
+    record as plain kernel nodes."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_step(wl, plan)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, capture_error_mode="relaxed"):
+            run_step(wl, plan)
+        torch.cuda.synchronize()
+        return g
+    except Exception as e:  # noqa: BLE001 - a failed capture only drops the graph timing
+        log(f"graph capture failed ({e}); reporting no graph timing")
+        torch.cuda.synchronize()
+        return None
+
+
+def time_steps(torch, wl, plan, steps, warmup, per_op=True, only=None, graph=True):
+    """(ms per step, per-op ms, ms per graph-replayed step or None).  The
+    steps are timed as plain stream launches with nothing between them (the
+    fastest mode measured on MI355X); the same step captured in a HIP graph is
+    timed as well when capture works.  Per-op durations come from a separate
+    pass with events around each op, so the events stay out of the timed
+    steps."""
+    g = capture_step(torch, wl, plan) if graph and only is None else None
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    ms = timed(lambda: run_step(wl, plan, only=only))
+    graph_ms = timed(g.replay) if g is not None else None
+    op_ms = None
     if per_op:
         evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
                for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s in range(steps):
-        run_step(wl, plan, events=evs[s] if evs else None, only=only)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-    op_ms = None
-    if evs:
+        for st in range(steps):
+            run_step(wl, plan, events=evs[st], only=only)
+        torch.cuda.synchronize()
         idx = range(5) if only is None else [OP_ORDER.index(only)]
         op_ms = [0.0] * 5
         for i in idx:
-            op_ms[i] = statistics.mean(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps))
-    return dt * 1e3, op_ms
+            op_ms[i] = statistics.mean(evs[st][i][0].elapsed_time(evs[st][i][1]) for st in range(steps))
+    del g
+    return ms, op_ms, graph_ms
 
 
 def cpu_baseline(wl, reps=5):
@@ -440,7 +477,7 @@ def main(argv=None):
     plan = wl.plan(k, den)
     log(f"timing {args.steps} steps at x = {k}/{den}")
     if args.only is not None:
-        ms, op_ms = time_steps(torch, wl, plan, args.steps, args.warmup, only=args.only)
+        ms, op_ms, _ = time_steps(torch, wl, plan, args.steps, args.warmup, only=args.only)
         i = OP_ORDER.index(args.only)
         name, C, n = ops[i]
         h = host_units(k, den, n)
@@ -448,7 +485,7 @@ def main(argv=None):
                           "host_bytes": h * (C // n), "GBps": C / (op_ms[i] * 1e-3) / 1e9,
                           "b_hbm_GBps": b_hbm, "b_host_GBps": b_host}), flush=True)
         return 0
-    ms, op_ms = time_steps(torch, wl, plan, args.steps, args.warmup)
+    ms, op_ms, graph_ms = time_steps(torch, wl, plan, args.steps, args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
     t_roof = two_tier_roofline_ms(wl, k, den, b_hbm, b_host)
     names = [n for n, _, _ in ops]
@@ -484,6 +521,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -505,10 +543,11 @@ def main(argv=None):
         sweep = []
         for kk in range(0, 11):
             p = wl.plan(kk, den)
-            sms, sop = time_steps(torch, wl, p, args.sweep_steps, 1)
+            sms, sop, sgraph = time_steps(torch, wl, p, args.sweep_steps, 1)
             tr = two_tier_roofline_ms(wl, kk, den, b_hbm, b_host)
             sweep.append({"x": kk / den, "GBps": round(step_bytes / (sms * 1e-3) / 1e9, 2),
                           "frac_two_tier": round(tr / sms, 4), "ms": round(sms, 4),
+                          "graph_ms": round(sgraph, 4) if sgraph is not None else None,
                           "op_ms": [round(t, 4) for t in sop]})
             log(f"sweep x={kk / den:.2f}: {sweep[-1]['GBps']} GB/s, {sweep[-1]['frac_two_tier']:.3f} of roofline")
         result["sweep"] = sweep

@@ -106,8 +106,8 @@ dak_status dak_op_turning_points(const dak_op_desc* op, double b_hbm, double b_h
 /* Host work-group count for `items` host work items under a cap of `cap`
  * host work-groups: the G in [1, min(cap, items)] with the fewest waves
  * ceil(items / G), and the smallest such G.  DAK paper §4.1 (wave alignment,
- * congestion cap); walkthrough (waves = ceil(tiles / SMs)).  0 if items <= 0;
- * -1 if cap <= 0. */
+ * congestion cap); walkthrough (waves = ceil(tiles / SMs)).  0 if items <= 0
+ * (whatever the cap); otherwise -1 if cap <= 0. */
 int64_t dak_host_workgroups(int64_t items, int32_t cap);
 
 /* ------------------------------------------------------------------------ */

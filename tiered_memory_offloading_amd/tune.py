@@ -11,6 +11,11 @@ Three measurements, all through the C ABI:
   * the chosen (host_cus, window) per operator class, written as JSON.
 
 Run:  python -m tiered_memory_offloading_amd.tune --out tuning.json
+
+tuning_mi355x.json beside this file is the table measured on MI355X with the
+current kernels; the library's built-in host work-group defaults (8 for the
+GEMV path and attention, the bandwidth-delay rule for the staged GEMM) sit at
+its plateaus.
 """
 from __future__ import annotations
 

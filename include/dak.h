@@ -122,22 +122,25 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  *                  GEMM 4 < N <= 64: the fewest whose staged chunks in flight
  *                  cover about 256 KiB (8 to 32); 64 < N <= 256: 16; split
  *                  attention: 8 (the fewest that reach the full link rate in
- *                  the library's sweep on MI355X); N > 256: 192, i.e. one
- *                  work-group per host item in the compute-bound regime, where
- *                  a host item (32 rows x all N) is compute- rather than
- *                  link-limited
+ *                  the library's sweep on MI355X); N > 256: no cap, the
+ *                  launch picks its group count from a time model of the
+ *                  link and of both roles' rounds.  For N > 256 host
+ *                  work-groups come in groups of ceil(N/256), one per
+ *                  256-column tile of a 256-row block, placed on one XCD so
+ *                  that its L2 serves their repeated reads of the block (the
+ *                  link carries each host byte once); a cap is rounded down
+ *                  to whole groups, at least one
  *   window         host in-flight window: loop steps whose loads a host-role
  *                  wave issues before consuming the first; one of 1, 2, 4, 8.
  *                  0 = sized so that all host work-groups together keep about
  *                  256 KiB in flight (the link's bandwidth-delay product).  A
  *                  step is 512 k of the wave's 4 rows (GEMM, N <= 4), a 256-k
  *                  chunk of its 16 rows (GEMM, 64 < N <= 256, at most 2
- *                  chunks), a 256-k chunk of its 32 rows (GEMM, N > 256, at
- *                  most 2) or 16 tokens of K and V (attention; clamped to what
- *                  registers allow).  The split GEMM for 4 < N <= 64 stages its
- *                  tiles through an LDS ring whose depth is fixed by the
- *                  shape; there the window is accepted and ignored (its host
- *                  bytes in flight follow from host_cus)
+ *                  chunks) or 16 tokens of K and V (attention; clamped to what
+ *                  registers allow).  The split GEMM for 4 < N <= 64 and for
+ *                  N > 256 stages its tiles through LDS rings whose depth is
+ *                  fixed by the kernel; there the window is accepted and
+ *                  ignored (its host bytes in flight follow from host_cus)
  *   flags          bit-or of DAK_FLAG_*
  *   byte_counters  device pointer to 2 uint64 (host bytes, HBM bytes), used
  *                  only with DAK_FLAG_COUNT_BYTES: the kernels add the bytes
@@ -187,14 +190,15 @@ typedef struct {
  *   x   bf16 [N, K] row-major in device memory, 16-byte aligned
  *   N   1 <= N <= 2048.  N <= 64 is the memory-bound (decode) regime; N > 256
  *       the compute-bound one (DAK paper §4.2.1), served by a 256 x 256 tiled
- *       MFMA kernel whose host work-groups own 32 rows x all N
+ *       MFMA kernel with one work-group per CU, whose host groups share each
+ *       host row block through one XCD's L2
  *   y   fp32 [N, M] row-major in device memory, 16-byte aligned; fully written
  *   cfg nullable launch configuration
  * The result depends on (M, K, m, N) and the inputs only: it is bit-identical
  * for every h, host_cus and window.
  * Errors: DAK_EINVAL for shapes/pointers outside the above; DAK_EUNSUPPORTED
- * for N > 2048, for N > 256 with m not a multiple of 32 or K >= 2^25;
- * DAK_EHIP if the launch fails. */
+ * for N > 2048 (or, on a device with fewer than 32 CUs per XCD, an N > 256
+ * whose host group does not fit one XCD); DAK_EHIP if the launch fails. */
 dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, float* y,
                            const dak_launch_cfg* cfg, void* stream);
 

@@ -3,7 +3,9 @@ oracle.  DAK paper §4.1: C = A.B with A's first h tile-rows in pinned host memo
 
 Bars: normwise error max|y - ref| / max|ref| <= 1e-2 against the fp64 oracle;
 bit-identical outputs for every host/HBM split, host CU cap and window; exact
-equality where every partial sum is an integer; host bytes read == h*m*K*2."""
+equality where every partial sum is an integer; host bytes read == h*m*K*2
+(N > 256: requested once per 256-column tile by work-groups that share one
+XCD's L2, and carried over the link once, which the timing test checks)."""
 import numpy as np
 import pytest
 import torch
@@ -224,7 +226,7 @@ def test_wide_n_small_shapes_ragged_all_splits_bit_identical(N):
         assert torch.equal(y, outs[0]), f"h={h} differs from h=0"
 
 
-@pytest.mark.parametrize("M,K,m,N", [(32, 8, 32, 257), (96, 40, 32, 600), (512, 4104, 128, 1536)])
+@pytest.mark.parametrize("M,K,m,N", [(32, 8, 32, 257), (96, 40, 32, 600), (512, 4104, 128, 1536), (48, 264, 16, 300)])
 def test_wide_n_edge_shapes(M, K, m, N):
     A, X = synth.gemm_inputs(M, K, N, seed=M + K + N)
     ref = ref_of(A, X)
@@ -233,7 +235,7 @@ def test_wide_n_edge_shapes(M, K, m, N):
     assert torch.equal(y, run(A, X, m, 0))
 
 
-def test_wide_n_host_bytes_are_read_exactly_once():
+def test_wide_n_bytes_requested_per_column_tile():
     M, K, N, h = 1024, 1024, 512, 7
     A, X = synth.gemm_inputs(M, K, N, seed=110)
     S = dak.place_matrix(A, 64, h)
@@ -241,10 +243,42 @@ def test_wide_n_host_bytes_are_read_exactly_once():
     dak.splitk_gemm(S, X.cuda(), cfg=dak.LaunchConfig(byte_counters=cnt))
     torch.cuda.synchronize()
     host_b, hbm_b = cnt.tolist()
-    assert host_b == h * 64 * K * 2
-    # HBM tiles are 256 x 256 output blocks: each A panel is loaded once per
-    # 256-column block of the output (from L2 or HBM), host rows exactly once.
+    # Both roles compute 256 x 256 output tiles: each A panel is requested once
+    # per 256-column tile of the output.  Host panels are requested by the
+    # work-groups of one host group, which share an XCD's L2.
+    assert host_b == -(-N // 256) * h * 64 * K * 2
     assert hbm_b == -(-N // 256) * (M - h * 64) * K * 2
+
+
+def test_wide_n_host_rows_cross_the_link_once():
+    # All of A on the host, N = 2048: the 8 work-groups of each host group
+    # request every host byte, but the XCD's L2 serves the repeats, so the
+    # launch takes about as long as one streaming read of the host rows (with
+    # no sharing it would take ~8x as long).  Medians of 3; the streaming read
+    # is the library's probe over the same pinned buffer.
+    import statistics
+    M, K, N, m = 4096, 8192, 2048, 64
+    A, X = synth.gemm_inputs(M, K, N, seed=114, device="cuda")
+    S = dak.place_matrix(A, m, M // m)
+    x = X.contiguous()
+    y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    cfg = dak.LaunchConfig(host_cus=16 * 8)   # compute is then far from binding
+    dak.splitk_gemm(S, x, y=y, cfg=cfg)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dak.splitk_gemm(S, x, y=y, cfg=cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t_gemm = statistics.median(ts)
+    t_read = dak.probe_read(S.host, 64, 8, reps=3)
+    print(f"all-host N=2048 GEMM {t_gemm:.3f} ms, one streaming read of its host rows {t_read:.3f} ms")
+    assert t_gemm <= 1.6 * t_read
+    del A, S
+    torch.cuda.empty_cache()
 
 
 def test_wide_n_integer_inputs_are_exact():
@@ -290,23 +324,26 @@ def test_compute_bound_prefill_gemm_full_size():
     torch.cuda.empty_cache()
 
 
-def test_compute_bound_host_share_costs_little_time():
+def test_compute_bound_planner_share_costs_no_time():
     # DAK paper §4.2.1: in the compute-bound regime host reads hide behind the
-    # MFMA work up to the turning point B_h * T_comp / C.  With one host
-    # work-group per 32-row host item (the default for N > 256), a 1/20 host
-    # share of the 28672 x 8192 x 2048 prefill GEMM stays within 25% of the
-    # all-HBM time (measured 1.07-1.11).  Medians of 5 event-timed launches.
+    # MFMA work up to the turning point b = B_host * T_comp / (C / n).  The
+    # planner's b for the 28672 x 8192 x 2048 prefill GEMM (T_comp measured at
+    # x = 0, B_host by the library's streaming probe) must cost at most 10 %
+    # over the all-HBM time (measured 0.97-1.0 with the default 8 host groups).
+    # After a warm-up (the clock climbs under sustained MFMA load), each x > 0
+    # median is paired with an x = 0 median taken just before it; the bar
+    # applies to the median of three such pairs.
     import statistics
+    import time
     M, K, N, m = 28672, 8192, 2048, 64
+    n = M // m
     A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
     y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    S0 = dak.place_matrix(A, m, 0)
 
-    def timed(h):
-        S = dak.place_matrix(A, m, h)
-        dak.splitk_gemm(S, X, y=y)
-        torch.cuda.synchronize()
+    def timed(S, reps=7):
         ts = []
-        for _ in range(5):
+        for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             dak.splitk_gemm(S, X, y=y)
@@ -315,9 +352,23 @@ def test_compute_bound_host_share_costs_little_time():
             ts.append(e0.elapsed_time(e1))
         return statistics.median(ts)
 
-    t0 = timed(0)
-    t1 = timed(og.host_units((1, 20), M // m))
-    print(f"prefill GEMM x=0 {t0:.3f} ms, x=1/20 {t1:.3f} ms, ratio {t1 / t0:.3f}")
-    assert t1 <= 1.25 * t0
-    del A
+    t_end = time.perf_counter() + 1.5
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            dak.splitk_gemm(S0, X, y=y)
+        torch.cuda.synchronize()
+    t0 = timed(S0)
+    probe = torch.empty((256 << 20,), dtype=torch.uint8, pin_memory=True)
+    b_host = probe.numel() / (dak.probe_read(probe, 64, 8, reps=3) * 1e-3)
+    _, b, mb = dak.op_turning_points(dak.Op(n, m * K * 2, t0 * 1e-3), 6.4e12, b_host)
+    assert not mb and 0 < b < n
+    Sb = dak.place_matrix(A, m, b)
+    ratios = []
+    for _ in range(3):
+        t0p = timed(S0)
+        tb = timed(Sb)
+        ratios.append(tb / t0p)
+        print(f"prefill GEMM x=0 {t0p:.3f} ms, planner's x={b / n:.3f} (b={b}) {tb:.3f} ms, ratio {tb / t0p:.3f}")
+    assert statistics.median(ratios) <= 1.10
+    del A, Sb, S0
     torch.cuda.empty_cache()

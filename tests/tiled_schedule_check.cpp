@@ -1,0 +1,113 @@
+// Host-only check of the tiled split GEMM's work-group schedule
+// (tiled_schedule.hpp): over many device sizes, column-tile counts, host group
+// counts and row splits, every host (row block, column tile) pair and every
+// HBM tile is computed by exactly one work-group; the members of a host group
+// share an XCD and cover distinct column tiles; every XCD keeps an HBM
+// work-group; each XCD's HBM share is within one tile of its CU share.
+#include <cstdio>
+#include <initializer_list>
+#include <cstdlib>
+#include <map>
+#include <set>
+#include <vector>
+
+#include "tiled_schedule.hpp"
+
+using namespace dak;
+
+static int fails = 0;
+#define CHECK(c, ...)                    \
+  do {                                   \
+    if (!(c)) {                          \
+      if (fails++ < 20) {                \
+        std::printf("FAIL %s: ", #c);    \
+        std::printf(__VA_ARGS__);        \
+        std::printf("\n");               \
+      }                                  \
+    }                                    \
+  } while (0)
+
+static void check(int cus, int tn, int n_groups, int64_t host_blocks, int64_t hbm_row_tiles) {
+  const int n_xcd = tiled_xcds(cus);
+  const int64_t hbm_tiles = hbm_row_tiles * tn;
+  std::vector<int> host_cover(host_blocks * tn, 0), hbm_cover(hbm_tiles, 0);
+  std::map<int, std::set<int>> group_xcd, group_cols;
+  std::vector<int64_t> hbm_wgs(n_xcd, 0), hbm_share(n_xcd, 0);
+  for (int b = 0; b < cus; ++b) {
+    const TiledWork w = tiled_work(b, cus, n_xcd, n_groups, tn, host_blocks, hbm_tiles);
+    const int xcd = b % n_xcd;
+    if (w.host) {
+      const int q = (int)w.first;
+      CHECK(q >= 0 && q < n_groups, "cus=%d tn=%d g=%d b=%d q=%d", cus, tn, n_groups, b, q);
+      CHECK(w.stride == n_groups && w.end == host_blocks, "b=%d", b);
+      CHECK(w.col_tile >= 0 && w.col_tile < tn, "b=%d col=%d", b, w.col_tile);
+      group_xcd[q].insert(xcd);
+      CHECK(group_cols[q].insert(w.col_tile).second, "group %d repeats column %d", q, w.col_tile);
+      for (int64_t rb = w.first; rb < w.end; rb += w.stride) host_cover[rb * tn + w.col_tile]++;
+    } else {
+      hbm_wgs[xcd]++;
+      CHECK(w.stride >= 1, "cus=%d tn=%d g=%d b=%d stride=%lld", cus, tn, n_groups, b, (long long)w.stride);
+      if (w.stride < 1) continue;
+      CHECK(w.first >= 0 && w.end <= hbm_tiles, "b=%d [%lld, %lld)", b, (long long)w.first, (long long)w.end);
+      for (int64_t t = w.first; t < w.end; t += w.stride) {
+        if (t >= 0 && t < hbm_tiles) hbm_cover[t]++;
+        hbm_share[xcd]++;
+      }
+    }
+  }
+  for (size_t i = 0; i < host_cover.size(); ++i)
+    CHECK(host_cover[i] == 1, "cus=%d tn=%d g=%d host pair %zu covered %d times", cus, tn, n_groups, i, host_cover[i]);
+  for (size_t i = 0; i < hbm_cover.size(); ++i)
+    CHECK(hbm_cover[i] == 1, "cus=%d tn=%d g=%d hbm tile %zu covered %d times", cus, tn, n_groups, i, hbm_cover[i]);
+  if (host_blocks > 0)
+    for (int q = 0; q < n_groups; ++q) {
+      CHECK(group_xcd[q].size() == 1, "group %d spans %zu XCDs", q, group_xcd[q].size());
+      CHECK((int)group_cols[q].size() == tn, "group %d has %zu members", q, group_cols[q].size());
+    }
+  int64_t total = 0;
+  for (int v = 0; v < n_xcd; ++v) {
+    CHECK(hbm_wgs[v] >= 1, "cus=%d tn=%d g=%d: XCD %d has no HBM work-group", cus, tn, n_groups, v);
+    total += hbm_wgs[v];
+  }
+  for (int v = 0; v < n_xcd && total > 0; ++v) {
+    const double want = (double)hbm_tiles * hbm_wgs[v] / total;
+    CHECK(hbm_share[v] >= want - 1.0 && hbm_share[v] <= want + 1.0, "XCD %d share %lld vs %.1f", v,
+          (long long)hbm_share[v], want);
+  }
+}
+
+int main() {
+  int n = 0;
+  const int cus_list[] = {256, 32, 128, 64, 80, 304, 40};
+  for (int cus : cus_list)
+    for (int tn = 2; tn <= 8; ++tn) {
+      const int gmax = tiled_max_groups(cus, tn);
+      for (int g = 0; g <= gmax; ++g)
+        for (int64_t hb : {0, 1, 3, 15, 113})
+          for (int64_t hr : {0, 1, 7, 97, 112}) {
+            if (g == 0 && hb > 0) continue;   // host rows always get a group
+            if (g > 0 && hb == 0) continue;
+            if (g > hb && hb > 0) continue;   // never more groups than row blocks
+            check(cus, tn, g, hb, hr);
+            ++n;
+          }
+    }
+  // The group chooser: within [1, min(cap, blocks, max)], 0 without host rows,
+  // and, for the 28672 x 8192 x 2048 prefill GEMM on 256 CUs, the counts that
+  // measured fastest in the warm paired sweep on MI355X (h tile-rows of 64:
+  // h = 45 -> 6 groups, 52 -> 7, 59 -> 8).
+  CHECK(tiled_choose_groups(256, 8, 0, 112, 8192, 64) == 0, "no host rows");
+  for (int64_t hr : {64, 1000, 2880, 3328, 7168, 28672})
+    for (int cap : {1, 2, 5, 100}) {
+      const int g = tiled_choose_groups(256, 8, hr, (28672 - hr + 255) / 256, 8192, cap);
+      CHECK(g >= 1 && g <= cap && g <= (hr + 255) / 256 && g <= tiled_max_groups(256, 8), "hr=%lld cap=%d g=%d",
+            (long long)hr, cap, g);
+    }
+  CHECK(tiled_choose_groups(256, 8, 45 * 64, (28672 - 45 * 64 + 255) / 256, 8192, 1 << 20) == 6, "h=45");
+  CHECK(tiled_choose_groups(256, 8, 52 * 64, (28672 - 52 * 64 + 255) / 256, 8192, 1 << 20) == 7, "h=52");
+  CHECK(tiled_choose_groups(256, 8, 59 * 64, (28672 - 59 * 64 + 255) / 256, 8192, 1 << 20) == 8, "h=59");
+  // The XCD layout of MI355X: 8 x 32 CUs.
+  CHECK(tiled_xcds(256) == 8 && tiled_max_groups(256, 8) == 24 && tiled_max_groups(256, 2) == 120, "MI355X layout");
+  std::printf("%d configurations, %d failures\n", n, fails);
+  return fails ? 1 : 0;
+}

@@ -26,11 +26,10 @@ struct HostDefaults {
 constexpr HostDefaults kGemmFmaDefaults{8};    // split GEMM, N <= 4
 constexpr HostDefaults kGemmMfmaDefaults{16};  // split GEMM, N > 4
 constexpr HostDefaults kAttnDefaults{8};       // split decode attention
-// Split GEMM, N > 256: a host item (32 rows x all N) streams all of x through
-// one CU, so it takes several times longer than an HBM tile of the same flops;
-// the host role is given one work-group per item (up to 192) so that it keeps
-// pace with the HBM role.
-constexpr HostDefaults kGemmTiledDefaults{192};
+// Split GEMM, N > 256: no cap by default; the launch picks its number of host
+// groups (one work-group per 256-column tile each) from a time model of the
+// link, the groups and the HBM tiles' rounds.
+constexpr int kGemmTiledMaxHostCus = 1 << 30;
 
 // Congestion window when the caller leaves it at 0: the host role as a whole
 // keeps about this many bytes in flight, roughly the link's bandwidth-delay
@@ -56,6 +55,9 @@ struct LaunchCfg {
   uint64_t* byte_counters;
 };
 dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* out);
+
+// Compute units of the current device (queried once per device).
+dak_status device_cus(int* cus);
 
 // Host work-group count under a cap (fewest waves, then fewest groups).
 int64_t host_workgroups(int64_t items, int32_t cap);

@@ -7,6 +7,9 @@
 
 namespace dak {
 
+// Largest N of the split GEMM (N > 256 takes the tiled kernel).
+constexpr int64_t kTiledMaxN = 2048;
+
 struct TiledArgs {
   const uint16_t* a_host;
   const uint16_t* a_hbm;
@@ -14,19 +17,15 @@ struct TiledArgs {
   const uint16_t* x;
   int64_t N;
   float* y;
-  int host_wgs;
-  int64_t host_items;
-  int64_t tiles_m, tiles_n, per_slot;   // filled by launch_gemm_tiled
-  int cbw;                              // filled by launch_gemm_tiled
+  int n_groups;   // host groups of ceil(N/256) work-groups (0 when host_rows == 0)
+  int cus;        // compute units of the device: the grid, one work-group each
   unsigned long long* counters;
   hipStream_t stream;
 };
 
-// Rows per host item of the tiled kernel (the tile-row height must divide by it).
-int64_t tiled_host_item_rows();
-// Largest N the tiled kernel's host role holds in registers.
-int64_t tiled_max_n();
-// Launch; `window` = host chunks loaded ahead (1 or 2).
-void launch_gemm_tiled(TiledArgs& g, int window, bool count);
+// Most host groups a launch on `cus` CUs can hold (each XCD keeps one HBM
+// work-group).
+int tiled_max_host_groups(int64_t N, int cus);
+void launch_gemm_tiled(const TiledArgs& g, bool count);
 
 }  // namespace dak

@@ -1,6 +1,9 @@
 // Host-side runtime helpers of libdak that need the HIP runtime: validation of
-// caller pointers against the tier they are declared to live in.
+// caller pointers against the tier they are declared to live in, and the
+// current device's compute-unit count.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 
 #include "device_common.hpp"
 
@@ -48,6 +51,23 @@ dak_status check_tier_ptr(const void* p, uint64_t bytes, Tier tier, const char* 
     return fail(DAK_EUNSUPPORTED, "%s: pinned memory is not mapped at its host address on the GPU", name);
   }
   *dev = p;
+  return DAK_OK;
+}
+
+dak_status device_cus(int* cus) {
+  static std::atomic<int> cache[64];   // per device id; 0 = not queried yet
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip((int)e, "hipGetDevice");
+  const bool cached = dev >= 0 && dev < 64;
+  int c = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (c <= 0) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail_hip((int)e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    if (c <= 0) return fail(DAK_EHIP, "device %d reports %d compute units", dev, c);
+    if (cached) cache[dev].store(c, std::memory_order_relaxed);
+  }
+  *cus = c;
   return DAK_OK;
 }
 

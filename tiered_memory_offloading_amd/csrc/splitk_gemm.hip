@@ -32,6 +32,7 @@
 #include "device_common.hpp"
 #include "gemm_staged.hpp"
 #include "gemm_tiled.hpp"
+#include "tiled_schedule.hpp"
 
 namespace dak {
 namespace {
@@ -457,20 +458,15 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   const int64_t n_units = M / m;
   if (h < 0 || h > n_units) return fail(DAK_EINVAL, "h=%lld outside [0, %lld]", (long long)h, (long long)n_units);
   if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
-  if (N > tiled_max_n()) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld", (long long)N, (long long)tiled_max_n());
-  if (N > 256 && (m % tiled_host_item_rows()))
-    return fail(DAK_EUNSUPPORTED, "N > 256 needs a tile-row height m that is a multiple of %lld",
-                (long long)tiled_host_item_rows());
+  if (N > kTiledMaxN) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld", (long long)N, (long long)kTiledMaxN);
   if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
-  // The wide-N kernel addresses 16-row blocks of x with 32-bit byte offsets.
-  if (N > 256 && K >= (int64_t(1) << 25))
-    return fail(DAK_EUNSUPPORTED, "N > 256 needs K < 2^25 (K=%lld)", (long long)K);
   const bool fma = N <= 4;
   const bool tiled = N > 256;
   const bool staged = !fma && N <= kStagedMaxN;
   const int staged_rbw = staged ? staged_row_blocks(M, m, N) : 1;
   LaunchCfg lc;
-  const HostDefaults def = tiled ? kGemmTiledDefaults
+  const int tn = (int)((N + 255) / 256);   // column tiles of the tiled kernel
+  const HostDefaults def = tiled ? HostDefaults{kGemmTiledMaxHostCus}
                            : fma ? kGemmFmaDefaults
                            : staged ? HostDefaults{staged_host_cus(N, staged_rbw)}
                                     : kGemmMfmaDefaults;
@@ -498,13 +494,16 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     t.x = static_cast<const uint16_t*>(dx);
     t.N = N;
     t.y = y;
-    t.host_items = host_rows / tiled_host_item_rows();
-    t.host_wgs = (int)host_workgroups(t.host_items, lc.host_cus);
+    if ((st = device_cus(&t.cus))) return st;
+    const int max_groups = tiled_max_host_groups(N, t.cus);
+    if (max_groups < 1)
+      return fail(DAK_EUNSUPPORTED, "N=%lld: a host group of %d work-groups does not fit one XCD of this device",
+                  (long long)N, tn);
+    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, (M - host_rows + 255) / 256, K,
+                                     std::max(1, lc.host_cus / tn));
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.stream = static_cast<hipStream_t>(stream);
-    // Host window: one chunk is 32 rows x 512 B = 16 KiB per work-group.
-    const int window = lc.window ? std::min(lc.window, 2) : auto_window(t.host_wgs, 16u << 10, 2);
-    launch_gemm_tiled(t, window, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+    launch_gemm_tiled(t, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail_hip((int)e, "tiled gemm kernel launch");
     return DAK_OK;

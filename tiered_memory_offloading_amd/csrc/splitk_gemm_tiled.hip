@@ -13,20 +13,36 @@
 // Both roles follow exactly this sequence, so results are bit-identical for
 // any host/HBM split.
 //
-// HBM role: 256 x 256 output tiles, K in chunks of 64 staged through LDS
-// (coalesced 128-byte row pieces, double-buffered), 8 waves of 128 x 64
-// (8 x 4 MFMA blocks each).  Tiles are grouped so that the work-groups of one
-// XCD walk consecutive tiles and share A panels in their L2.
-// Host role: 32 host rows x all N columns per work-group, so each host byte is
-// read once.  Rows are read in 256-k chunks (512 contiguous bytes per row),
-// staged in LDS and shared by the 8 waves; wave w accumulates its share of the
-// column blocks in registers and reads x fragments from L2.
+// Both roles compute 256 x 256 output tiles with 8 waves of 128 x 64 (8 x 4
+// MFMA blocks each), K in 32-k steps staged through LDS by the DMA form of the
+// load.  HBM tiles: a ring of 4 one-step slots, three steps in flight behind
+// the one consumed.  Host tiles: the link moves long row pieces far better
+// than short ones (256 rows x 64 bytes at a time top out near 37 GB/s, 256
+// bytes per row reach the link's 57 GB/s), so A arrives in super-steps of 4
+// k-steps (256 bytes per row) through two 64 KiB super-slots, x in one-step
+// slots.  Only the staging differs; the MFMA sequence is the same.
+//
+// Scheduling: one work-group per CU (the LDS rings admit no second), and
+// work-group b runs on XCD b % n_xcd.  A CU belongs to one role for the whole
+// launch (§4.1's disjoint CU groups):
+//   * host groups: the ceil(N/256) work-groups that compute the column tiles
+//     of one 256-row block of host rows sit on one XCD and start together.
+//     Each requests the block's A rows, but the XCD's L2 serves the repeats,
+//     so every host byte crosses the link once (the L2's read requests to IO
+//     memory per launch equal the host bytes to within 2 %); this plays the
+//     part of §4.3.2's multicast, which CDNA4 lacks, and lets host rows
+//     compute at the full tile rate.  Groups walk the host row blocks with a
+//     static stride;
+//   * the remaining work-groups split the HBM tiles among the XCDs in
+//     proportion to their free CUs, and those of one XCD walk consecutive
+//     tiles (n fastest), sharing A panels in that L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
 #include "device_common.hpp"
 #include "gemm_tiled.hpp"
+#include "tiled_schedule.hpp"
 
 namespace dak {
 namespace {
@@ -35,18 +51,24 @@ constexpr int kTW = 8;                       // waves per work-group
 constexpr int kTT = 64 * kTW;                // threads per work-group
 constexpr int kBM = 256, kBN = 256;
 constexpr int kSlotRow = 64;                 // bytes per staged row: one 32-k step
-constexpr int kSlotA = kBM * kSlotRow;       // 16 KiB of A rows
-constexpr int kSlot = kSlotA + kBN * kSlotRow;   // + 16 KiB of x rows
-constexpr int kStages = 4;                   // ring slots: three steps in flight behind the one consumed
-constexpr int kDmaPerWave = kSlot / 1024 / kTW;  // 1 KiB DMA instructions per wave per step
-
-constexpr int kHRows = 32;                   // host item rows
-constexpr int kHChunkSteps = 8;              // host chunk: 8 steps = 256 k
-constexpr int kHRowB = kHChunkSteps * 32 * 2 + 16;
-constexpr int kCBW = 16;                     // max column blocks per wave (N <= 8 * 16 * 16)
-constexpr int kLds = kStages * kSlot > kHRows * kHRowB ? kStages * kSlot : kHRows * kHRowB;   // 128 KiB
-static_assert(kDmaPerWave * kTW * 1024 == kSlot, "the waves split a slot's DMA evenly");
-static_assert((kStages & (kStages - 1)) == 0, "ring depth is a power of two");
+constexpr int kSlotA = kBM * kSlotRow;       // one step of A rows (or of x rows): 16 KiB
+static_assert(kBN == kBM, "A and x slots have one size");
+constexpr int kDmaPerWave = 2 * kSlotA / 1024 / kTW;   // 1 KiB DMA instructions per wave per step
+static_assert(kDmaPerWave * kTW * 1024 == 2 * kSlotA, "the waves split a step's DMA evenly");
+// HBM tiles: a ring of 4 one-step slots (A rows, then x rows), three steps in
+// flight behind the one consumed.
+constexpr int kHbmStages = 4;
+static_assert((kHbmStages & (kHbmStages - 1)) == 0, "ring depth is a power of two");
+// Host tiles: the link needs long pieces of each row (with 64- or 128-byte
+// pieces from 256 rows at once it tops out near 37 GB/s; from 256 bytes on it
+// reaches its 57 GB/s), so A moves in super-steps of 4 k-steps, 256 bytes per
+// row, through 2 super-slots of 64 KiB; x keeps 2 one-step slots.
+constexpr int kSuper = 4;
+constexpr int kSuperRow = kSuper * kSlotRow;   // 256 bytes
+constexpr int kSuperSlot = kBM * kSuperRow;    // 64 KiB
+constexpr int kHostSX = 2;
+constexpr int kLds = 2 * kSuperSlot + kHostSX * kSlotA;   // 160 KiB
+static_assert(kHbmStages * 2 * kSlotA <= kLds, "the HBM ring fits");
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -103,13 +125,14 @@ __device__ __forceinline__ TileDma tile_dma(const uint16_t* __restrict__ a, int6
   return d;
 }
 
-// DMA step s (k in [32 s, 32 s + 32)) of the tile into `slot`.  Pieces at or
-// past K (only in a partial last step) are fetched from column 0 (in bounds)
-// and zeroed where they are read.
+// DMA step s (k in [32 s, 32 s + 32)) of this wave's rows (A rows for waves
+// 0-3, x rows for 4-7) into `slot`, the part of a ring slot that holds them.  Pieces at or past K
+// (only in a partial last step) are fetched from column 0 (in bounds) and
+// zeroed where they are read.
 template <bool COUNT, bool RAGGED>
 __device__ __forceinline__ void tile_issue(const TileDma& d, int64_t s, int64_t K, unsigned char* slot, int wave,
                                            uint64_t& nbytes) {
-  unsigned char* base = slot + (wave < 4 ? 0 : kSlotA) + (16 * 4 * (wave & 3)) * kSlotRow;
+  unsigned char* base = slot + (16 * 4 * (wave & 3)) * kSlotRow;
   if (!RAGGED || 32 * (s + 1) <= K) {   // uniform: a full step
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
@@ -126,35 +149,72 @@ __device__ __forceinline__ void tile_issue(const TileDma& d, int64_t s, int64_t 
   }
 }
 
-// One k-step from `slot` for wave (wm, wn): 8 x 4 MFMA blocks.  MASK zeroes
-// the fragments of k at or past K (a partial last step).
-template <bool MASK>
-__device__ __forceinline__ void tile_step(const unsigned char* slot, int wm, int wn, int lane, bool kok,
-                                          f32x4_t (&acc)[8][4]) {
+// One k-step from slots `sa` (A rows) and `sx` (x rows) for wave (wm, wn):
+// 8 x 4 MFMA blocks.  MASK zeroes the fragments of k at or past K (a partial
+// last step).
+// WIDE: `sa` is a host super-slot (rows of 256 bytes, 16-byte position
+// p ^ (row & 15) holding piece p) and `ss` the step within it.
+template <bool MASK, bool WIDE>
+__device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigned char* sx, int ss, int wm, int wn,
+                                          int lane, bool kok, f32x4_t (&acc)[8][4]) {
   const int i16 = lane & 15, g = lane >> 4;
   uint4 bf[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    bf[cb] = *reinterpret_cast<const uint4*>(slot + kSlotA + slot_pos(wn * 64 + cb * 16 + i16, g));
+    bf[cb] = *reinterpret_cast<const uint4*>(sx + slot_pos(wn * 64 + cb * 16 + i16, g));
     if (MASK && !kok) bf[cb] = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
-    uint4 af = *reinterpret_cast<const uint4*>(slot + slot_pos(wm * 128 + rb * 16 + i16, g));
+    const int ra = wm * 128 + rb * 16 + i16;
+    uint4 af = WIDE ? *reinterpret_cast<const uint4*>(sa + ra * kSuperRow + (((kSuper * ss + g) ^ i16) << 4))
+                    : *reinterpret_cast<const uint4*>(sa + slot_pos(ra, g));
     if (MASK && !kok) af = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
   }
 }
 
-// RAGGED: K is not a multiple of 32, so the last step is partial.
+// Write a finished tile: rows below P, columns below N.
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[8][4], int64_t P, int64_t row0, int64_t N,
+                                           int64_t col0, int64_t M, int64_t yrow0, float* __restrict__ y, int wm,
+                                           int wn, int lane) {
+  const int i16 = lane & 15, r4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int rb2 = 0; rb2 < 8; ++rb2) {
+    const int64_t row = row0 + wm * 128 + rb2 * 16 + r4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int64_t n = col0 + wn * 64 + cb * 16 + i16;
+      if (n < N && row < P) *reinterpret_cast<f32x4_t*>(y + n * M + yrow0 + row) = acc[rb2][cb];
+    }
+  }
+}
+
+// Wait until this wave's DMA of step s has landed, when up to `later` steps
+// issued after it may still be pending (kDmaPerWave instructions each).
+template <int L>
+__device__ __forceinline__ void wait_step(int64_t later) {
+  if constexpr (L == 0) {
+    vm_wait<0>();
+  } else {
+    if (later >= L) vm_wait<L * kDmaPerWave>();
+    else wait_step<L - 1>(later);
+  }
+}
+
+// HBM tile: output rows [row0, row0 + 256) of the P rows at `a` (written at y
+// rows yrow0 + row), columns [col0, col0 + 256).  A ring of kHbmStages slots,
+// each one step of A rows followed by one step of x rows.  RAGGED: K is not a
+// multiple of 32, so the last step is partial.
 template <bool COUNT, bool RAGGED>
-__device__ __forceinline__ void hbm_tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
-                                         const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
-                                         int64_t M, int64_t host_rows, float* __restrict__ y, unsigned char* lds,
-                                         uint64_t& nbytes) {
+__device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+                                     const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t M,
+                                     int64_t yrow0, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
+  constexpr int kSlot = 2 * kSlotA;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
+  const int half = wave < 4 ? 0 : kSlotA;   // waves 0-3 move A rows, 4-7 x rows
   f32x4_t acc[8][4];
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb)
@@ -163,164 +223,120 @@ __device__ __forceinline__ void hbm_tile(const uint16_t* __restrict__ a, int64_t
   const int64_t T = (K + 31) >> 5;
   const TileDma d = tile_dma(a, P, row0, x, N, col0, K, wave, lane);
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, lds + s * kSlot, wave, nbytes);
+  for (int s = 0; s < kHbmStages - 1; ++s)
+    if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, lds + s * kSlot + half, wave, nbytes);
   // Step s: wait for its DMA (every wave's part, via the barrier, which also
   // retires every read of the slot refilled next), refill that slot with step
-  // s + 3, then consume step s.
+  // s + kHbmStages - 1, then consume step s.
   for (int64_t s = 0; s < T; ++s) {
-    const int64_t later = T - 1 - s;
-    if (later >= kStages - 2)
-      vm_wait<(kStages - 2) * kDmaPerWave>();
-    else if (later == 1)
-      vm_wait<kDmaPerWave>();
-    else
-      vm_wait<0>();
+    wait_step<kHbmStages - 2>(T - 1 - s);
     __builtin_amdgcn_s_barrier();
-    const int slot = (int)(s & (kStages - 1));
-    if (s + kStages - 1 < T)
-      tile_issue<COUNT, RAGGED>(d, s + kStages - 1, K, lds + ((slot + kStages - 1) & (kStages - 1)) * kSlot, wave,
-                                nbytes);
-    tile_step<RAGGED>(lds + slot * kSlot, wm, wn, lane, 32 * s + 8 * (lane >> 4) < K, acc);
+    const int slot = (int)(s & (kHbmStages - 1));
+    if (s + kHbmStages - 1 < T)
+      tile_issue<COUNT, RAGGED>(d, s + kHbmStages - 1, K,
+                                lds + ((slot + kHbmStages - 1) & (kHbmStages - 1)) * kSlot + half, wave, nbytes);
+    tile_step<RAGGED, false>(lds + slot * kSlot, lds + slot * kSlot + kSlotA, 0, wm, wn, lane,
+                             32 * s + 8 * (lane >> 4) < K, acc);
   }
-  const int i16 = lane & 15, r4 = 4 * (lane >> 4);
+  store_tile(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane);
+}
+
+// Host super-step S (k in [128 S, 128 S + 128)) of A-wave w's 64 rows into a
+// super-slot: instruction j moves rows 64 w + 4 j .. + 3, lane l row
+// 64 w + 4 j + l / 16, position l & 15, i.e. global piece (l & 15) ^ (row & 15).
+// Rows at or past P read row row0 (never stored); pieces at or past K read
+// column 0 (zeroed where they are read).
+template <bool COUNT>
+__device__ __forceinline__ void host_a_issue(const uint16_t* __restrict__ a, int64_t P, int64_t row0, int64_t K,
+                                             int64_t S, unsigned char* slot, int wave, int lane, uint64_t& nbytes) {
+  const int pos = lane & 15, rl = lane >> 4;
 #pragma unroll
-  for (int rb2 = 0; rb2 < 8; ++rb2) {
-    const int64_t row = row0 + wm * 128 + rb2 * 16 + r4;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int64_t n = col0 + wn * 64 + cb * 16 + i16;
-      if (n < N && row < P) *reinterpret_cast<f32x4_t*>(y + n * M + host_rows + row) = acc[rb2][cb];
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int r = 64 * wave + 4 * j + rl;
+    const int gp = pos ^ ((4 * j + rl) & 15);
+    const bool in = row0 + r < P;
+    const int64_t k = 128 * S + 8 * gp;
+    const bool kin = k < K;
+    dma16(a + (in ? row0 + r : row0) * K + (kin ? k : 0), slot + (64 * wave + 4 * j) * kSuperRow);
+    if (COUNT && in && kin) nbytes += 16;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Host role
-// ---------------------------------------------------------------------------
-// 16-byte load at byte offset `off` of the 16-row block of x starting at row
-// n0, through a buffer descriptor whose extent ends at row min(N, n0 + 16):
-// offsets past the extent (rows >= N, or the caller's out-of-range marker)
-// return zeros.  The block base and extent are wave-uniform, so only the
-// 32-bit lane offset lives in a vector register.
-__device__ __forceinline__ uint4 ld_block(const uint16_t* x, int64_t N, int64_t K, int64_t n0, int off) {
-  const int64_t rows = N - n0 < 16 ? (N - n0 > 0 ? N - n0 : 0) : 16;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(x + n0 * K), (short)0, (int)(rows * K * 2), 0x00020000);
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
-
-// One item: host rows [row0, row0 + 32) x all N columns.  Thread t loads rows
-// (t >> 5) and (t >> 5) + 16, 16-byte piece (t & 31) of each 256-k chunk.
-template <int U, bool COUNT>
-__device__ __forceinline__ void host_item(const uint16_t* __restrict__ a, int64_t row0, const uint16_t* __restrict__ x,
-                                          int64_t N, int64_t K, int64_t M, float* __restrict__ y, unsigned char* lds,
-                                          int cbw, uint64_t& nbytes) {
+// The tile of `tile` for host rows: A through two super-slots (one super-step
+// in flight while the other is consumed), x through kHostSX one-step slots.
+template <bool COUNT, bool RAGGED>
+__device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+                                          const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
+                                          int64_t M, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
+  static_assert(kHostSX >= 2 && (kHostSX - 2) * kDmaPerWave <= 63, "x ring");
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int i16 = lane & 15, kq = (lane >> 4) * 8;
-  const int r = tid >> 5, l32 = tid & 31;
-  f32x4_t acc[2][kCBW];
+  const int wm = wave >> 2, wn = wave & 3;
+  const bool is_a = wave < 4;
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < kCBW; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t T = (K + 31) >> 5;
-  const int64_t nb0 = (int64_t)wave * cbw;   // first column block of this wave
-  const int oob = (int)(32 * K);               // beyond any block's byte extent (16 K * 2)
-  for (int64_t c0 = 0; c0 < T; c0 += kHChunkSteps * U) {
-    uint4 hv[U][2];
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t T = (K + 31) >> 5, TS = (T + kSuper - 1) / kSuper;
+  const TileDma d = tile_dma(a, P, row0, x, N, col0, K, wave, lane);   // x waves use it
+  unsigned char* const ring_a = lds;
+  unsigned char* const ring_x = lds + 2 * kSuperSlot;
+  if (is_a) {
+    host_a_issue<COUNT>(a, P, row0, K, 0, ring_a, wave, lane, nbytes);
+  } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cs = c0 + u * kHChunkSteps;
-      const int64_t k = (cs << 5) + l32 * 8;
-      const bool ok = (cs < T) && (k < K);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        hv[u][h] = ok ? ld16(a + (row0 + r + 16 * h) * K + k) : make_uint4(0, 0, 0, 0);
-        if (COUNT && ok) nbytes += 16;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cs = c0 + u * kHChunkSteps;
-      if (cs < T) {   // uniform
-        __syncthreads();   // previous chunk's fragments have been read
-#pragma unroll
-        for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(lds + (r + 16 * h) * kHRowB + l32 * 16) = hv[u][h];
-        __syncthreads();
-        // The chunk's 8 k-steps in quarter steps of 4 column blocks; the x
-        // fragments of quarter u + 2 are requested before quarter u is
-        // multiplied, so two quarters of loads are in flight behind the MFMAs.
-        constexpr int kQ = kHChunkSteps * 4;
-        uint4 xb[3][4];
-        auto xload = [&](int u, uint4(&dst)[4]) {
-          const int st = u >> 2, qq = u & 3;
-          const int64_t kx = ((cs + st) << 5) + kq;
-          // Offset of this lane's fragment inside a 16-row block of x; past K
-          // it points beyond every block's extent and the load returns zeros.
-          const int xoff = (cs + st < T && kx < K) ? (int)((i16 * K + kx) * 2) : oob;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int cb = 4 * qq + j;
-            dst[j] = cb < cbw ? ld_block(x, N, K, (nb0 + cb) * 16, xoff) : make_uint4(0, 0, 0, 0);
-          }
-        };
-        xload(0, xb[0]);
-        xload(1, xb[1]);
-        uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < kQ; ++u) {
-          if (u + 2 < kQ) xload(u + 2, xb[(u + 2) % 3]);
-          const int st = u >> 2, qq = u & 3;
-          if (cs + st < T) {   // uniform
-            if (qq == 0) {
-              a0 = *reinterpret_cast<const uint4*>(lds + i16 * kHRowB + (st * 32 + kq) * 2);
-              a1 = *reinterpret_cast<const uint4*>(lds + (16 + i16) * kHRowB + (st * 32 + kq) * 2);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int cb = 4 * qq + j;
-              if (cb < cbw) {   // uniform
-                acc[0][cb] = mfma(a0, xb[u % 3][j], acc[0][cb]);
-                acc[1][cb] = mfma(a1, xb[u % 3][j], acc[1][cb]);
-              }
-            }
-          }
-        }
-      }
-    }
+    for (int s = 0; s < kHostSX - 1; ++s)
+      if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, ring_x + s * kSlotA, wave, nbytes);
   }
-  const int r4 = 4 * (lane >> 4);
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < kCBW; ++cb) {
-      const int64_t n = (nb0 + cb) * 16 + i16;
-      if (cb < cbw && n < N) *reinterpret_cast<f32x4_t*>(y + n * M + row0 + rb * 16 + r4) = acc[rb][cb];
+  // Step s: A waves wait for super-step s / 4 at its first step; x waves for
+  // step s.  After the barrier (every read of step s - 1 retired), the first
+  // step of a super-step refills the other super-slot with the next super-step
+  // and every step refills x's slot of step s - 1.
+  int rx = 0;
+  for (int64_t s = 0; s < T; ++s) {
+    const int ss = (int)(s & (kSuper - 1));
+    const int64_t S = s / kSuper;
+    if (is_a) {
+      if (ss == 0) vm_wait<0>();
+    } else {
+      wait_step<kHostSX - 2>(T - 1 - s);
     }
-  __syncthreads();   // LDS is reused by the next item
+    __builtin_amdgcn_s_barrier();
+    if (is_a) {
+      if (ss == 0 && S + 1 < TS)
+        host_a_issue<COUNT>(a, P, row0, K, S + 1, ring_a + ((S + 1) & 1) * kSuperSlot, wave, lane, nbytes);
+    } else {
+      if (s + kHostSX - 1 < T)
+        tile_issue<COUNT, RAGGED>(d, s + kHostSX - 1, K, ring_x + (rx == 0 ? kHostSX - 1 : rx - 1) * kSlotA, wave,
+                                  nbytes);
+    }
+    tile_step<RAGGED, true>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
+                            32 * s + 8 * (lane >> 4) < K, acc);
+    rx = rx == kHostSX - 1 ? 0 : rx + 1;
+  }
+  store_tile(acc, P, row0, N, col0, M, 0, y, wm, wn, lane);
 }
 
-template <int UH, bool COUNT, bool RAGGED>
+template <bool COUNT, bool RAGGED>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
-    int64_t host_items, int64_t tiles_m, int64_t tiles_n, int64_t per_slot, int cbw,
-    unsigned long long* __restrict__ counters) {
+    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int n_groups, int cus,
+    int n_xcd, unsigned long long* __restrict__ counters) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
-  const bool host_role = (int)blockIdx.x < host_wgs;
+  const int tn = (int)((N + kBN - 1) / kBN);
+  const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, (host_rows + kBM - 1) / kBM,
+                                 (M - host_rows + kBM - 1) / kBM * tn);
+  const bool host_role = w.host;
   if (host_role) {
-    for (int64_t it = blockIdx.x; it < host_items; it += host_wgs)
-      host_item<UH, COUNT>(a_host, it * kHRows, x, N, K, M, y, lds, cbw, nbytes);
+    for (int64_t rb = w.first; rb < w.end; rb += w.stride) {
+      __syncthreads();   // the ring is reused
+      tile_host<COUNT, RAGGED>(a_host, host_rows, rb * kBM, x, N, (int64_t)w.col_tile * kBN, K, M, y, lds, nbytes);
+    }
   } else {
-    // HBM work-group g takes tile (g % 8) * per_slot + g / 8: the work-groups
-    // that land on one XCD walk consecutive tiles (n fastest), sharing A panels.
-    const int64_t g = (int64_t)blockIdx.x - host_wgs;
-    const int64_t t = (g % 8) * per_slot + g / 8;
-    if (t < tiles_m * tiles_n) {
-      const int64_t tm = t / tiles_n, tn = t % tiles_n;
-      hbm_tile<COUNT, RAGGED>(a_hbm, M - host_rows, tm * kBM, x, N, tn * kBN, K, M, host_rows, y, lds, nbytes);
+    for (int64_t t = w.first; t < w.end; t += w.stride) {
+      __syncthreads();   // the ring is reused
+      tile<COUNT, RAGGED>(a_hbm, M - host_rows, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, lds, nbytes);
     }
   }
   if (COUNT) {
@@ -332,38 +348,22 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   }
 }
 
-template <bool COUNT>
-void launch(const TiledArgs& g, int window) {
-  const int64_t grid = g.host_wgs + 8 * g.per_slot;
-  const bool ragged = (g.K & 31) != 0;
-#define DAK_TILED(U, R)                                                                                         \
-  hipLaunchKernelGGL((gemm_tiled_split<U, COUNT, R>), dim3((unsigned)grid), dim3(kTT), 0, g.stream, g.a_host,  \
-                     g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items, g.tiles_m,         \
-                     g.tiles_n, g.per_slot, g.cbw, g.counters)
-  if (window == 1) {
-    if (ragged) DAK_TILED(1, true); else DAK_TILED(1, false);
-  } else {
-    if (ragged) DAK_TILED(2, true); else DAK_TILED(2, false);
-  }
-#undef DAK_TILED
-}
-
 }  // namespace
 
-int64_t tiled_host_item_rows() { return kHRows; }
-int64_t tiled_max_n() { return (int64_t)kTW * kCBW * 16; }
+int tiled_max_host_groups(int64_t N, int cus) { return tiled_max_groups(cus, (int)((N + kBN - 1) / kBN)); }
 
-void launch_gemm_tiled(TiledArgs& g, int window, bool count) {
-  g.tiles_m = (g.M - g.host_rows + kBM - 1) / kBM;
-  g.tiles_n = (g.N + kBN - 1) / kBN;
-  g.per_slot = (g.tiles_m * g.tiles_n + 7) / 8;
-  const int64_t nbt = (g.N + 15) / 16;
-  g.cbw = (int)((nbt + kTW - 1) / kTW);
-  if (g.M - g.host_rows == 0) g.per_slot = 0;
-  if (count)
-    launch<true>(g, window);
-  else
-    launch<false>(g, window);
+void launch_gemm_tiled(const TiledArgs& g, bool count) {
+  const int n_xcd = tiled_xcds(g.cus);
+  const bool ragged = (g.K & 31) != 0;
+#define DAK_TILED(C, R)                                                                                          \
+  hipLaunchKernelGGL((gemm_tiled_split<C, R>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host, g.a_hbm, \
+                     g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.counters)
+  if (count) {
+    if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
+  } else {
+    if (ragged) DAK_TILED(false, true); else DAK_TILED(false, false);
+  }
+#undef DAK_TILED
 }
 
 }  // namespace dak

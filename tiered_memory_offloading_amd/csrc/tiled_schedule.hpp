@@ -1,0 +1,135 @@
+// Work of one work-group of the tiled split GEMM (N > 256).  Plain constexpr
+// C++ (usable from device code and from a host-only build), so the schedule
+// can be checked on the CPU.
+//
+// DAK paper §4.1: disjoint groups of compute units own disjoint output rows,
+// one tier each.  The launch has one work-group per CU; work-group b runs on
+// XCD b % n_xcd as its j = b / n_xcd-th work-group there.
+//   * Host groups q = 0 .. n_groups - 1 sit on XCD q % n_xcd, as that XCD's
+//     work-groups [(q / n_xcd) tn, (q / n_xcd + 1) tn), one per column tile;
+//     group q computes host row blocks q, q + n_groups, ... .
+//   * The other work-groups of an XCD take a contiguous range of the HBM tiles
+//     (row-major, column fastest), sized in proportion to their number, and
+//     walk it with a stride of that number.
+#pragma once
+
+#include <cstdint>
+
+namespace dak {
+
+struct TiledWork {
+  bool host;        // host role: `first`, `end`, `stride` count host row blocks
+  int col_tile;     // host role: the column tile
+  int64_t first, end, stride;   // HBM role: tile indices t = row_tile * tn + col_tile
+};
+
+constexpr int tiled_cus_on(int v, int cus, int n_xcd) { return cus / n_xcd + (v < cus % n_xcd ? 1 : 0); }
+constexpr int tiled_groups_on(int v, int n_groups, int n_xcd) {
+  return n_groups > v ? (n_groups - v + n_xcd - 1) / n_xcd : 0;
+}
+
+// b in [0, cus); tn column tiles; host_blocks 256-row blocks of host rows;
+// hbm_tiles = HBM row tiles * tn.  Requires every XCD to keep at least one
+// HBM work-group: tiled_groups_on(v) * tn < tiled_cus_on(v) for all v.
+constexpr TiledWork tiled_work(int b, int cus, int n_xcd, int n_groups, int tn, int64_t host_blocks,
+                               int64_t hbm_tiles) {
+  const int xcd = b % n_xcd, j = b / n_xcd;
+  const int hw = tiled_groups_on(xcd, n_groups, n_xcd) * tn;
+  if (j < hw) {
+    const int q = (j / tn) * n_xcd + xcd;
+    return TiledWork{true, j % tn, q, host_blocks, n_groups};
+  }
+  int64_t before = 0, total = 0;
+  for (int v = 0; v < n_xcd; ++v) {
+    const int64_t c = tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+    before += v < xcd ? c : 0;
+    total += c;
+  }
+  const int64_t mine = tiled_cus_on(xcd, cus, n_xcd) - hw;
+  return TiledWork{false, 0, hbm_tiles * before / total + (j - hw), hbm_tiles * (before + mine) / total, mine};
+}
+
+// XCDs of a device with `cus` compute units (MI355X: 32 CUs per XCD).
+constexpr int tiled_xcds(int cus) { return cus >= 32 ? cus / 32 : 1; }
+
+// Most host groups that leave every XCD at least one HBM work-group.
+constexpr int tiled_max_groups(int cus, int tn) {
+  const int n_xcd = tiled_xcds(cus);
+  const int per = (cus / n_xcd - 1) / tn;
+  return per > 0 ? n_xcd * per : 0;
+}
+
+}  // namespace dak
+
+namespace dak {
+
+// Time model used to pick the number of host groups (the choice only places
+// work; results do not depend on it).  Constants measured on MI355X with the
+// 28672 x 8192 x 2048 prefill GEMM (warm clocks): one 32-k step of a 256 x 256
+// tile takes ~0.92 us; a group streams ~10 GB/s of host rows when the link is
+// not the limit (one 64 KiB super-step in flight); the link carries ~55 GB/s.
+struct TiledCost {
+  double step_us;
+  double group_gbps;
+  double link_gbps;
+};
+inline constexpr TiledCost kTiledCostMi355x{0.92, 10.0, 55.0};
+
+constexpr double tiled_max_d(double a, double b) { return a > b ? a : b; }
+
+// Predicted microseconds of a launch with `n_groups` host groups: host row
+// blocks go round by round to the groups (a round lasts as long as a tile, as
+// one group's stream of a block, or as the link needs for all active groups'
+// blocks, whichever is longest); each XCD's HBM work-groups run their share
+// of the HBM tiles in whole rounds of one tile.
+constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_row_tiles, int64_t K,
+                                  TiledCost c) {
+  const int n_xcd = tiled_xcds(cus);
+  const double t_tile = (double)((K + 31) / 32) * c.step_us;
+  const double block_bytes = 256.0 * (double)K * 2.0;
+  double t_host = 0.0;
+  int64_t left = (host_rows + 255) / 256;
+  while (left > 0) {
+    const int64_t active = left < n_groups ? left : n_groups;
+    t_host += tiled_max_d(t_tile, tiled_max_d(block_bytes / (c.group_gbps * 1e3),
+                                              (double)active * block_bytes / (c.link_gbps * 1e3)));
+    left -= active;
+  }
+  const int64_t tiles = hbm_row_tiles * tn;
+  int64_t total = 0;
+  for (int v = 0; v < n_xcd; ++v) total += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+  double t_hbm = 0.0;
+  int64_t before = 0;
+  for (int v = 0; v < n_xcd; ++v) {
+    const int64_t w = tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+    const int64_t share = tiles * (before + w) / total - tiles * before / total;
+    before += w;
+    t_hbm = tiled_max_d(t_hbm, (double)((share + w - 1) / w) * t_tile);
+  }
+  return tiled_max_d(t_host, t_hbm);
+}
+
+// Host groups for a launch: the count in [1, cap] (and at most one per host
+// row block) with the least predicted time, the fewest on ties; 0 without
+// host rows.
+constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_row_tiles, int64_t K, int cap,
+                                  TiledCost c = kTiledCostMi355x) {
+  if (host_rows <= 0) return 0;
+  const int64_t blocks = (host_rows + 255) / 256;
+  int hi = tiled_max_groups(cus, tn);
+  if (cap < hi) hi = cap;
+  if (blocks < hi) hi = (int)blocks;
+  if (hi < 1) hi = 1;
+  int best = 1;
+  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_row_tiles, K, c);
+  for (int g = 2; g <= hi; ++g) {
+    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_row_tiles, K, c);
+    if (t < best_t * (1.0 - 1e-9)) {
+      best = g;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+}  // namespace dak

@@ -382,7 +382,7 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     # load; warm it up, then time every host share right after an x = 0
     # measurement of its own, so that each slowdown compares like with like.
     S0 = desc(0)
-    t_end = time.perf_counter() + 1.5
+    t_end = time.perf_counter() + args.warm_seconds
     while time.perf_counter() < t_end:
         for _ in range(20):
             dak.splitk_gemm(S0, X, y=y)
@@ -390,7 +390,7 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     t0s = [time_h(0, reps)]
     a, b, mb = dak.op_turning_points(dak.Op(n, C // n, t0s[0] * 1e-3), b_hbm * 1e9, b_host * 1e9)
     log(f"x=0: {t0s[0]:.3f} ms, {flops / t0s[0] / 1e9:.1f} TFLOP/s; turning points a={a} b={b} of n={n}")
-    xs = sorted({(b, n)} | {(kk, 20) for kk in (1, 2, 3, 4, 6, 10, 15)})
+    xs = sorted({(b, n)} | (set() if args.no_sweep else {(kk, 20) for kk in (1, 2, 3, 4, 6, 10, 15)}))
     sweep = []
     for num, den in xs:
         h = host_units(num, den, n) if den != n else num
@@ -454,6 +454,8 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=1.5,
+                    help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
     ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill"), default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM (each prints its own JSON line)")

@@ -445,6 +445,89 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_linears(torch, dak, args, b_hbm, b_host):
+    """The Llama-8B decode linears one by one (QKV 6144x4096, O 4096x4096, gate+up
+    28672x4096, down 4096x14336; A ~N(0, 0.02), x [N, K] ~N(0, 1)) at N in
+    {1, 16, 64} and x = k/20 for k = 0..10, and the 1024x1024 GEMV (N = 1, x = 0
+    and 1/4) hot and cold.  Cold: every launch reads a different copy of the
+    HBM part (at least 1 GiB of copies in rotation, beyond the memory-side
+    cache); host bytes always cross the link.  Each point is the mean over
+    `--sweep-steps` rotations of all copies after one untimed rotation; outputs
+    at every x are checked bit-identical to x = 0."""
+    reps = max(1, args.sweep_steps)
+
+    def timed(descs, x, y):
+        for S in descs:
+            dak.splitk_gemm(S, x, y=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for S in descs:
+                dak.splitk_gemm(S, x, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(descs))
+
+    points = []
+    ops = [("gemv_cfg1", 1024, 1024)] + list(synth.LLAMA8B_LINEARS)
+    for oi, (name, M, K) in enumerate(ops):
+        n = M // M_TILE
+        C = M * K * 2
+        copies = max(2, -(-(1 << 30) // C))
+        A = synth.gemm_inputs(M, K, 1, seed=oi, device="cuda")[0]
+        As = [A] + [A.clone() for _ in range(copies - 1)]
+        hmax = host_units(1, 2, n)
+        A_host = torch.empty((hmax * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+        A_host.copy_(A[:hmax * M_TILE])
+        ns = (1,) if name == "gemv_cfg1" else (1, 16, 64)
+        ks = (0, 5) if name == "gemv_cfg1" else tuple(range(11))
+        for N in ns:
+            X = synth.gemm_inputs(M, K, N, seed=oi, device="cuda")[1].contiguous()
+            y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+            ref = None
+            for k in ks:
+                h = host_units(k, 20, n)
+                descs = [dak.SplitMatrix(A_host[:h * M_TILE] if h else None, a[h * M_TILE:] if h < n else None,
+                                         M, K, M_TILE, h) for a in As]
+                t = timed(descs, X, y)
+                if ref is None:
+                    ref = y.clone()
+                same = bool(torch.equal(y, ref))
+                t_roof = max((n - h) * (C // n) / (b_hbm * 1e9), h * (C // n) / (b_host * 1e9)) * 1e3
+                pt = {"op": name, "M": M, "K": K, "N": N, "x": round(h / n, 4), "h": h, "ms": round(t, 5),
+                      "GBps": round(C / (t * 1e-3) / 1e9, 2), "frac_two_tier": round(t_roof / t, 4),
+                      "frac_b_hbm_at_x0": round(t_roof / t, 4) if h == 0 else None, "bit_identical_to_x0": same,
+                      "cold_copies": copies}
+                if name == "gemv_cfg1":
+                    pt["hot_ms"] = round(timed(descs[:1], X, y), 5)
+                points.append(pt)
+                log(f"{name} N={N} x={h / n:.3f}: {t * 1e3:.1f} us, {pt['GBps']:.0f} GB/s, "
+                    f"{pt['frac_two_tier']:.3f} of roofline{'' if same else ' BITS DIFFER'}")
+            del X, y
+        del A, As, A_host
+        torch.cuda.empty_cache()
+    cfg2 = [p for p in points if p["op"] != "gemv_cfg1"]
+    worst_x_pos = min(p["frac_two_tier"] for p in cfg2 if p["x"] > 0)
+    x0 = [p for p in cfg2 if p["h"] == 0]
+    res = {
+        "metric": "effective GB/s (HBM+host) and % of two-tier roofline vs offload ratio x, per decode linear",
+        "value": round(statistics.mean(p["frac_two_tier"] for p in cfg2 if p["x"] > 0), 4),
+        "unit": "mean fraction of the two-tier roofline over N in {1,16,64}, 4 ops, x = 0.05..0.5",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "Llama-8B decode linears QKV 6144x4096, O 4096x4096, gate+up 28672x4096, "
+                               "down 4096x14336 at N in {1,16,64}, x = k/20 (k = 0..10), 64-row tile-rows, cold; "
+                               "plus the 1024x1024 GEMV (N = 1, x = 0 and 1/4) hot and cold"},
+        "worst_frac_two_tier_x_pos": worst_x_pos,
+        "frac_b_hbm_at_x0": {f"{p['op']}_N{p['N']}": p["frac_two_tier"] for p in x0},
+        "all_bit_identical_across_x": all(p["bit_identical_to_x0"] for p in points),
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "points": points,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,9 +539,11 @@ def main(argv=None):
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
-    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill"), default="llama8b-layer",
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears"),
+                    default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
-                         "the compute-bound 28672x8192x2048 split GEMM (each prints its own JSON line)")
+                         "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
+                         "at N in {1,16,64} over x = 0..0.5, cold (each prints its own JSON line)")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,
                     help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,
@@ -487,6 +572,8 @@ def main(argv=None):
         return run_llama70b(torch, dak, args, b_hbm, b_host)
     if args.workload == "prefill":
         return run_prefill(torch, dak, args, b_hbm, b_host)
+    if args.workload == "linears":
+        return run_linears(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

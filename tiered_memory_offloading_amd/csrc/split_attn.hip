@@ -430,7 +430,11 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   a.stream = static_cast<hipStream_t>(stream);
   if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
   // Host window: one tile is 4 waves x 16 tokens x (K + V) = 32 KiB per work-group.
-  const int window = lc.window ? lc.window : auto_window(a.host_wgs, 32u << 10, G >= 8 ? 1 : G >= 4 ? 2 : 8);
+  // Without host work-groups the window does not apply; the one-tile instance
+  // needs the fewest registers (more waves per SIMD for the HBM role).
+  const int window = lc.window         ? lc.window
+                     : a.host_wgs == 0 ? 1
+                                       : auto_window(a.host_wgs, 32u << 10, G >= 8 ? 1 : G >= 4 ? 2 : 8);
   if (lc.flags & DAK_FLAG_COUNT_BYTES)
     launch_partial_w<true>(a, G, window);
   else

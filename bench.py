@@ -528,6 +528,81 @@ def run_linears(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_plan_compare(torch, dak, args, b_hbm, b_host):
+    """Greedy per-op ratios against one uniform ratio (DAK §4.2.2 and its
+    evaluation of per-op ratios at large batch): one Llama-8B decoder layer at
+    batch `--plan-batch` (its linears then run at N = batch) over
+    `--plan-ctx` tokens per request, with the same global host share x for
+    both plans.  T_comp of each GEMM is its measured all-HBM time when that
+    exceeds its HBM streaming time by 20 % (compute-bound), else 0; attention
+    is memory-bound (T_comp = 0).  Each plan's step is timed and set beside
+    the model's time for it."""
+    from tiered_memory_offloading_amd.model import LLAMA8B_ONE_LAYER, DecodeModel
+    batch, ctx = args.plan_batch, args.plan_ctx
+    free, _ = torch.cuda.mem_get_info()
+
+    def time_model(mdl):
+        for _ in range(args.warmup):
+            mdl.step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            mdl.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in mdl.slots]
+        mdl.step(events=evs)
+        torch.cuda.synchronize()
+        return ms, [a.elapsed_time(b) for a, b in evs]
+
+    log(f"all-HBM layer at batch {batch}, ctx {ctx}: per-op times for T_comp")
+    base = DecodeModel(LLAMA8B_ONE_LAYER, batch, ctx, b_hbm * 1e9, b_host * 1e9, free, x_global=0.0, log=log)
+    _, op0 = time_model(base)
+    t_comp = {}
+    for o, t in zip(base.slots, op0):
+        stream_ms = o.bytes / (b_hbm * 1e9) * 1e3
+        t_comp[o.kind] = t * 1e-3 if (o.kind != "attn" and t > 1.2 * stream_ms) else 0.0
+        log(f"  {o.kind}: {t:.3f} ms all-HBM, streaming {stream_ms:.3f} ms, T_comp {t_comp[o.kind] * 1e3:.3f} ms")
+    footprint = base.footprint
+    del base
+    torch.cuda.empty_cache()
+    rows = []
+    for xg in args.plan_x:
+        row = {"x_global": xg}
+        for policy in ("uniform", "greedy"):
+            mdl = DecodeModel(LLAMA8B_ONE_LAYER, batch, ctx, b_hbm * 1e9, b_host * 1e9, free, x_global=xg,
+                              policy=policy, t_comp=lambda o: t_comp[o.kind], log=lambda *_: None)
+            ms, op_ms = time_model(mdl)
+            row[policy] = {"ms": round(ms, 4), "modeled_ms": round(mdl.modeled_s * 1e3, 4),
+                           "host_bytes": mdl.host_bytes,
+                           "host_units": {o.kind: o.host_units for o in mdl.slots},
+                           "op_ms": {o.kind: round(t, 4) for o, t in zip(mdl.slots, op_ms)}}
+            log(f"x_global {xg}: {policy:7s} {ms:.3f} ms (model {mdl.modeled_s * 1e3:.3f}), host units "
+                + ", ".join(f"{o.kind}={o.host_units}/{o.units}" for o in mdl.slots))
+            del mdl
+            torch.cuda.empty_cache()
+        row["speedup_greedy_over_uniform"] = round(row["uniform"]["ms"] / row["greedy"]["ms"], 4)
+        row["modeled_speedup"] = round(row["uniform"]["modeled_ms"] / row["greedy"]["modeled_ms"], 4)
+        rows.append(row)
+    res = {
+        "metric": "decode-layer step time with greedy per-op ratios vs one uniform ratio at the same global x",
+        "value": round(statistics.mean(r["speedup_greedy_over_uniform"] for r in rows), 4),
+        "unit": "mean speedup (uniform ms / greedy ms)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": f"one Llama-8B decoder layer (QKV, split-KV attention 32q/8kv hd128, O, gate+up, "
+                               f"down) at batch {batch}, {ctx} ctx/request", "footprint_bytes": footprint},
+        "t_comp_ms": {k: round(v * 1e3, 4) for k, v in t_comp.items()},
+        "all_hbm_op_ms": {"qkv": round(op0[0], 4), "attn": round(op0[1], 4), "o": round(op0[2], 4),
+                          "gate_up": round(op0[3], 4), "down": round(op0[4], 4)},
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "rows": rows,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,11 +614,16 @@ def main(argv=None):
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
-    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears"),
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare"),
                     default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
-                         "at N in {1,16,64} over x = 0..0.5, cold (each prints its own JSON line)")
+                         "at N in {1,16,64} over x = 0..0.5, cold; plan-compare: greedy per-op ratios against a "
+                         "uniform ratio for one decoder layer at large batch (each prints its own JSON line)")
+    ap.add_argument("--plan-batch", type=int, default=512, help="plan-compare: batch (activation rows N)")
+    ap.add_argument("--plan-ctx", type=int, default=2048, help="plan-compare: tokens per request")
+    ap.add_argument("--plan-x", type=float, nargs="+", default=[0.01, 0.02, 0.05],
+                    help="plan-compare: global host shares to compare at")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,
                     help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,
@@ -574,6 +654,8 @@ def main(argv=None):
         return run_prefill(torch, dak, args, b_hbm, b_host)
     if args.workload == "linears":
         return run_linears(torch, dak, args, b_hbm, b_host)
+    if args.workload == "plan-compare":
+        return run_plan_compare(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
+from fractions import Fraction
 from typing import List, Optional
 
 import torch
@@ -48,6 +49,7 @@ class DecoderShape:
 
 LLAMA70B = DecoderShape(hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, ffn=28672, layers=80)
 LLAMA8B = DecoderShape(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=14336, layers=32)
+LLAMA8B_ONE_LAYER = DecoderShape(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=14336, layers=1)
 
 
 @dataclass
@@ -85,7 +87,8 @@ class DecodeModel:
     """Weights and KV of a decoder spread over two tiers by the greedy planner."""
 
     def __init__(self, shape: DecoderShape, batch: int, ctx: int, b_hbm: float, b_host: float,
-                 hbm_bytes: int, m: int = 64, seed: int = 0, t_comp=None, log=print):
+                 hbm_bytes: int, m: int = 64, seed: int = 0, t_comp=None, log=print,
+                 x_global: Optional[float] = None, policy: str = "greedy"):
         self.shape, self.batch, self.ctx, self.m = shape, batch, ctx, m
         self.b_hbm, self.b_host = b_hbm, b_host
         s = shape
@@ -100,10 +103,22 @@ class DecodeModel:
         # order within a layer: qkv, attn, o, gate_up, down
         self.footprint = sum(o.bytes for o in self.slots)
         self.hbm_bytes = hbm_bytes
-        self.x_global = min_offload_ratio(self.footprint, hbm_bytes)
+        self.x_global = min_offload_ratio(self.footprint, hbm_bytes) if x_global is None else float(x_global)
         tc = t_comp or (lambda slot: 0.0)
-        ops = [Op(o.units, o.unit_bytes, float(tc(o))) for o in self.slots]
-        self.host_units, self.modeled_s = plan_offload(ops, b_hbm, b_host, self.x_global)
+        self.t_comp = [float(tc(o)) for o in self.slots]
+        ops = [Op(o.units, o.unit_bytes, t) for o, t in zip(self.slots, self.t_comp)]
+        if policy == "greedy":
+            # DAK §4.2.2: the greedy per-op ratios under the global budget.
+            self.host_units, self.modeled_s = plan_offload(ops, b_hbm, b_host, self.x_global)
+        elif policy == "uniform":
+            # Every op at the global ratio, h = ceil(x n) (the baseline the
+            # pages' greedy planner is measured against).
+            r = Fraction(repr(self.x_global))
+            self.host_units = [min(o.units, -((-r.numerator * o.units) // r.denominator)) for o in self.slots]
+            self.modeled_s = sum(self._op_time(i, h) for i, h in enumerate(self.host_units))
+        else:
+            raise ValueError("policy must be 'greedy' or 'uniform'")
+        self.policy = policy
         for o, h in zip(self.slots, self.host_units):
             o.host_units = h
         self.host_bytes = sum(o.host_units * o.unit_bytes for o in self.slots)
@@ -179,7 +194,11 @@ class DecodeModel:
             if events is not None:
                 events[i][1].record()
 
-    def op_model_s(self, i: int) -> float:
-        """Modelled time of op i: max((n - h) u / B_hbm, h u / B_host) (T_comp = 0)."""
+    def _op_time(self, i: int, h: int) -> float:
+        """DAK §4.2.1: T_i(h) = max(T_comp, (n - h) u / B_hbm, h u / B_host)."""
         o = self.slots[i]
-        return max((o.units - o.host_units) * o.unit_bytes / self.b_hbm, o.host_units * o.unit_bytes / self.b_host)
+        return max(self.t_comp[i], (o.units - h) * o.unit_bytes / self.b_hbm, h * o.unit_bytes / self.b_host)
+
+    def op_model_s(self, i: int) -> float:
+        """Modelled time of op i at its planned host units."""
+        return self._op_time(i, self.slots[i].host_units)

@@ -241,7 +241,7 @@ void launch_nb_rb(const StagedArgs& g) {
 template <int NB, bool COUNT>
 void launch_nb(const StagedArgs& g, int rbw) {
   switch (rbw) {
-    case 4: return launch_nb_rb<NB, NB >= 4 ? 2 : 4, COUNT>(g);   // NB = 4 never selects 4
+    case 4: return launch_nb_rb<NB, 4, COUNT>(g);
     case 2: return launch_nb_rb<NB, 2, COUNT>(g);
     default: return launch_nb_rb<NB, 1, COUNT>(g);
   }
@@ -261,10 +261,12 @@ void launch(const StagedArgs& g, int rbw) {
 }  // namespace
 
 int staged_row_blocks(int64_t M, int64_t m, int64_t N) {
-  // Tall items share each staged activation chunk over more rows; keep at
-  // least 384 items so that the HBM role still spreads over every CU, and a
-  // three-slot ring within the 160 KiB of LDS.
-  for (int r = N > 32 ? 2 : 4; r >= 2; r >>= 1)
+  // Tall items share each staged activation chunk over more rows (each staged
+  // x row is an L2 request that a weight row could have used); keep at least
+  // 384 items so that the HBM role still spreads over every CU.  At N > 32 a
+  // 64-row item fills 128 KiB of LDS with two slots.
+  (void)N;
+  for (int r = 4; r >= 2; r >>= 1)
     if (m % (16 * r) == 0 && M / (16 * r) >= 384) return r;
   return 1;
 }

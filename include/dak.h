@@ -51,7 +51,7 @@ const char* dak_last_error(void);
 int32_t dak_last_hip_error(void);
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t dak_abi_version(void);
-#define DAK_ABI_VERSION 1
+#define DAK_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------ */
 /* Capacity and planning (pure CPU, deterministic)                            */
@@ -206,14 +206,30 @@ dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, 
 /* Split decode attention: KV cache split along the batch                      */
 /* ------------------------------------------------------------------------ */
 
-/* KV caches of `batch` requests; requests [0, h) in pinned host memory and
- * [h, batch) in HBM.  DAK paper §5 "Supporting FlashAttention": each request
- * attends entirely within one tier.
- *   k_host, v_host  bf16 [h, n_kv_heads, ctx, head_dim] row-major (NULL if h == 0)
- *   k_hbm,  v_hbm   bf16 [batch - h, n_kv_heads, ctx, head_dim] (NULL if h == batch)
+/* KV caches of `batch` requests, split between pinned host memory and HBM.
+ * DAK paper §5 "Supporting FlashAttention": the split runs along the batch,
+ * each request attending entirely within one tier.  The host share is the
+ * first h units in (request, KV head) order: whole requests (unit ==
+ * DAK_KV_UNIT_REQUEST, the pages' split), or single KV heads of requests
+ * (DAK_KV_UNIT_HEAD: unit u = b * n_kv_heads + g), a finer step for a small
+ * batch, where one request is a coarse share of the cache.  Either way every
+ * (request, KV head) attends within one tier.
+ *   k_host, v_host  bf16, the host units' [ctx, head_dim] blocks in unit order
+ *                   ([h, n_kv_heads, ctx, head_dim] for request units), row-major
+ *                   (NULL if there are no host units)
+ *   k_hbm,  v_hbm   bf16, the remaining units' blocks in unit order (NULL if none)
+ *   batch, h        requests; host units (0 <= h <= batch for request units,
+ *                   0 <= h <= batch * n_kv_heads for head units)
  *   head_dim        128
- *   ctx             >= 1 tokens per request, all valid (no mask)
- * All pointers 16-byte aligned. */
+ *   ctx             tokens stored per request
+ *   unit            DAK_KV_UNIT_REQUEST or DAK_KV_UNIT_HEAD
+ *   ctx_lens        nullable device array of `batch` int32: the valid tokens
+ *                   of each request, its first ctx_lens[b] positions (1..ctx;
+ *                   values outside [0, ctx] are clamped to it, and a request
+ *                   with no valid token gets NaN rows); NULL: all ctx valid
+ * All pointers 16-byte aligned, ctx_lens included. */
+#define DAK_KV_UNIT_REQUEST 0
+#define DAK_KV_UNIT_HEAD 1
 typedef struct {
   const void* k_host;
   const void* v_host;
@@ -224,6 +240,9 @@ typedef struct {
   int32_t n_kv_heads;
   int32_t head_dim;
   int64_t ctx;
+  int32_t unit;
+  int32_t reserved;
+  const int32_t* ctx_lens;
 } dak_split_kv;
 
 /* Bytes of device workspace dak_splitk_decode_attn needs for these shapes
@@ -232,7 +251,8 @@ size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads
 
 /* out[b, j, :] = sum_t softmax_t(scale * q[b, j] . K[b, g, t]) V[b, g, t, :]
  * with g = j / (n_q_heads / n_kv_heads) (grouped-query attention), one query
- * token per request, fp32 accumulation, exact softmax.
+ * token per request, fp32 accumulation, exact softmax; t runs over the
+ * request's valid tokens.
  *   q        bf16 [batch, n_q_heads, head_dim] in device memory
  *   kv       the split KV cache
  *   n_q_heads a multiple of n_kv_heads, group size 1, 2, 4 or 8

@@ -48,6 +48,23 @@ def decode_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) 
     return out
 
 
+def decode_attention_lens(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, lens) -> np.ndarray:
+    """``decode_attention`` over a ragged batch: request b attends to its first
+    lens[b] positions only (the cache holds T positions per request; those
+    past lens[b] are storage, not context)."""
+    B, Hq, D = q.shape
+    Hkv = K.shape[1]
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        if not 1 <= n <= K.shape[2]:
+            raise ValueError("every request needs 1..T valid positions")
+        for j in range(Hq):
+            g = kv_group(j, Hq, Hkv)
+            out[b, j] = attend_one(q[b, j], K[b, g, :n], V[b, g, :n], scale)
+    return out
+
+
 def split_decode_attention(q, K_host, V_host, K_hbm, V_hbm, scale: float) -> np.ndarray:
     """Same as ``decode_attention`` with requests [0, h) taken from the host arrays
     and the remaining requests from the HBM arrays (batch split of the KV cache)."""

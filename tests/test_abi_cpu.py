@@ -160,3 +160,34 @@ def test_mfma_probe_argument_errors_before_any_launch():
     assert lib.dak_probe_mfma(4, 0, 1, None, C.byref(ms), C.byref(tf)) == L.DAK_EINVAL
     assert lib.dak_probe_mfma(4, 16, 0, None, C.byref(ms), C.byref(tf)) == L.DAK_EINVAL
     assert lib.dak_probe_mfma(4, 16, 1, None, None, None) == L.DAK_EINVAL
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    # Compile the header with the C compiler and compare every struct's size and
+    # field offsets with the ctypes mirrors the binding passes across the ABI.
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = [("dak_op_desc", L.OpDesc), ("dak_launch_cfg", L.LaunchCfg),
+               ("dak_split_matrix", L.SplitMatrixDesc), ("dak_split_kv", L.SplitKVDesc)]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dak.h"', "int main(void) {"]
+    for cname, py in structs:
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, py in structs:
+        assert got[(cname, "sizeof")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

@@ -137,3 +137,86 @@ def test_llama70b_attention_full_size():
         assert normwise_error(out4[b, j].numpy(), ref) <= TOL, (b, j)
     del K, V
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Host units of single KV heads, and ragged batches (per-request lengths)
+# ---------------------------------------------------------------------------
+def run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_REQUEST, lens=None, cfg=None):
+    kv = dak.place_kv(K, V, h, unit=unit, ctx_lens=lens)
+    out = dak.splitk_decode_attn(q.cuda(), kv, scale, cfg=cfg)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def test_head_unit_splits_bit_identical():
+    # Host shares in (request, KV head) steps: 8 units at batch 2 x 4 KV heads.
+    B, Hq, Hkv, D, ctx = 2, 16, 4, 128, 3000
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=40)
+    scale = 1.0 / np.sqrt(D)
+    ref = oa.decode_attention(to_f64(q), to_f64(K), to_f64(V), scale)
+    base = run_kv(q, K, V, 0, scale)
+    assert normwise_error(base.numpy(), ref) <= TOL
+    for h in range(B * Hkv + 1):
+        assert torch.equal(run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_HEAD), base), h
+    assert torch.equal(run_kv(q, K, V, 1, scale), base)
+
+
+def test_ragged_lengths_match_the_oracle_at_every_split():
+    # Lengths at the chunk edges (2048 tokens per chunk) and a single token.
+    B, Hq, Hkv, D, ctx = 4, 8, 2, 128, 5000
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=41)
+    lens = torch.tensor([5000, 1, 2049, 2048], dtype=torch.int32)
+    scale = 1.0 / np.sqrt(D)
+    ref = oa.decode_attention_lens(to_f64(q), to_f64(K), to_f64(V), scale, lens.tolist())
+    base = run_kv(q, K, V, 0, scale, lens=lens)
+    # per request: the one-token request's exact row would dominate a joint norm
+    for b in range(B):
+        err = normwise_error(base[b].numpy(), ref[b])
+        print(f"ragged len {int(lens[b])} normwise error {err:.3e}")
+        assert err <= TOL
+    # and the lengths do matter: the full-length oracle is far from it
+    full = oa.decode_attention(to_f64(q), to_f64(K), to_f64(V), scale)
+    assert normwise_error(base[2].numpy(), full[2]) > 10 * TOL
+    # request 1 has one valid position: its value row, exactly
+    assert torch.equal(base[1], V[1, :, 0].float().repeat_interleave(Hq // Hkv, dim=0))
+    for h in range(B + 1):
+        assert torch.equal(run_kv(q, K, V, h, scale, lens=lens), base), h
+    for h in (1, 3, 6):
+        assert torch.equal(run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_HEAD, lens=lens), base), h
+
+
+def test_ragged_kv_bytes_read_once():
+    B, Hq, Hkv, D, ctx = 3, 4, 2, 128, 4100
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=42)
+    lens = torch.tensor([17, 4100, 2048], dtype=torch.int32)
+    for unit, h, host_units in ((dak.KV_UNIT_REQUEST, 1, 2), (dak.KV_UNIT_HEAD, 3, 3)):
+        kv = dak.place_kv(K, V, h, unit=unit, ctx_lens=lens)
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1, cfg=dak.LaunchConfig(byte_counters=cnt))
+        torch.cuda.synchronize()
+        per_unit = [int(lens[u // Hkv]) * D * 2 * 2 for u in range(B * Hkv)]
+        assert cnt.tolist() == [sum(per_unit[:host_units]), sum(per_unit[host_units:])]
+
+
+def test_ragged_and_unit_arguments_checked():
+    B, Hq, Hkv, D, ctx = 2, 4, 2, 128, 64
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=43)
+    kv = dak.place_kv(K, V, 1, ctx_lens=torch.tensor([64, 10]))
+    kv.ctx_lens = torch.tensor([64, 10], dtype=torch.int32)   # host memory: refused
+    with pytest.raises(dak.DakError):
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1)
+    kv = dak.place_kv(K, V, 1)
+    kv.unit = 7
+    with pytest.raises(dak.DakError):
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1)
+
+
+def test_ragged_lengths_clamped():
+    # len <= 0: an empty softmax, NaN rows; len > ctx: read as ctx.
+    B, Hq, Hkv, D, ctx = 3, 4, 2, 128, 700
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=44)
+    full = run_kv(q, K, V, 1, 0.1)
+    out = run_kv(q, K, V, 1, 0.1, lens=torch.tensor([0, -5, 10**6], dtype=torch.int32))
+    assert torch.isnan(out[:2]).all()
+    assert torch.equal(out[2], full[2])

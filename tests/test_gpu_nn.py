@@ -8,6 +8,7 @@ import torch
 import synth
 from oracle import attention as oa
 from oracle.gemm import gemm, normwise_error, to_f64
+import tiered_memory_offloading_amd as dak
 from tiered_memory_offloading_amd.nn import SplitK_FlashAttn, SplitK_GEMM
 
 pytestmark = pytest.mark.gpu
@@ -60,3 +61,16 @@ def test_splitk_flashattn_replaces_sdpa():
         mod(q.cuda(), attn_mask=torch.ones(1))
     with pytest.raises(ValueError):
         mod(q[:, :, None, :].expand(B, Hq, 2, D).contiguous().cuda())
+
+
+def test_splitk_flashattn_head_units_and_ragged_batch():
+    B, Hq, Hkv, D, ctx = 3, 8, 2, 128, 2500
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=23)
+    lens = torch.tensor([2500, 300, 2049])
+    ref = oa.decode_attention_lens(to_f64(q), to_f64(K), to_f64(V), 1.0 / np.sqrt(D), lens.tolist())
+    base = SplitK_FlashAttn(K, V, out_dtype=torch.float32, ctx_lens=lens)(q.cuda()).cpu()
+    for b in range(B):
+        assert normwise_error(base[b].numpy(), ref[b]) <= TOL
+    mod = SplitK_FlashAttn(K, V, host_ratio=0.5, out_dtype=torch.float32, unit=dak.KV_UNIT_HEAD, ctx_lens=lens)
+    assert mod.h == 3 and mod.kv.host_units == 3
+    assert torch.equal(mod(q.cuda()).cpu(), base)

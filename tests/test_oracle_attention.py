@@ -101,3 +101,46 @@ def test_batch_split_is_exact():
     for h in range(5):
         out = oa.split_decode_attention(q, K[:h], V[:h], K[h:], V[h:], 0.35)
         assert np.array_equal(out, ref)
+
+
+# ---------------------------------------------------------------------------
+# Ragged batch: request b attends to its first lens[b] positions only
+# ---------------------------------------------------------------------------
+def test_ragged_one_valid_position_returns_that_value_row():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 4, 8))
+    K = rng.standard_normal((3, 2, 6, 8))
+    V = rng.standard_normal((3, 2, 6, 8))
+    out = oa.decode_attention_lens(q, K, V, 0.7, [1, 1, 1])
+    for b in range(3):
+        for j in range(4):
+            assert np.array_equal(out[b, j], V[b, j // 2, 0])
+
+
+def test_ragged_equal_keys_give_the_mean_of_the_valid_rows():
+    # All keys equal: every valid position has the same weight 1/lens[b].
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 2, 4))
+    K = np.ones((2, 1, 9, 4))
+    V = rng.integers(-3, 4, size=(2, 1, 9, 4)).astype(np.float64)
+    lens = [9, 4]
+    out = oa.decode_attention_lens(q, K, V, 0.3, lens)
+    for b in range(2):
+        assert np.allclose(out[b, :], V[b, 0, :lens[b]].mean(axis=0)[None, :], rtol=0, atol=1e-15)
+
+
+def test_ragged_positions_past_the_length_do_not_matter():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((2, 4, 8))
+    K = rng.standard_normal((2, 2, 10, 8))
+    V = rng.standard_normal((2, 2, 10, 8))
+    lens = [10, 3]
+    a = oa.decode_attention_lens(q, K, V, 0.5, lens)
+    K2, V2 = K.copy(), V.copy()
+    K2[1, :, 3:] = 100.0
+    V2[1, :, 3:] = -7.0
+    assert np.array_equal(oa.decode_attention_lens(q, K2, V2, 0.5, lens), a)
+    # full lengths are the unragged attention
+    assert np.array_equal(oa.decode_attention_lens(q, K, V, 0.5, [10, 10]), oa.decode_attention(q, K, V, 0.5))
+    with pytest.raises(ValueError):
+        oa.decode_attention_lens(q, K, V, 0.5, [0, 3])

@@ -24,7 +24,7 @@ from . import _lib as L
 __all__ = [
     "DakError", "LaunchConfig", "SplitMatrix", "SplitKV", "Op",
     "min_offload_ratio", "plan_offload", "op_turning_points", "host_workgroups",
-    "place_matrix", "place_kv", "splitk_gemm", "decode_attn_workspace_bytes",
+    "place_matrix", "place_kv", "KV_UNIT_REQUEST", "KV_UNIT_HEAD", "splitk_gemm", "decode_attn_workspace_bytes",
     "splitk_decode_attn", "probe_read", "probe_read_concurrent", "library",
 ]
 
@@ -165,48 +165,69 @@ def place_matrix(A: torch.Tensor, m: int, h: int, device=None) -> SplitMatrix:
     return SplitMatrix(host, hbm, M, K, m, h)
 
 
+KV_UNIT_REQUEST = 0
+KV_UNIT_HEAD = 1
+
+
 @dataclass
 class SplitKV:
-    """KV caches of `batch` requests; requests [0, h) in pinned host memory."""
-    k_host: Optional[torch.Tensor]   # [h, Hkv, ctx, D] bf16 pinned
+    """KV caches of `batch` requests; the first h units (whole requests, or
+    (request, KV head) pairs with unit=KV_UNIT_HEAD) in pinned host memory."""
+    k_host: Optional[torch.Tensor]   # host units' [ctx, D] blocks in unit order, bf16 pinned
     v_host: Optional[torch.Tensor]
-    k_hbm: Optional[torch.Tensor]    # [batch - h, Hkv, ctx, D] bf16 CUDA
+    k_hbm: Optional[torch.Tensor]    # the other units' blocks, bf16 CUDA
     v_hbm: Optional[torch.Tensor]
     batch: int
     h: int
     n_kv_heads: int
     head_dim: int
     ctx: int
+    unit: int = KV_UNIT_REQUEST
+    ctx_lens: Optional[torch.Tensor] = None   # int32 [batch] on the GPU: valid tokens per request
 
     def desc(self) -> L.SplitKVDesc:
         def p(t):
             return t.data_ptr() if t is not None and t.numel() else None
         return L.SplitKVDesc(p(self.k_host), p(self.v_host), p(self.k_hbm), p(self.v_hbm), self.batch, self.h,
-                             self.n_kv_heads, self.head_dim, self.ctx)
+                             self.n_kv_heads, self.head_dim, self.ctx, self.unit, 0, p(self.ctx_lens))
+
+    @property
+    def host_units(self) -> int:
+        """Host units in (request, KV head) pairs."""
+        return self.h * self.n_kv_heads if self.unit == KV_UNIT_REQUEST else self.h
 
     @property
     def host_bytes(self) -> int:
-        return 2 * self.h * self.n_kv_heads * self.ctx * self.head_dim * 2
+        """Bytes of K and V stored on the host."""
+        return 2 * self.host_units * self.ctx * self.head_dim * 2
 
 
-def place_kv(K: torch.Tensor, V: torch.Tensor, h: int, device=None) -> SplitKV:
-    """Copy requests [0, h) of K, V [B, Hkv, ctx, D] into pinned host memory, the rest into HBM."""
+def place_kv(K: torch.Tensor, V: torch.Tensor, h: int, device=None, unit: int = KV_UNIT_REQUEST,
+             ctx_lens: Optional[torch.Tensor] = None) -> SplitKV:
+    """Copy the first h units of K, V [B, Hkv, ctx, D] (requests, or (request,
+    KV head) pairs with unit=KV_UNIT_HEAD) into pinned host memory and the rest
+    into HBM.  ctx_lens: optional valid-token counts per request (any integer
+    tensor of B entries)."""
     if K.shape != V.shape or K.dim() != 4 or K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
         raise ValueError("K and V must be bf16 tensors of equal shape [B, Hkv, ctx, D]")
     B, Hkv, ctx, D = K.shape
-    if not 0 <= h <= B:
-        raise ValueError("0 <= h <= batch")
+    units = B if unit == KV_UNIT_REQUEST else B * Hkv
+    if unit not in (KV_UNIT_REQUEST, KV_UNIT_HEAD) or not 0 <= h <= units:
+        raise ValueError("unit must be KV_UNIT_REQUEST or KV_UNIT_HEAD, with 0 <= h <= its unit count")
     device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    hu = h * Hkv if unit == KV_UNIT_REQUEST else h
+    Kf, Vf = K.reshape(B * Hkv, ctx, D), V.reshape(B * Hkv, ctx, D)
     kh = vh = kg = vg = None
-    if h:
-        kh = torch.empty((h, Hkv, ctx, D), dtype=torch.bfloat16, pin_memory=True)
-        vh = torch.empty((h, Hkv, ctx, D), dtype=torch.bfloat16, pin_memory=True)
-        kh.copy_(K[:h])
-        vh.copy_(V[:h])
-    if h < B:
-        kg = K[h:].to(device, copy=True).contiguous()
-        vg = V[h:].to(device, copy=True).contiguous()
-    return SplitKV(kh, vh, kg, vg, B, h, Hkv, D, ctx)
+    if hu:
+        kh = torch.empty((hu, ctx, D), dtype=torch.bfloat16, pin_memory=True)
+        vh = torch.empty((hu, ctx, D), dtype=torch.bfloat16, pin_memory=True)
+        kh.copy_(Kf[:hu])
+        vh.copy_(Vf[:hu])
+    if hu < B * Hkv:
+        kg = Kf[hu:].to(device, copy=True).contiguous()
+        vg = Vf[hu:].to(device, copy=True).contiguous()
+    lens = None if ctx_lens is None else ctx_lens.to(device=device, dtype=torch.int32).contiguous()
+    return SplitKV(kh, vh, kg, vg, B, h, Hkv, D, ctx, unit, lens)
 
 
 # ----------------------------------------------------------------------------

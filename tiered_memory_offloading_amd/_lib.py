@@ -13,7 +13,7 @@ DAK_EINFEASIBLE = -2
 DAK_EHIP = -3
 DAK_EUNSUPPORTED = -4
 DAK_FLAG_COUNT_BYTES = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class OpDesc(C.Structure):
@@ -33,7 +33,7 @@ class SplitMatrixDesc(C.Structure):
 class SplitKVDesc(C.Structure):
     _fields_ = [("k_host", C.c_void_p), ("v_host", C.c_void_p), ("k_hbm", C.c_void_p), ("v_hbm", C.c_void_p),
                 ("batch", C.c_int64), ("h", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("ctx", C.c_int64)]
+                ("ctx", C.c_int64), ("unit", C.c_int32), ("reserved", C.c_int32), ("ctx_lens", C.c_void_p)]
 
 
 # (name, restype, argtypes) for every symbol include/dak.h declares.

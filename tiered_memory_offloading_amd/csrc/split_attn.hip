@@ -155,7 +155,7 @@ __device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, co
 // merged (lane groups, then waves in order) and the chunk partial is written.
 template <int G, int U, bool COUNT>
 __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kbg,
-                                          const uint16_t* __restrict__ Vbg, int64_t b, int g, int c, int64_t ctx,
+                                          const uint16_t* __restrict__ Vbg, int64_t b, int g, int c, int64_t len,
                                           int Hq, int C, float qscale, float* __restrict__ o_ws,
                                           float* __restrict__ ml_ws, float* red_o, float* red_ml, int wave,
                                           int lane, uint64_t& nbytes) {
@@ -178,7 +178,7 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
   const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
-  const int64_t te = tb + kWaveTokens < ctx ? tb + kWaveTokens : ctx;
+  const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
   attn_tokens<G, U, COUNT>(Kbg, Vbg, tb, te, qb, qscale, m, l, o, lane, nbytes);
 
   // Merge the four lane groups (xor 16, then xor 32).
@@ -234,34 +234,48 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
   __syncthreads();   // LDS reused by the next item
 }
 
+// Valid tokens of request b: ctx_lens[b] clamped to [0, ctx] (all ctx without
+// a length array).  The clamp keeps every load inside the request's block.
+__device__ __forceinline__ int64_t valid_len(const int32_t* __restrict__ ctx_lens, int64_t b, int64_t ctx) {
+  if (!ctx_lens) return ctx;
+  const int64_t v = ctx_lens[b];
+  return v < 0 ? 0 : v > ctx ? ctx : v;
+}
+
+// Items are (unit, chunk) pairs, unit u = b * Hkv + g (a request's KV head);
+// the first h_units units live in host memory, each a [ctx, D] block of K and
+// of V at offset u * ctx * D of its tier.  Chunks past a request's valid
+// length have no tokens and are skipped (the combine does not read them).
 template <int G, int UH, int UG, bool COUNT>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_host, const uint16_t* __restrict__ v_host,
-    const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t h_req, int Hkv, int Hq,
-    int64_t ctx, int C, float qscale, float* __restrict__ o_ws, float* __restrict__ ml_ws, int host_wgs,
-    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+    const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t h_units, int Hkv, int Hq,
+    int64_t ctx, int C, const int32_t* __restrict__ ctx_lens, float qscale, float* __restrict__ o_ws,
+    float* __restrict__ ml_ws, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
   __shared__ float red_o[kAttnWaves * G * kD];
   __shared__ float red_ml[kAttnWaves * G * 2];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
-  const int64_t per_req = (int64_t)Hkv * C;
   if (host_role) {
     for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
-      const int64_t bl = it / per_req;
-      const int g = (int)((it / C) % Hkv), c = (int)(it % C);
-      const int64_t off = (bl * Hkv + g) * ctx * kD;
-      attn_item<G, UH, COUNT>(q, k_host + off, v_host + off, bl, g, c, ctx, Hq, C, qscale, o_ws, ml_ws, red_o,
-                              red_ml, wave, lane, nbytes);
+      const int64_t u = it / C;
+      const int c = (int)(it % C);
+      const int64_t b = u / Hkv, len = valid_len(ctx_lens, b, ctx);
+      if ((int64_t)c * kChunk >= len) continue;   // uniform
+      attn_item<G, UH, COUNT>(q, k_host + u * ctx * kD, v_host + u * ctx * kD, b, (int)(u % Hkv), c, len, Hq, C,
+                              qscale, o_ws, ml_ws, red_o, red_ml, wave, lane, nbytes);
     }
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
     if (it < hbm_items) {
-      const int64_t bl = it / per_req;
-      const int g = (int)((it / C) % Hkv), c = (int)(it % C);
-      const int64_t off = (bl * Hkv + g) * ctx * kD;
-      attn_item<G, UG, COUNT>(q, k_hbm + off, v_hbm + off, h_req + bl, g, c, ctx, Hq, C, qscale, o_ws, ml_ws,
-                              red_o, red_ml, wave, lane, nbytes);
+      const int64_t u = it / C, gu = h_units + u;
+      const int c = (int)(it % C);
+      const int64_t b = gu / Hkv, len = valid_len(ctx_lens, b, ctx);
+      if ((int64_t)c * kChunk < len)
+        attn_item<G, UG, COUNT>(q, k_hbm + u * ctx * kD, v_hbm + u * ctx * kD, b, (int)(gu % Hkv), c, len, Hq, C,
+                                qscale, o_ws, ml_ws, red_o, red_ml, wave, lane, nbytes);
     }
   }
   if (COUNT) {
@@ -278,12 +292,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
 // dimension over the chunks in chunk order; the chunk loads are independent, so
 // many are in flight at once.
 __global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_ws, const float* __restrict__ ml_ws,
-                                                   int C, float* __restrict__ out) {
+                                                   int C_ws, int Hq, int64_t ctx,
+                                                   const int32_t* __restrict__ ctx_lens, float* __restrict__ out) {
   __shared__ float sm[2 * 256];
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
-  const float* ml = ml_ws + row * C * 2;
-  const float* ow = o_ws + row * C * kD;
+  const float* ml = ml_ws + row * C_ws * 2;
+  const float* ow = o_ws + row * C_ws * kD;
+  // The chunks that hold tokens of this row's request.
+  const int64_t len = valid_len(ctx_lens, row / Hq, ctx);
+  const int C = (int)((len + kChunk - 1) / kChunk);
   float O = 0.f, L = 0.f;
   // Chunks in groups of 256 (C is at most ctx / kChunk).
   float M = kNegInf;
@@ -314,10 +332,11 @@ __global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_w
 
 struct AttnArgs {
   const uint16_t *q, *k_host, *v_host, *k_hbm, *v_hbm;
-  int64_t batch, h_req;
+  int64_t batch, h_units;
   int Hkv, Hq;
   int64_t ctx;
   int C;
+  const int32_t* ctx_lens;
   float qscale;
   float *o_ws, *ml_ws, *out;
   int host_wgs;
@@ -332,8 +351,8 @@ void launch_partial_g(const AttnArgs& a) {
   constexpr int UHc = G >= 8 ? 1 : (G >= 4 && UH > 2 ? 2 : UH);
   const int64_t grid = a.host_wgs + a.hbm_items;
   hipLaunchKernelGGL((attn_partial_split<G, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0,
-                     a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_req, a.Hkv, a.Hq, a.ctx, a.C,
-                     a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
+                     a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_units, a.Hkv, a.Hq, a.ctx, a.C,
+                     a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
 }
 
 template <int UH, bool COUNT>
@@ -356,8 +375,18 @@ void launch_partial_w(const AttnArgs& a, int G, int window) {
   }
 }
 
+// Host units in (request, KV head) pairs, or -1 for an invalid unit code.
+int64_t host_units_of(const dak_split_kv* kv) {
+  if (kv->unit == DAK_KV_UNIT_REQUEST) return kv->h * kv->n_kv_heads;
+  if (kv->unit == DAK_KV_UNIT_HEAD) return kv->h;
+  return -1;
+}
+
 bool attn_shapes_ok(const dak_split_kv* kv, int32_t n_q_heads) {
-  return kv && kv->batch >= 1 && kv->h >= 0 && kv->h <= kv->batch && kv->n_kv_heads >= 1 && kv->ctx >= 1 &&
+  if (!kv || kv->n_kv_heads < 1 || kv->batch < 1 || kv->batch > (int64_t(1) << 24) || kv->n_kv_heads > 4096)
+    return false;
+  const int64_t units = kv->batch * kv->n_kv_heads, hu = host_units_of(kv);
+  return hu >= 0 && hu <= units && kv->h >= 0 && kv->ctx >= 1 &&
          n_q_heads >= 1 && n_q_heads % kv->n_kv_heads == 0 && kv->head_dim == kD &&
          kv->batch <= (int64_t(1) << 24) && kv->ctx <= (int64_t(1) << 31) && n_q_heads <= 4096;
 }
@@ -391,19 +420,23 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   const size_t need = dak_decode_attn_workspace_bytes(kv, n_q_heads);
   if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
-  const int64_t B = kv->batch, h = kv->h, Hkv = kv->n_kv_heads, ctx = kv->ctx;
-  const uint64_t per_req = (uint64_t)Hkv * ctx * kD * 2;
+  const int64_t B = kv->batch, Hkv = kv->n_kv_heads, ctx = kv->ctx;
+  const int64_t hu = host_units_of(kv), units = B * Hkv;   // host units in (request, KV head) pairs
+  const uint64_t per_unit = (uint64_t)ctx * kD * 2;
   const void *dq = nullptr, *dkh = nullptr, *dvh = nullptr, *dkg = nullptr, *dvg = nullptr, *dout = nullptr,
              *dws = nullptr;
   if ((st = check_tier_ptr(q, (uint64_t)B * n_q_heads * kD * 2, Tier::kDevice, "q", &dq))) return st;
-  if (h > 0) {
-    if ((st = check_tier_ptr(kv->k_host, per_req * h, Tier::kHost, "k_host", &dkh))) return st;
-    if ((st = check_tier_ptr(kv->v_host, per_req * h, Tier::kHost, "v_host", &dvh))) return st;
+  if (hu > 0) {
+    if ((st = check_tier_ptr(kv->k_host, per_unit * hu, Tier::kHost, "k_host", &dkh))) return st;
+    if ((st = check_tier_ptr(kv->v_host, per_unit * hu, Tier::kHost, "v_host", &dvh))) return st;
   }
-  if (h < B) {
-    if ((st = check_tier_ptr(kv->k_hbm, per_req * (B - h), Tier::kDevice, "k_hbm", &dkg))) return st;
-    if ((st = check_tier_ptr(kv->v_hbm, per_req * (B - h), Tier::kDevice, "v_hbm", &dvg))) return st;
+  if (hu < units) {
+    if ((st = check_tier_ptr(kv->k_hbm, per_unit * (units - hu), Tier::kDevice, "k_hbm", &dkg))) return st;
+    if ((st = check_tier_ptr(kv->v_hbm, per_unit * (units - hu), Tier::kDevice, "v_hbm", &dvg))) return st;
   }
+  const void* dlens = nullptr;
+  if (kv->ctx_lens && (st = check_tier_ptr(kv->ctx_lens, (uint64_t)B * 4, Tier::kDevice, "ctx_lens", &dlens)))
+    return st;
   if ((st = check_tier_ptr(out, (uint64_t)B * n_q_heads * kD * 4, Tier::kDevice, "out", &dout))) return st;
   if ((st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws))) return st;
 
@@ -414,7 +447,8 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   a.k_hbm = static_cast<const uint16_t*>(dkg);
   a.v_hbm = static_cast<const uint16_t*>(dvg);
   a.batch = B;
-  a.h_req = h;
+  a.h_units = hu;
+  a.ctx_lens = static_cast<const int32_t*>(dlens);
   a.Hkv = (int)Hkv;
   a.Hq = n_q_heads;
   a.ctx = ctx;
@@ -423,8 +457,8 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   a.o_ws = static_cast<float*>(ws);
   a.ml_ws = a.o_ws + (size_t)B * n_q_heads * a.C * kD;
   a.out = out;
-  a.host_items = h * Hkv * a.C;
-  a.hbm_items = (B - h) * Hkv * a.C;
+  a.host_items = hu * a.C;
+  a.hbm_items = (units - hu) * a.C;
   a.host_wgs = (int)host_workgroups(a.host_items, lc.host_cus);
   a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   a.stream = static_cast<hipStream_t>(stream);
@@ -442,7 +476,7 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
-                     out);
+                     n_q_heads, ctx, a.ctx_lens, out);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");
   return DAK_OK;

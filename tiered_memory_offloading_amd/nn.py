@@ -17,7 +17,8 @@ from typing import Optional, Union
 
 import torch
 
-from . import place_kv, place_matrix, splitk_decode_attn, splitk_gemm, decode_attn_workspace_bytes
+from . import (KV_UNIT_HEAD, KV_UNIT_REQUEST, decode_attn_workspace_bytes, place_kv, place_matrix,
+               splitk_decode_attn, splitk_gemm)
 
 Ratio = Union[float, Fraction]
 
@@ -80,7 +81,9 @@ class SplitK_GEMM(torch.nn.Module):
 class SplitK_FlashAttn(torch.nn.Module):
     """Decode attention over a KV cache split along the batch: requests
     [0, h) in pinned host memory, the rest in HBM (every request attends within
-    one tier).
+    one tier).  With unit=KV_UNIT_HEAD the split steps in (request, KV head)
+    pairs instead, h = ceil(ratio * B * Hkv); ctx_lens (B integers) gives each
+    request's valid cache length for a ragged batch.
 
     Call as scaled_dot_product_attention for one query token per request:
     query [B, Hq, 1, D] (or [B, Hq, D]) bf16 with Hq a multiple of the cache's
@@ -89,12 +92,17 @@ class SplitK_FlashAttn(torch.nn.Module):
     `out_dtype` (default: the query's dtype)."""
 
     def __init__(self, key: torch.Tensor, value: torch.Tensor, host_ratio: Ratio = 0.0,
-                 out_dtype: Optional[torch.dtype] = None):
+                 out_dtype: Optional[torch.dtype] = None, unit: int = KV_UNIT_REQUEST,
+                 ctx_lens: Optional[torch.Tensor] = None):
         super().__init__()
         if key.dim() != 4 or key.shape != value.shape:
             raise ValueError("key and value must be [B, Hkv, ctx, D] of equal shape")
-        self.h = host_units(host_ratio, key.shape[0])
-        self.kv = place_kv(key.detach().to(torch.bfloat16), value.detach().to(torch.bfloat16), self.h)
+        if unit not in (KV_UNIT_REQUEST, KV_UNIT_HEAD):
+            raise ValueError("unit must be KV_UNIT_REQUEST or KV_UNIT_HEAD")
+        n = key.shape[0] * (key.shape[1] if unit == KV_UNIT_HEAD else 1)
+        self.h = host_units(host_ratio, n)
+        self.kv = place_kv(key.detach().to(torch.bfloat16), value.detach().to(torch.bfloat16), self.h,
+                           unit=unit, ctx_lens=ctx_lens)
         self.out_dtype = out_dtype
         self._ws = None
 

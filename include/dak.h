@@ -266,6 +266,70 @@ dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t
                                   float scale, float* out, void* ws, size_t ws_bytes,
                                   const dak_launch_cfg* cfg, void* stream);
 
+/* A paged KV cache split between two page pools.  Paged attention keeps each
+ * request's cache in fixed-size pages drawn from a free pool; BOOST §3.3 and
+ * §4.3 ("Block-level KV Head Chunk Partitioning", "Wave-aware Block
+ * Fulfillment") reorder the pages head-major so one KV head's pages can live
+ * in the host tier while the request's other heads stay in HBM.  Here the
+ * units are (request, KV head) pairs u = b * n_kv_heads + g, each with its own
+ * row of the page table, and every unit lies wholly in one tier (DAK §4.1:
+ * one data path per work-group).  Which units are host units changes as
+ * requests come and go, so it is given on the device: the first n_host_units
+ * entries of unit_order name them.
+ *   k_host, v_host   bf16 host pool [host_pages, page, head_dim], pinned
+ *                    (NULL when host_pages == 0)
+ *   k_hbm,  v_hbm    bf16 HBM pool [hbm_pages, page, head_dim], device memory
+ *                    (NULL when hbm_pages == 0)
+ *   host_pages, hbm_pages  pages in each pool
+ *   batch, n_kv_heads, head_dim (128)
+ *   page             tokens per page: a power of two, 16 .. 2^20
+ *   max_pages        columns of page_table (pages per unit at most)
+ *   page_table       device int32 [batch * n_kv_heads, max_pages]: entry
+ *                    [u, i] is the index, in u's tier's pool, of the page
+ *                    holding u's tokens [i * page, (i + 1) * page)
+ *   ctx_lens         device int32 [batch]: valid tokens of each request,
+ *                    clamped to [0, max_pages * page]; entries of page_table
+ *                    past a unit's last valid page are never read
+ *   unit_order       device int32 [batch * n_kv_heads]: a permutation of the
+ *                    units; entries [0, n_host_units) are the host units
+ *   n_host_units     0 .. batch * n_kv_heads
+ * Contents of the device arrays are checked by the kernel, which never reads
+ * outside a pool: a unit with a page index outside its pool gets NaN rows;
+ * an entry of unit_order outside [0, units) is skipped.  If unit_order is not
+ * a permutation, the rows of the units it misses are unspecified.
+ * All pointers 16-byte aligned. */
+typedef struct {
+  const void* k_host;
+  const void* v_host;
+  const void* k_hbm;
+  const void* v_hbm;
+  int64_t host_pages;
+  int64_t hbm_pages;
+  int64_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t page;
+  int32_t max_pages;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  const int32_t* unit_order;
+  int64_t n_host_units;
+} dak_paged_kv;
+
+/* Bytes of device workspace dak_paged_decode_attn needs (0 on invalid
+ * shapes). */
+size_t dak_paged_decode_attn_workspace_bytes(const dak_paged_kv* kv, int32_t n_q_heads);
+
+/* dak_splitk_decode_attn over a paged KV cache: out[b, j, :] is the softmax
+ * over request b's first ctx_lens[b] tokens of KV head g = j / (n_q_heads /
+ * n_kv_heads).  Same arguments, workspace rule, determinism (the result bits
+ * do not depend on which units are host units, nor on the pages' pool
+ * indices) and errors as dak_splitk_decode_attn.  A request with no valid
+ * token gets NaN rows. */
+dak_status dak_paged_decode_attn(const void* q, const dak_paged_kv* kv, int32_t n_q_heads, float scale,
+                                 float* out, void* ws, size_t ws_bytes, const dak_launch_cfg* cfg,
+                                 void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Streaming-read probes (roofline bandwidths and the congestion sweep)        */
 /* ------------------------------------------------------------------------ */

@@ -25,7 +25,8 @@ __all__ = [
     "DakError", "LaunchConfig", "SplitMatrix", "SplitKV", "Op",
     "min_offload_ratio", "plan_offload", "op_turning_points", "host_workgroups",
     "place_matrix", "place_kv", "KV_UNIT_REQUEST", "KV_UNIT_HEAD", "splitk_gemm", "decode_attn_workspace_bytes",
-    "splitk_decode_attn", "probe_read", "probe_read_concurrent", "library",
+    "splitk_decode_attn", "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
+    "probe_read", "probe_read_concurrent", "library",
 ]
 
 
@@ -272,6 +273,133 @@ def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_splitk_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
                                       ws.data_ptr(), ws.numel() * ws.element_size(), cp, _stream_handle(stream)))
+    return out
+
+
+@dataclass
+class PagedKV:
+    """A paged KV cache: pages of `page` tokens of one (request, KV head) unit
+    in a host pool (pinned) and an HBM pool; page_table [units, max_pages]
+    gives each unit's pages in its tier's pool, unit_order lists the host units
+    first (n_host_units of them)."""
+    k_host: Optional[torch.Tensor]   # [host_pages, page, D] bf16 pinned
+    v_host: Optional[torch.Tensor]
+    k_hbm: Optional[torch.Tensor]    # [hbm_pages, page, D] bf16 CUDA
+    v_hbm: Optional[torch.Tensor]
+    page_table: torch.Tensor         # int32 [B * Hkv, max_pages] CUDA
+    ctx_lens: torch.Tensor           # int32 [B] CUDA
+    unit_order: torch.Tensor         # int32 [B * Hkv] CUDA
+    batch: int
+    n_kv_heads: int
+    head_dim: int
+    page: int
+    n_host_units: int
+
+    @property
+    def max_pages(self) -> int:
+        return self.page_table.shape[1]
+
+    @property
+    def host_pages(self) -> int:
+        return 0 if self.k_host is None else self.k_host.shape[0]
+
+    @property
+    def hbm_pages(self) -> int:
+        return 0 if self.k_hbm is None else self.k_hbm.shape[0]
+
+    @property
+    def host_bytes(self) -> int:
+        return 2 * self.host_pages * self.page * self.head_dim * 2
+
+    def desc(self) -> L.PagedKVDesc:
+        def p(t):
+            return t.data_ptr() if t is not None and t.numel() else None
+        return L.PagedKVDesc(p(self.k_host), p(self.v_host), p(self.k_hbm), p(self.v_hbm), self.host_pages,
+                             self.hbm_pages, self.batch, self.n_kv_heads, self.head_dim, self.page, self.max_pages,
+                             p(self.page_table), p(self.ctx_lens), p(self.unit_order), self.n_host_units)
+
+
+def place_paged_kv(K: torch.Tensor, V: torch.Tensor, ctx_lens, page: int, host_units=(), seed: Optional[int] = None,
+                   device=None) -> PagedKV:
+    """Page K, V [B, Hkv, ctx, D] into two pools.  Unit u = b * Hkv + g is a
+    host unit iff u is in host_units; each unit gets ceil(len_b / page) pages
+    of its tier's pool (len_b = ctx_lens[b] clamped to [0, ctx]).  With a seed
+    the pages' pool indices are a seeded random permutation (a pool after
+    churn), otherwise they are in unit order."""
+    if K.shape != V.shape or K.dim() != 4 or K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+        raise ValueError("K and V must be bf16 tensors of equal shape [B, Hkv, ctx, D]")
+    if page < 16 or page & (page - 1):
+        raise ValueError("page must be a power of two >= 16")
+    B, Hkv, ctx, D = K.shape
+    units = B * Hkv
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lens = [min(max(int(v), 0), ctx) for v in torch.as_tensor(ctx_lens).tolist()]
+    if len(lens) != B:
+        raise ValueError("ctx_lens needs one entry per request")
+    host = sorted(set(int(u) for u in host_units))
+    if any(not 0 <= u < units for u in host):
+        raise ValueError("host unit out of range")
+    hs = set(host)
+    order = host + [u for u in range(units) if u not in hs]
+    max_pages = max(1, -(-ctx // page))
+    table = torch.full((units, max_pages), -1, dtype=torch.int32)
+    padded = max_pages * page
+    Kf, Vf = K.reshape(units, ctx, D), V.reshape(units, ctx, D)
+    gen = None
+    if seed is not None:
+        gen = torch.Generator().manual_seed(seed)
+    pools = []
+    for tier_units, pinned in ((host, True), ([u for u in range(units) if u not in hs], False)):
+        pairs = [(u, i) for u in tier_units for i in range(-(-lens[u // Hkv] // page))]
+        n = len(pairs)
+        if n == 0:
+            pools.append((None, None))
+            continue
+        idx = torch.randperm(n, generator=gen) if gen is not None else torch.arange(n)
+        uu = torch.tensor([u for u, _ in pairs])
+        ii = torch.tensor([i for _, i in pairs])
+        table[uu, ii] = idx.to(torch.int32)
+        kp, vp = [], []
+        for src in (Kf, Vf):
+            s = src.to(device)
+            if padded != ctx:
+                s = torch.nn.functional.pad(s, (0, 0, 0, padded - ctx))
+            s = s.reshape(units, max_pages, page, D)
+            pool = torch.empty((n, page, D), dtype=torch.bfloat16, device=device)
+            pool[idx.to(device)] = s[uu.to(device), ii.to(device)]
+            if pinned:
+                ph = torch.empty((n, page, D), dtype=torch.bfloat16, pin_memory=True)
+                ph.copy_(pool)
+                pool = ph
+            (kp if src is Kf else vp).append(pool)
+        pools.append((kp[0], vp[0]))
+    (kh, vh), (kg, vg) = pools
+    return PagedKV(kh, vh, kg, vg, table.to(device), torch.tensor(lens, dtype=torch.int32, device=device),
+                   torch.tensor(order, dtype=torch.int32, device=device), B, Hkv, D, page, len(host))
+
+
+def paged_decode_attn_workspace_bytes(kv: PagedKV, n_q_heads: int) -> int:
+    d = kv.desc()
+    return int(library().dak_paged_decode_attn_workspace_bytes(C.byref(d), int(n_q_heads)))
+
+
+def paged_decode_attn(q: torch.Tensor, kv: PagedKV, scale: float, out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, cfg: Optional[LaunchConfig] = None,
+                      stream=None) -> torch.Tensor:
+    """out [B, Hq, D] fp32 from q bf16 [B, Hq, D] over a paged split KV cache."""
+    lib = library()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 CUDA tensor [B, Hq, D]")
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    need = paged_decode_attn_workspace_bytes(kv, Hq)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    d = kv.desc()
+    c, cp = _cfg_ptr(cfg)
+    _check(lib.dak_paged_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
+                                     ws.data_ptr(), ws.numel() * ws.element_size(), cp, _stream_handle(stream)))
     return out
 
 

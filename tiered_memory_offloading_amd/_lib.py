@@ -36,6 +36,14 @@ class SplitKVDesc(C.Structure):
                 ("ctx", C.c_int64), ("unit", C.c_int32), ("reserved", C.c_int32), ("ctx_lens", C.c_void_p)]
 
 
+class PagedKVDesc(C.Structure):
+    _fields_ = [("k_host", C.c_void_p), ("v_host", C.c_void_p), ("k_hbm", C.c_void_p), ("v_hbm", C.c_void_p),
+                ("host_pages", C.c_int64), ("hbm_pages", C.c_int64), ("batch", C.c_int64),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("page", C.c_int32), ("max_pages", C.c_int32),
+                ("page_table", C.c_void_p), ("ctx_lens", C.c_void_p), ("unit_order", C.c_void_p),
+                ("n_host_units", C.c_int64)]
+
+
 # (name, restype, argtypes) for every symbol include/dak.h declares.
 SIGNATURES = [
     ("dak_last_error", C.c_char_p, []),
@@ -52,6 +60,9 @@ SIGNATURES = [
     ("dak_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(SplitKVDesc), C.c_int32]),
     ("dak_splitk_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(SplitKVDesc), C.c_int32, C.c_float, C.c_void_p,
                                            C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_paged_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(PagedKVDesc), C.c_int32]),
+    ("dak_paged_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(PagedKVDesc), C.c_int32, C.c_float, C.c_void_p,
+                                          C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),
     ("dak_probe_read", C.c_int32, [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                    C.POINTER(C.c_float)]),
     ("dak_probe_read_concurrent", C.c_int32, [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,

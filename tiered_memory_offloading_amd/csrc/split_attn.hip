@@ -63,12 +63,37 @@ __device__ __forceinline__ void merge_state(float (&m)[G], float (&l)[G], float 
   }
 }
 
+// Where token t of one unit's K and V rows lies.  Dense: a contiguous
+// [len, D] block.
+struct DenseRows {
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  __device__ __forceinline__ int64_t off(int64_t /*ts*/, int64_t t) const { return t * kD; }
+};
+
+// Paged: token t lies in the unit's page t >> shift, at row t & (2^shift - 1)
+// of a [2^shift, D] pool page.  A wave's tokens span at most 32 pages (pages
+// hold 16 tokens or more); lane l holds the pool index of page p0 + l, and the
+// page of the 16-token tile starting at ts (a tile never straddles pages) is
+// read from that lane.
+struct PagedRows {
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  int shift;
+  int64_t p0;
+  int id;
+  __device__ __forceinline__ int64_t off(int64_t ts, int64_t t) const {
+    const int pid = __builtin_amdgcn_readlane(id, (int)(((ts >> shift) - p0) & 63));
+    return (((int64_t)pid << shift) + (t & ((int64_t(1) << shift) - 1))) * kD;
+  }
+};
+
 // Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the lane
 // group's online-softmax state.  qb holds the lane's 8 query dims per head as
 // bf16 pairs (unscaled); qscale = scale * log2(e).
-template <int G, int U, bool COUNT>
-__device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, const uint16_t* __restrict__ Vbg,
-                                            int64_t tb, int64_t te, const uint32_t (&qb)[G][4], float qscale,
+template <int G, int U, bool COUNT, class Rows>
+__device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_t te, const uint32_t (&qb)[G][4],
+                                            float qscale,
                                             float (&m)[G], float (&l)[G], float (&o)[G][8], int lane,
                                             uint64_t& nbytes) {
   const int grp = lane >> 4;
@@ -78,12 +103,14 @@ __device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, co
     uint4 kv[U][4], vv[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int64_t ts = tb + (t0 + u) * kTile;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t t = tb + (t0 + u) * kTile + 4 * i + grp;
+        const int64_t t = ts + 4 * i + grp;
         const bool ok = (t0 + u < ntiles) && (t < te);
-        kv[u][i] = ok ? ld16(Kbg + t * kD + dq) : make_uint4(0, 0, 0, 0);
-        vv[u][i] = ok ? ld16(Vbg + t * kD + dq) : make_uint4(0, 0, 0, 0);
+        const int64_t r = rows.off(ts, t) + dq;
+        kv[u][i] = ok ? ld16(rows.k + r) : make_uint4(0, 0, 0, 0);
+        vv[u][i] = ok ? ld16(rows.v + r) : make_uint4(0, 0, 0, 0);
         if (COUNT && ok) nbytes += 32;
       }
     }
@@ -151,14 +178,15 @@ __device__ __forceinline__ void attn_tokens(const uint16_t* __restrict__ Kbg, co
   }
 }
 
-// One (b, g, chunk) item: every wave walks its 256 tokens, then the states are
+// One (b, g, chunk) item: every wave walks its 512 tokens, then the states are
 // merged (lane groups, then waves in order) and the chunk partial is written.
-template <int G, int U, bool COUNT>
-__device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kbg,
-                                          const uint16_t* __restrict__ Vbg, int64_t b, int g, int c, int64_t len,
-                                          int Hq, int C, float qscale, float* __restrict__ o_ws,
-                                          float* __restrict__ ml_ws, float* red_o, float* red_ml, int wave,
-                                          int lane, uint64_t& nbytes) {
+// A poisoned item (uniform over the work-group) reads nothing and writes a
+// partial with o = l = NaN, which makes its rows NaN after the combine.
+template <int G, int U, bool COUNT, class Rows>
+__device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const Rows& rows, bool poison, int64_t b,
+                                          int g, int c, int64_t len, int Hq, int C, float qscale,
+                                          float* __restrict__ o_ws, float* __restrict__ ml_ws, float* red_o,
+                                          float* red_ml, int wave, int lane, uint64_t& nbytes) {
   const int dq = (lane & 15) * 8;
   uint32_t qb[G][4];
 #pragma unroll
@@ -179,7 +207,7 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
   }
   const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
   const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
-  attn_tokens<G, U, COUNT>(Kbg, Vbg, tb, te, qb, qscale, m, l, o, lane, nbytes);
+  if (!poison) attn_tokens<G, U, COUNT>(rows, tb, te, qb, qscale, m, l, o, lane, nbytes);
 
   // Merge the four lane groups (xor 16, then xor 32).
 #pragma unroll
@@ -225,10 +253,10 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
       mm = mn;
     }
     const int64_t rec = ((b * Hq) + g * G + h) * C + c;
-    o_ws[rec * kD + d] = oo;
+    o_ws[rec * kD + d] = poison ? __builtin_nanf("") : oo;
     if (d == 0) {
-      ml_ws[rec * 2 + 0] = mm;
-      ml_ws[rec * 2 + 1] = ll;
+      ml_ws[rec * 2 + 0] = poison ? 0.f : mm;
+      ml_ws[rec * 2 + 1] = poison ? __builtin_nanf("") : ll;
     }
   }
   __syncthreads();   // LDS reused by the next item
@@ -264,8 +292,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
       const int c = (int)(it % C);
       const int64_t b = u / Hkv, len = valid_len(ctx_lens, b, ctx);
       if ((int64_t)c * kChunk >= len) continue;   // uniform
-      attn_item<G, UH, COUNT>(q, k_host + u * ctx * kD, v_host + u * ctx * kD, b, (int)(u % Hkv), c, len, Hq, C,
-                              qscale, o_ws, ml_ws, red_o, red_ml, wave, lane, nbytes);
+      const DenseRows rows{k_host + u * ctx * kD, v_host + u * ctx * kD};
+      attn_item<G, UH, COUNT>(q, rows, false, b, (int)(u % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o, red_ml,
+                              wave, lane, nbytes);
     }
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
@@ -273,9 +302,89 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
       const int64_t u = it / C, gu = h_units + u;
       const int c = (int)(it % C);
       const int64_t b = gu / Hkv, len = valid_len(ctx_lens, b, ctx);
-      if ((int64_t)c * kChunk < len)
-        attn_item<G, UG, COUNT>(q, k_hbm + u * ctx * kD, v_hbm + u * ctx * kD, b, (int)(gu % Hkv), c, len, Hq, C,
-                                qscale, o_ws, ml_ws, red_o, red_ml, wave, lane, nbytes);
+      if ((int64_t)c * kChunk < len) {
+        const DenseRows rows{k_hbm + u * ctx * kD, v_hbm + u * ctx * kD};
+        attn_item<G, UG, COUNT>(q, rows, false, b, (int)(gu % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o,
+                                red_ml, wave, lane, nbytes);
+      }
+    }
+  }
+  if (COUNT) {
+    uint64_t v = nbytes;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&counters[host_role ? 0 : 1], (unsigned long long)v);
+  }
+}
+
+// Paged items are (order slot i, chunk c) with unit u = unit_order[i]; the
+// first n_host slots are host units.  Each wave fetches the pool indices of
+// the pages its tokens span (lane l: page p0 + l) and checks them against its
+// pool; one bad index poisons the whole item, so nothing outside a pool is
+// ever read.
+template <int G, int U, bool COUNT>
+__device__ __forceinline__ void paged_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool_k,
+                                           const uint16_t* __restrict__ pool_v, int64_t pool_pages, int64_t u,
+                                           int Hkv, int Hq, int shift, int max_pages,
+                                           const int32_t* __restrict__ page_table,
+                                           const int32_t* __restrict__ ctx_lens, int c, int C, float qscale,
+                                           float* __restrict__ o_ws, float* __restrict__ ml_ws, float* red_o,
+                                           float* red_ml, int* bad_w, int wave, int lane, uint64_t& nbytes) {
+  const int64_t b = u / Hkv;
+  const int64_t len = valid_len(ctx_lens, b, (int64_t)max_pages << shift);
+  if ((int64_t)c * kChunk >= len) return;   // uniform: no tokens in this chunk
+  const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
+  const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
+  const int64_t p0 = tb >> shift;
+  int id = 0;
+  bool bad = false;
+  if (te > tb) {
+    const int64_t p = p0 + lane;
+    if (p <= ((te - 1) >> shift)) {
+      id = page_table[u * max_pages + p];
+      bad = id < 0 || id >= pool_pages;
+    }
+  }
+  const bool wbad = __any(bad);
+  if (lane == 0) bad_w[wave] = wbad ? 1 : 0;
+  __syncthreads();
+  int poison = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) poison |= bad_w[w];
+  const PagedRows rows{pool_k, pool_v, shift, p0, id};
+  // attn_item ends with a barrier, after which bad_w may be rewritten.
+  attn_item<G, U, COUNT>(q, rows, poison != 0, b, (int)(u % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o, red_ml,
+                         wave, lane, nbytes);
+}
+
+template <int G, int UH, int UG, bool COUNT>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_paged(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_host, const uint16_t* __restrict__ v_host,
+    const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t host_pages, int64_t hbm_pages,
+    int64_t units, int Hkv, int Hq, int shift, int max_pages, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ unit_order, int64_t n_host, int C,
+    float qscale, float* __restrict__ o_ws, float* __restrict__ ml_ws, int host_wgs, int64_t host_items,
+    int64_t hbm_items, unsigned long long* __restrict__ counters) {
+  __shared__ float red_o[kAttnWaves * G * kD];
+  __shared__ float red_ml[kAttnWaves * G * 2];
+  __shared__ int bad_w[kAttnWaves];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t nbytes = 0;
+  const bool host_role = (int)blockIdx.x < host_wgs;
+  if (host_role) {
+    for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
+      const int64_t u = unit_order[it / C];
+      if (u < 0 || u >= units) continue;   // uniform
+      paged_item<G, UH, COUNT>(q, k_host, v_host, host_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens,
+                               (int)(it % C), C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
+    }
+  } else {
+    const int64_t it = (int64_t)blockIdx.x - host_wgs;
+    if (it < hbm_items) {
+      const int64_t u = unit_order[n_host + it / C];
+      if (u >= 0 && u < units)
+        paged_item<G, UG, COUNT>(q, k_hbm, v_hbm, hbm_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens,
+                                 (int)(it % C), C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
     }
   }
   if (COUNT) {
@@ -345,34 +454,90 @@ struct AttnArgs {
   hipStream_t stream;
 };
 
-template <int G, int UH, bool COUNT>
-void launch_partial_g(const AttnArgs& a) {
-  constexpr int UG = G >= 8 ? 1 : 2;
-  constexpr int UHc = G >= 8 ? 1 : (G >= 4 && UH > 2 ? 2 : UH);
-  const int64_t grid = a.host_wgs + a.hbm_items;
-  hipLaunchKernelGGL((attn_partial_split<G, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0,
-                     a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_units, a.Hkv, a.Hq, a.ctx, a.C,
-                     a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
-}
+struct PagedArgs {
+  const uint16_t *q, *k_host, *v_host, *k_hbm, *v_hbm;
+  int64_t host_pages, hbm_pages, units;
+  int Hkv, Hq, shift, max_pages;
+  const int32_t *page_table, *ctx_lens, *unit_order;
+  int64_t n_host;
+  int C;
+  float qscale;
+  float *o_ws, *ml_ws;
+  int host_wgs;
+  int64_t host_items, hbm_items;
+  unsigned long long* counters;
+  hipStream_t stream;
+};
 
-template <int UH, bool COUNT>
-void launch_partial(const AttnArgs& a, int G) {
+// Per-role unroll: tiles in flight per wave (UH for host work-groups, the
+// window; UG for HBM work-groups), capped by the registers of larger groups.
+template <int G, int UH>
+struct Unroll {
+  static constexpr int kG = G >= 8 ? 1 : 2;
+  static constexpr int kH = G >= 8 ? 1 : (G >= 4 && UH > 2 ? 2 : UH);
+};
+
+struct DenseLaunch {
+  using Args = AttnArgs;
+  template <int G, int UH, bool COUNT>
+  static void run(const Args& a) {
+    using Un = Unroll<G, UH>;
+    const int64_t grid = a.host_wgs + a.hbm_items;
+    hipLaunchKernelGGL((attn_partial_split<G, Un::kH, Un::kG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64),
+                       0, a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_units, a.Hkv, a.Hq, a.ctx, a.C,
+                       a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
+  }
+};
+
+struct PagedLaunch {
+  using Args = PagedArgs;
+  template <int G, int UH, bool COUNT>
+  static void run(const Args& a) {
+    using Un = Unroll<G, UH>;
+    const int64_t grid = a.host_wgs + a.hbm_items;
+    hipLaunchKernelGGL((attn_partial_paged<G, Un::kH, Un::kG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64),
+                       0, a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.host_pages, a.hbm_pages, a.units,
+                       a.Hkv, a.Hq, a.shift, a.max_pages, a.page_table, a.ctx_lens, a.unit_order, a.n_host, a.C,
+                       a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
+  }
+};
+
+template <class L, int UH, bool COUNT>
+void launch_partial(const typename L::Args& a, int G) {
   switch (G) {
-    case 1: return launch_partial_g<1, UH, COUNT>(a);
-    case 2: return launch_partial_g<2, UH, COUNT>(a);
-    case 4: return launch_partial_g<4, UH, COUNT>(a);
-    default: return launch_partial_g<8, UH, COUNT>(a);
+    case 1: return L::template run<1, UH, COUNT>(a);
+    case 2: return L::template run<2, UH, COUNT>(a);
+    case 4: return L::template run<4, UH, COUNT>(a);
+    default: return L::template run<8, UH, COUNT>(a);
   }
 }
 
-template <bool COUNT>
-void launch_partial_w(const AttnArgs& a, int G, int window) {
-  switch (window) {
-    case 1: return launch_partial<1, COUNT>(a, G);
-    case 2: return launch_partial<2, COUNT>(a, G);
-    case 8: return launch_partial<8, COUNT>(a, G);
-    default: return launch_partial<4, COUNT>(a, G);
+template <class L>
+void launch_partial_w(const typename L::Args& a, int G, int window, bool count) {
+  if (count) {
+    switch (window) {
+      case 1: return launch_partial<L, 1, true>(a, G);
+      case 2: return launch_partial<L, 2, true>(a, G);
+      case 8: return launch_partial<L, 8, true>(a, G);
+      default: return launch_partial<L, 4, true>(a, G);
+    }
   }
+  switch (window) {
+    case 1: return launch_partial<L, 1, false>(a, G);
+    case 2: return launch_partial<L, 2, false>(a, G);
+    case 8: return launch_partial<L, 8, false>(a, G);
+    default: return launch_partial<L, 4, false>(a, G);
+  }
+}
+
+// Host window in tiles: one tile is 4 waves x 16 tokens x (K + V) = 32 KiB per
+// work-group.  Without host work-groups the window does not apply; the
+// one-tile instance needs the fewest registers (more waves per SIMD for the
+// HBM role).
+int attn_window(int cfg_window, int host_wgs, int G) {
+  if (cfg_window) return cfg_window;
+  if (host_wgs == 0) return 1;
+  return auto_window(host_wgs, 32u << 10, G >= 8 ? 1 : G >= 4 ? 2 : 8);
 }
 
 // Host units in (request, KV head) pairs, or -1 for an invalid unit code.
@@ -463,21 +628,119 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   a.stream = static_cast<hipStream_t>(stream);
   if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
-  // Host window: one tile is 4 waves x 16 tokens x (K + V) = 32 KiB per work-group.
-  // Without host work-groups the window does not apply; the one-tile instance
-  // needs the fewest registers (more waves per SIMD for the HBM role).
-  const int window = lc.window         ? lc.window
-                     : a.host_wgs == 0 ? 1
-                                       : auto_window(a.host_wgs, 32u << 10, G >= 8 ? 1 : G >= 4 ? 2 : 8);
-  if (lc.flags & DAK_FLAG_COUNT_BYTES)
-    launch_partial_w<true>(a, G, window);
-  else
-    launch_partial_w<false>(a, G, window);
+  launch_partial_w<DenseLaunch>(a, G, attn_window(lc.window, a.host_wgs, G), (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
                      n_q_heads, ctx, a.ctx_lens, out);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");
+  return DAK_OK;
+}
+
+namespace dak {
+namespace {
+
+bool paged_shapes_ok(const dak_paged_kv* kv, int32_t n_q_heads) {
+  if (!kv || kv->batch < 1 || kv->batch > (int64_t(1) << 24) || kv->n_kv_heads < 1 || kv->n_kv_heads > 4096)
+    return false;
+  if (n_q_heads < 1 || n_q_heads > 4096 || n_q_heads % kv->n_kv_heads != 0 || kv->head_dim != kD) return false;
+  const int64_t page = kv->page;
+  if (page < 16 || page > (int64_t(1) << 20) || (page & (page - 1)) != 0) return false;
+  if (kv->max_pages < 1 || (int64_t)kv->max_pages * page > (int64_t(1) << 31)) return false;
+  const int64_t units = kv->batch * kv->n_kv_heads;
+  const int64_t pool_cap = (int64_t(1) << 40) / (page * kD * 2);   // 1 TiB per pool
+  return kv->n_host_units >= 0 && kv->n_host_units <= units && kv->host_pages >= 0 && kv->hbm_pages >= 0 &&
+         kv->host_pages <= pool_cap && kv->hbm_pages <= pool_cap && kv->host_pages < (int64_t(1) << 31) &&
+         kv->hbm_pages < (int64_t(1) << 31);
+}
+
+int64_t paged_chunks(const dak_paged_kv* kv) { return ((int64_t)kv->max_pages * kv->page + kChunk - 1) / kChunk; }
+
+}  // namespace
+}  // namespace dak
+
+extern "C" size_t dak_paged_decode_attn_workspace_bytes(const dak_paged_kv* kv, int32_t n_q_heads) {
+  using namespace dak;
+  if (!paged_shapes_ok(kv, n_q_heads)) return 0;
+  return (size_t)(kv->batch * n_q_heads * paged_chunks(kv)) * (kD + 2) * sizeof(float);
+}
+
+extern "C" dak_status dak_paged_decode_attn(const void* q, const dak_paged_kv* kv, int32_t n_q_heads, float scale,
+                                            float* out, void* ws, size_t ws_bytes, const dak_launch_cfg* cfg,
+                                            void* stream) {
+  using namespace dak;
+  clear_error();
+  if (!kv) return fail(DAK_EINVAL, "kv is NULL");
+  if (kv->head_dim != kD) return fail(DAK_EUNSUPPORTED, "head_dim %d (only 128 is built)", kv->head_dim);
+  if (!paged_shapes_ok(kv, n_q_heads))
+    return fail(DAK_EINVAL,
+                "bad shapes: batch=%lld Hkv=%d Hq=%d page=%d max_pages=%d n_host_units=%lld host_pages=%lld "
+                "hbm_pages=%lld",
+                (long long)kv->batch, kv->n_kv_heads, n_q_heads, kv->page, kv->max_pages,
+                (long long)kv->n_host_units, (long long)kv->host_pages, (long long)kv->hbm_pages);
+  const int G = n_q_heads / kv->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(DAK_EUNSUPPORTED, "group size %d is not 1, 2, 4 or 8", G);
+  if (!std::isfinite(scale)) return fail(DAK_EINVAL, "scale must be finite");
+  LaunchCfg lc;
+  dak_status st = resolve_cfg(cfg, kAttnDefaults, &lc);
+  if (st) return st;
+  const size_t need = dak_paged_decode_attn_workspace_bytes(kv, n_q_heads);
+  if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+
+  const int64_t B = kv->batch, units = B * kv->n_kv_heads;
+  const uint64_t page_bytes = (uint64_t)kv->page * kD * 2;
+  const void *dq = nullptr, *dkh = nullptr, *dvh = nullptr, *dkg = nullptr, *dvg = nullptr, *dtab = nullptr,
+             *dlens = nullptr, *dord = nullptr, *dout = nullptr, *dws = nullptr;
+  if ((st = check_tier_ptr(q, (uint64_t)B * n_q_heads * kD * 2, Tier::kDevice, "q", &dq))) return st;
+  if (kv->host_pages > 0) {
+    if ((st = check_tier_ptr(kv->k_host, page_bytes * kv->host_pages, Tier::kHost, "k_host", &dkh))) return st;
+    if ((st = check_tier_ptr(kv->v_host, page_bytes * kv->host_pages, Tier::kHost, "v_host", &dvh))) return st;
+  }
+  if (kv->hbm_pages > 0) {
+    if ((st = check_tier_ptr(kv->k_hbm, page_bytes * kv->hbm_pages, Tier::kDevice, "k_hbm", &dkg))) return st;
+    if ((st = check_tier_ptr(kv->v_hbm, page_bytes * kv->hbm_pages, Tier::kDevice, "v_hbm", &dvg))) return st;
+  }
+  if ((st = check_tier_ptr(kv->page_table, (uint64_t)units * kv->max_pages * 4, Tier::kDevice, "page_table", &dtab)))
+    return st;
+  if ((st = check_tier_ptr(kv->ctx_lens, (uint64_t)B * 4, Tier::kDevice, "ctx_lens", &dlens))) return st;
+  if ((st = check_tier_ptr(kv->unit_order, (uint64_t)units * 4, Tier::kDevice, "unit_order", &dord))) return st;
+  if ((st = check_tier_ptr(out, (uint64_t)B * n_q_heads * kD * 4, Tier::kDevice, "out", &dout))) return st;
+  if ((st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws))) return st;
+
+  PagedArgs a;
+  a.q = static_cast<const uint16_t*>(dq);
+  a.k_host = static_cast<const uint16_t*>(dkh);
+  a.v_host = static_cast<const uint16_t*>(dvh);
+  a.k_hbm = static_cast<const uint16_t*>(dkg);
+  a.v_hbm = static_cast<const uint16_t*>(dvg);
+  a.host_pages = kv->host_pages;
+  a.hbm_pages = kv->hbm_pages;
+  a.units = units;
+  a.Hkv = kv->n_kv_heads;
+  a.Hq = n_q_heads;
+  a.shift = __builtin_ctz((unsigned)kv->page);
+  a.max_pages = kv->max_pages;
+  a.page_table = static_cast<const int32_t*>(dtab);
+  a.ctx_lens = static_cast<const int32_t*>(dlens);
+  a.unit_order = static_cast<const int32_t*>(dord);
+  a.n_host = kv->n_host_units;
+  a.C = (int)paged_chunks(kv);
+  a.qscale = scale * 1.4426950408889634f;
+  a.o_ws = static_cast<float*>(ws);
+  a.ml_ws = a.o_ws + (size_t)B * n_q_heads * a.C * kD;
+  a.host_items = kv->n_host_units * a.C;
+  a.hbm_items = (units - kv->n_host_units) * a.C;
+  a.host_wgs = (int)host_workgroups(a.host_items, lc.host_cus);
+  a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+  a.stream = static_cast<hipStream_t>(stream);
+  if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
+  launch_partial_w<PagedLaunch>(a, G, attn_window(lc.window, a.host_wgs, G), (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "paged attention partial launch");
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
+                     n_q_heads, (int64_t)kv->max_pages * kv->page, a.ctx_lens, out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "paged attention combine launch");
   return DAK_OK;
 }

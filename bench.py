@@ -528,6 +528,81 @@ def run_linears(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_paged(torch, dak, args, b_hbm, b_host):
+    """Paged against dense split decode attention at the Llama-8B decode size
+    (batch 16, 32 query / 8 KV heads, head_dim 128, 32768 cached tokens; K, V
+    ~N(0, 1)).  Paged: 16-token pages at seeded random pool indices (a pool
+    after churn) and a seeded random set of host (request, KV head) units, as
+    BOOST's single-head-host placement leaves them; dense: the same number of
+    head units, the first ones.  Two length mixes: every request full, and
+    lengths uniform in [1, 32768] (seeded).  Each point is the mean over
+    `--sweep-steps` launches after one untimed launch; paged outputs are
+    checked bit-identical to dense."""
+    reps = max(1, args.sweep_steps)
+    B, Hq, Hkv, D, ctx, page = 16, 32, 8, 128, 32768, 16
+    units = B * Hkv
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=7, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    gen = torch.Generator().manual_seed(11)
+    mixes = {"full": [ctx] * B, "ragged": torch.randint(1, ctx + 1, (B,), generator=gen).tolist()}
+    points = []
+    for mix, lens in mixes.items():
+        lens_t = torch.tensor(lens, dtype=torch.int32)
+        unit_bytes = [lens[u // Hkv] * D * 2 * 2 for u in range(units)]
+        total = sum(unit_bytes)
+        for h in (0, 4, 8, 16):
+            host_set = torch.randperm(units, generator=torch.Generator().manual_seed(100 + h))[:h].tolist()
+            kvd = dak.place_kv(K, V, h, unit=dak.KV_UNIT_HEAD, ctx_lens=lens_t)
+            kvp = dak.place_paged_kv(K, V, lens_t, page, host_set, seed=h)
+            od = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+            op_ = torch.empty_like(od)
+            wsd = torch.empty(dak.decode_attn_workspace_bytes(kvd, Hq), dtype=torch.uint8, device="cuda")
+            wsp = torch.empty(dak.paged_decode_attn_workspace_bytes(kvp, Hq), dtype=torch.uint8, device="cuda")
+            td = timed(lambda: dak.splitk_decode_attn(q, kvd, scale, out=od, ws=wsd))
+            tp = timed(lambda: dak.paged_decode_attn(q, kvp, scale, out=op_, ws=wsp))
+            same = bool(torch.equal(od, op_))
+            for kind, t, hb in (("dense", td, sum(unit_bytes[:h])), ("paged", tp, sum(unit_bytes[u] for u in host_set))):
+                t_roof = max((total - hb) / (b_hbm * 1e9), hb / (b_host * 1e9)) * 1e3
+                points.append({"mix": mix, "kind": kind, "host_units": h, "x": round(hb / total, 4),
+                               "ms": round(t, 4), "GBps": round(total / (t * 1e-3) / 1e9, 1),
+                               "frac_two_tier": round(t_roof / t, 4)})
+            log(f"{mix} h={h}: dense {td:.3f} ms, paged {tp:.3f} ms ({tp / td:.3f}x)"
+                f"{'' if same else ' BITS DIFFER'}")
+            points[-1]["bit_identical_to_dense"] = points[-2]["bit_identical_to_dense"] = same
+            del kvd, kvp, wsd, wsp
+            torch.cuda.empty_cache()
+    paged_pts = [p for p in points if p["kind"] == "paged"]
+    ratios = [p["ms"] / d["ms"] for p, d in zip(points[1::2], points[0::2])]
+    res = {
+        "metric": "paged split decode attention: time relative to the dense split kernel, and % of two-tier roofline",
+        "value": round(statistics.mean(p["frac_two_tier"] for p in paged_pts), 4),
+        "unit": "mean fraction of the two-tier roofline over the paged points",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "Llama-8B decode attention, batch 16, 32q/8kv heads, head_dim 128, 32768 tokens, "
+                               "16-token pages at random pool indices, 0/4/8/16 host (request, KV head) units; "
+                               "full and ragged (uniform [1, 32768]) lengths"},
+        "paged_over_dense_time": {"mean": round(statistics.mean(ratios), 4), "max": round(max(ratios), 4)},
+        "all_bit_identical_to_dense": all(p["bit_identical_to_dense"] for p in points),
+        "ragged_lengths": mixes["ragged"],
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "points": points,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def run_plan_compare(torch, dak, args, b_hbm, b_host):
     """Greedy per-op ratios against one uniform ratio (DAK §4.2.2 and its
     evaluation of per-op ratios at large batch): one Llama-8B decoder layer at
@@ -614,12 +689,14 @@ def main(argv=None):
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
-    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare"),
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare",
+                                           "paged"),
                     default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
                          "at N in {1,16,64} over x = 0..0.5, cold; plan-compare: greedy per-op ratios against a "
-                         "uniform ratio for one decoder layer at large batch (each prints its own JSON line)")
+                         "uniform ratio for one decoder layer at large batch; paged: paged against dense "
+                         "split attention (each prints its own JSON line)")
     ap.add_argument("--plan-batch", type=int, default=512, help="plan-compare: batch (activation rows N)")
     ap.add_argument("--plan-ctx", type=int, default=2048, help="plan-compare: tokens per request")
     ap.add_argument("--plan-x", type=float, nargs="+", default=[0.01, 0.02, 0.05],
@@ -656,6 +733,8 @@ def main(argv=None):
         return run_linears(torch, dak, args, b_hbm, b_host)
     if args.workload == "plan-compare":
         return run_plan_compare(torch, dak, args, b_hbm, b_host)
+    if args.workload == "paged":
+        return run_paged(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

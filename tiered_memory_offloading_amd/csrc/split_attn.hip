@@ -270,6 +270,20 @@ __device__ __forceinline__ int64_t valid_len(const int32_t* __restrict__ ctx_len
   return v < 0 ? 0 : v > ctx ? ctx : v;
 }
 
+// Item k of a role's n units x C chunks: chunk c = k / n, unit (k - c + c * n)
+// mod n, i.e. chunk-major with the units rotated by c.  Work-group k runs on
+// XCD k mod 8 (plus the role's offset), so when n is a multiple of 8 unit u's
+// chunk c lands on XCD (u + c) mod 8: a unit's chunks spread over the XCDs
+// and, with ragged lengths, the first chunks (the ones every request has) do
+// not pile onto the same XCDs.
+__device__ __forceinline__ void item_of(int64_t k, int64_t n, int64_t& u, int& c) {
+  const int64_t cc = k / n;
+  const int64_t r = k - cc * n;
+  const int64_t rot = cc % n;
+  u = r >= rot ? r - rot : r - rot + n;
+  c = (int)cc;
+}
+
 // Items are (unit, chunk) pairs, unit u = b * Hkv + g (a request's KV head);
 // the first h_units units live in host memory, each a [ctx, D] block of K and
 // of V at offset u * ctx * D of its tier.  Chunks past a request's valid
@@ -288,8 +302,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
   const bool host_role = (int)blockIdx.x < host_wgs;
   if (host_role) {
     for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
-      const int64_t u = it / C;
-      const int c = (int)(it % C);
+      int64_t u;
+      int c;
+      item_of(it, h_units, u, c);
       const int64_t b = u / Hkv, len = valid_len(ctx_lens, b, ctx);
       if ((int64_t)c * kChunk >= len) continue;   // uniform
       const DenseRows rows{k_host + u * ctx * kD, v_host + u * ctx * kD};
@@ -299,8 +314,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
     if (it < hbm_items) {
-      const int64_t u = it / C, gu = h_units + u;
-      const int c = (int)(it % C);
+      int64_t u;
+      int c;
+      item_of(it, hbm_items / C, u, c);
+      const int64_t gu = h_units + u;
       const int64_t b = gu / Hkv, len = valid_len(ctx_lens, b, ctx);
       if ((int64_t)c * kChunk < len) {
         const DenseRows rows{k_hbm + u * ctx * kD, v_hbm + u * ctx * kD};
@@ -373,18 +390,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_paged(
   const bool host_role = (int)blockIdx.x < host_wgs;
   if (host_role) {
     for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
-      const int64_t u = unit_order[it / C];
+      int64_t i;
+      int c;
+      item_of(it, n_host, i, c);
+      const int64_t u = unit_order[i];
       if (u < 0 || u >= units) continue;   // uniform
-      paged_item<G, UH, COUNT>(q, k_host, v_host, host_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens,
-                               (int)(it % C), C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
+      paged_item<G, UH, COUNT>(q, k_host, v_host, host_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens, c,
+                               C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
     }
   } else {
     const int64_t it = (int64_t)blockIdx.x - host_wgs;
     if (it < hbm_items) {
-      const int64_t u = unit_order[n_host + it / C];
+      int64_t i;
+      int c;
+      item_of(it, units - n_host, i, c);
+      const int64_t u = unit_order[n_host + i];
       if (u >= 0 && u < units)
-        paged_item<G, UG, COUNT>(q, k_hbm, v_hbm, hbm_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens,
-                                 (int)(it % C), C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
+        paged_item<G, UG, COUNT>(q, k_hbm, v_hbm, hbm_pages, u, Hkv, Hq, shift, max_pages, page_table, ctx_lens, c,
+                                 C, qscale, o_ws, ml_ws, red_o, red_ml, bad_w, wave, lane, nbytes);
     }
   }
   if (COUNT) {

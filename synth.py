@@ -64,6 +64,32 @@ def gemm_inputs(M: int, K: int, N: int, seed: int = 0, a_std: float = 0.02,
     return A, X
 
 
+def fp8_gemm_inputs(M: int, K: int, N: int, seed: int = 0, a_std: float = 0.02, x_std: float = 1.0,
+                    device=None):
+    """FP8 weights as a checkpoint would hold them: codes [M, K] uint8 (OCP
+    E4M3), one fp32 scale per row [M], and activations x [N, K] bf16.
+
+    Weights are drawn ~N(0, a_std) in fp32, each row is scaled so that its
+    largest magnitude maps to 448 (the largest finite e4m3 value) and cast to
+    e4m3 by torch's round-to-nearest-even cast; x ~N(0, x_std) in bf16.
+    Draw order: all of A, then all of x."""
+    gen = torch.Generator(device=device if device is not None else "cpu").manual_seed(seed)
+    Af = torch.randn((M, K), generator=gen, device=gen.device, dtype=torch.float32) * a_std
+    scale = (Af.abs().amax(dim=1) / 448.0).clamp_min(2.0 ** -100)
+    codes = (Af / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    X = normal_bf16((N, K), x_std, gen)
+    return codes, scale, X
+
+
+def fp8_all_codes(M: int, K: int, seed: int = 0, device=None) -> torch.Tensor:
+    """uint8 [M, K] with every finite e4m3 code (all but 0x7F and 0xFF) drawn
+    uniformly: covers zeros, subnormals, both signs and +-448."""
+    gen = torch.Generator(device=device if device is not None else "cpu").manual_seed(seed)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8, device=gen.device)
+    idx = torch.randint(0, finite.numel(), (M, K), generator=gen, device=gen.device)
+    return finite[idx]
+
+
 def int_valued_bf16(shape, lo: int, hi: int, seed: int = 0) -> torch.Tensor:
     """Integers drawn uniformly from [lo, hi] (inclusive), stored exactly in bf16."""
     gen = torch.Generator().manual_seed(seed)

@@ -50,6 +50,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the
+// LDS-DMA form of the global load).  Issued through inline assembly so that
+// the compiler adds no conservative waits for the pending LDS writes; callers
+// order them with their own vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+
+// Wait until at most N vector-memory instructions of this wave are pending.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Host-side validation of a caller pointer covering `bytes` bytes.
 enum class Tier { kHost, kDevice };
 // Checks that [p, p + bytes) lies inside one pinned host allocation (kHost) or

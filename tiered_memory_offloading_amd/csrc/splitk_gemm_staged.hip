@@ -59,20 +59,6 @@ struct StagedShape {
   static_assert(PER_WAVE * 2 <= 63, "vmcnt range");
 };
 
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane.  Issued
-// through inline assembly so that the compiler adds no conservative waits for
-// the pending LDS writes; the kernel's own vmcnt waits and barriers order them.
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
-}
-
-// Wait until at most N vector-memory instructions of this wave are pending.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int NB, int RB, bool COUNT>
 struct StagedItem {
   using S = StagedShape<NB, RB>;

@@ -77,20 +77,6 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // ---------------------------------------------------------------------------
 // HBM role
 // ---------------------------------------------------------------------------
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (the DMA
-// form of the load), issued through inline assembly so that the compiler adds
-// no conservative waits for the pending LDS writes; the tile loop's own vmcnt
-// waits and barriers order them.
-__device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Slot layout: row r (A rows 0..255, then x rows 0..255) holds the step's 32
 // k values as four 16-byte pieces, piece p at position p ^ ((r >> 2) & 3): the
 // 16 lanes that read one MFMA fragment (16 consecutive rows, one piece) then

@@ -202,6 +202,47 @@ typedef struct {
 dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, float* y,
                            const dak_launch_cfg* cfg, void* stream);
 
+/* A weight matrix of FP8 codes, cut along M like dak_split_matrix.  Each
+ * weight is an OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities; 0x7F and 0xFF are NaN) and each row r carries
+ * one fp32 scale: the logical weight is row_scale[r] * e4m3(A[r, k]).  The
+ * pages run their models in FP8 (BOOST §5, Models), which halves the bytes of
+ * every weight tile-row; they do not fix the scaling, so this is the plainest
+ * per-output-channel reading.
+ *   host, hbm   uint8 codes, rows [0, h*m) pinned host / rows [h*m, M) device,
+ *               row-major with leading dimension K (bytes)
+ *   M, K, m, h  as in dak_split_matrix; K a multiple of 16
+ *   row_scale   fp32 [M] in device memory
+ * All pointers 16-byte aligned. */
+typedef struct {
+  const void* host;
+  const void* hbm;
+  int64_t M;
+  int64_t K;
+  int32_t m;
+  int32_t reserved;
+  int64_t h;
+  const float* row_scale;
+} dak_split_matrix_fp8;
+
+/* y[n, r] = row_scale[r] * sum_k e4m3(A[r, k]) * x[n, k] for n < N, r < M.
+ * Each product of an e4m3 weight and a bf16 activation is exact in fp32; the
+ * sums accumulate in fp32 in an order fixed by the shape, and the scale is
+ * applied once to the finished sum, so the result bits do not depend on h,
+ * the host CU cap or the window.  Same split rule as dak_splitk_gemm (DAK
+ * §4.1): disjoint work-groups own disjoint output rows, each reads one tier,
+ * and every host byte crosses the link once.
+ *   A     the FP8 split matrix
+ *   x     bf16 [N, K] in device memory
+ *   N     1 .. 64 (decode batches; larger N is DAK_EUNSUPPORTED)
+ *   y     fp32 [N, M] in device memory; fully written
+ *   cfg   nullable launch configuration (the window does not apply: the
+ *         kernel stages fixed-depth rings)
+ * Errors: DAK_EINVAL for shapes/pointers outside the above, DAK_EUNSUPPORTED
+ * for N > 64.  A NaN code gives NaN in its row. */
+dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
+                               const dak_launch_cfg* cfg, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Split decode attention: KV cache split along the batch                      */
 /* ------------------------------------------------------------------------ */

@@ -18,6 +18,7 @@ Modules:
   planner     -- global capacity ratio and the three-phase greedy per-op planner (DAK §4.2.2)
   brute       -- exhaustive search over per-op plans for tiny op sets (DAK App. A, eq. 1)
   schedule    -- host work-group count from wave alignment under a host-CU cap (DAK §4.1, §4.3.1)
+  fp8         -- the split GEMM over FP8 (OCP E4M3) weights with per-row scales (BOOST §5 runs FP8 models)
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test against
 values the pages print, closed forms or brute force (see tests/test_oracle_*.py).

@@ -171,7 +171,8 @@ def test_binding_structs_match_the_header_layout(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     structs = [("dak_op_desc", L.OpDesc), ("dak_launch_cfg", L.LaunchCfg),
-               ("dak_split_matrix", L.SplitMatrixDesc), ("dak_split_kv", L.SplitKVDesc),
+               ("dak_split_matrix", L.SplitMatrixDesc),
+               ("dak_split_matrix_fp8", L.SplitMatrixFP8Desc), ("dak_split_kv", L.SplitKVDesc),
                ("dak_paged_kv", L.PagedKVDesc)]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dak.h"', "int main(void) {"]
     for cname, py in structs:

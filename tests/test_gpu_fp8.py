@@ -1,0 +1,110 @@
+"""GPU parity of the FP8-weight split GEMM against the fp64 oracle.
+
+FP8 (OCP E4M3) weight codes with one fp32 scale per row, bf16 activations
+(the pages run their models in FP8; DAK §4.1 splits the weight by
+tile-rows).  Bars: normwise error <= 1e-2 (measured ~1e-7: products are exact,
+only the fp32 sums round); bit-identical outputs for every host share; every
+e4m3 code decoded as the format defines it; host bytes read once."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tiered_memory_offloading_amd as dak
+from oracle import fp8 as of
+from oracle.gemm import normwise_error
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def run(codes, scale, x, m, h, cfg=None):
+    S = dak.place_matrix_fp8(codes, scale, m, h)
+    y = dak.splitk_gemm_fp8(S, x.cuda().contiguous(), cfg=cfg)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+@pytest.mark.parametrize("N", [1, 4, 5, 16, 17, 33, 64])
+def test_every_code_and_split(N):
+    # Every finite code, K not a multiple of 32 (a half step at the end).
+    M, K, m = 192, 528, 64
+    codes = synth.fp8_all_codes(M, K, seed=N)
+    gen = torch.Generator().manual_seed(100 + N)
+    scale = torch.rand(M, generator=gen) * 0.01 + 1e-3
+    x = synth.gemm_inputs(16, K, N, seed=N)[1]
+    ref = of.gemm_fp8(codes, scale, x)
+    base = run(codes, scale, x, m, 0)
+    err = normwise_error(base.numpy(), ref)
+    print(f"N={N} normwise error {err:.3e}")
+    assert err <= TOL
+    for h in range(1, M // m + 1):
+        assert torch.equal(run(codes, scale, x, m, h), base), h
+
+
+def test_power_of_two_scales_exact():
+    # Integer-valued codes, power-of-two scales and integer activations: every
+    # partial sum is an exact small integer, so the result is exact.
+    ints = torch.tensor([0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0x00], dtype=torch.uint8)
+    gen = torch.Generator().manual_seed(7)
+    M, K = 128, 1024
+    codes = ints[torch.randint(0, len(ints), (M, K), generator=gen)]
+    scale = 2.0 ** torch.randint(-3, 3, (M,), generator=gen).float()
+    x = torch.randint(-3, 4, (16, K), generator=gen).to(torch.bfloat16)
+    ref = of.gemm_fp8(codes, scale, x)
+    for h in (0, 1, 2):
+        assert np.array_equal(run(codes, scale, x, 64, h).double().numpy(), ref)
+
+
+@pytest.mark.parametrize("name, M, K", [("qkv", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
+@pytest.mark.parametrize("N", [1, 16, 64])
+def test_llama8b_linears_sampled(name, M, K, N):
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, N, seed=3, device="cuda")
+    n = M // 64
+    outs = [run(codes, scale, x, 64, h) for h in (0, n // 4, n)]
+    assert torch.equal(outs[1], outs[0]) and torch.equal(outs[2], outs[0])
+    rows = torch.randperm(M, generator=torch.Generator().manual_seed(N))[:256].sort().values
+    ref = of.gemm_fp8(codes.cpu()[rows], scale.cpu()[rows], x.cpu())
+    err = normwise_error(outs[0][:, rows].numpy(), ref)
+    print(f"{name} N={N} sampled normwise error {err:.3e}")
+    assert err <= TOL
+
+
+def test_host_bytes_read_once():
+    M, K, m, h = 4096, 4096, 64, 16
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, 16, seed=4, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    run(codes, scale, x, m, h, cfg=dak.LaunchConfig(byte_counters=cnt))
+    assert cnt.tolist() == [h * m * K, (M - h * m) * K]
+
+
+def test_nan_code_poisons_its_row_only():
+    M, K = 64, 256
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, 3, seed=5)
+    base = run(codes, scale, x, 64, 0)
+    bad = codes.clone()
+    bad[17, 100] = 0x7F
+    y = run(bad, scale, x, 64, 1)
+    assert torch.isnan(y[:, 17]).all()
+    keep = [r for r in range(M) if r != 17]
+    assert torch.equal(y[:, keep], base[:, keep])
+
+
+def test_fp8_arguments_checked():
+    codes, scale, x = synth.fp8_gemm_inputs(64, 256, 65, seed=6)
+    S = dak.place_matrix_fp8(codes, scale, 64, 0)
+    with pytest.raises(dak.DakError) as e:
+        dak.splitk_gemm_fp8(S, x.cuda())              # N = 65
+    assert e.value.status == -4   # DAK_EUNSUPPORTED
+    S.row_scale = S.row_scale.cpu()                   # scales must be device memory
+    with pytest.raises(dak.DakError):
+        dak.splitk_gemm_fp8(S, x[:8].cuda().contiguous())
+    codes2, scale2, x2 = synth.fp8_gemm_inputs(64, 264, 4, seed=7)   # K % 16 != 0
+    S2 = dak.place_matrix_fp8(codes2, scale2, 64, 0)
+    with pytest.raises(dak.DakError):
+        dak.splitk_gemm_fp8(S2, x2.cuda())

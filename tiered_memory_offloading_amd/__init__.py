@@ -25,6 +25,7 @@ __all__ = [
     "DakError", "LaunchConfig", "SplitMatrix", "SplitKV", "Op",
     "min_offload_ratio", "plan_offload", "op_turning_points", "host_workgroups",
     "place_matrix", "place_kv", "KV_UNIT_REQUEST", "KV_UNIT_HEAD", "splitk_gemm", "decode_attn_workspace_bytes",
+    "SplitMatrixFP8", "place_matrix_fp8", "splitk_gemm_fp8",
     "splitk_decode_attn", "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
     "probe_read", "probe_read_concurrent", "library",
 ]
@@ -248,6 +249,72 @@ def splitk_gemm(A: SplitMatrix, x: torch.Tensor, y: Optional[torch.Tensor] = Non
     d = A.desc()
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_splitk_gemm(C.byref(d), x.data_ptr(), N, y.data_ptr(), cp, _stream_handle(stream)))
+    return y
+
+
+@dataclass
+class SplitMatrixFP8:
+    """A [M, K] matrix of FP8 (OCP E4M3) weight codes with one fp32 scale per
+    row; tile-rows [0, h) of m rows in pinned host memory, the rest in HBM."""
+    host: Optional[torch.Tensor]   # [h*m, K] uint8, pinned CPU
+    hbm: Optional[torch.Tensor]    # [M - h*m, K] uint8, CUDA
+    row_scale: torch.Tensor        # [M] fp32, CUDA
+    M: int
+    K: int
+    m: int
+    h: int
+
+    def desc(self) -> L.SplitMatrixFP8Desc:
+        hp = self.host.data_ptr() if self.host is not None and self.host.numel() else None
+        gp = self.hbm.data_ptr() if self.hbm is not None and self.hbm.numel() else None
+        return L.SplitMatrixFP8Desc(hp, gp, self.M, self.K, self.m, 0, self.h, self.row_scale.data_ptr())
+
+    @property
+    def host_bytes(self) -> int:
+        return self.h * self.m * self.K
+
+
+def place_matrix_fp8(codes: torch.Tensor, row_scale: torch.Tensor, m: int, h: int, device=None) -> SplitMatrixFP8:
+    """Copy tile-rows [0, h) of the e4m3 codes [M, K] (uint8, or a
+    float8_e4m3fn tensor) into pinned host memory and the rest into HBM; the
+    per-row scales [M] go to HBM as fp32."""
+    if codes.dtype == torch.float8_e4m3fn:
+        codes = codes.view(torch.uint8)
+    if codes.dtype != torch.uint8 or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D uint8 (or float8_e4m3fn) tensor")
+    M, K = codes.shape
+    if M % m or not (0 <= h <= M // m):
+        raise ValueError("M must be a multiple of m and 0 <= h <= M/m")
+    if row_scale.numel() != M:
+        raise ValueError("one scale per row")
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    rows = h * m
+    host = None
+    if rows:
+        host = torch.empty((rows, K), dtype=torch.uint8, pin_memory=True)
+        host.copy_(codes[:rows])
+    hbm = None
+    if rows < M:
+        hbm = codes[rows:].to(device, copy=True).contiguous()
+    scale = row_scale.detach().to(device=device, dtype=torch.float32).contiguous()
+    return SplitMatrixFP8(host, hbm, scale, M, K, m, h)
+
+
+def splitk_gemm_fp8(A: SplitMatrixFP8, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                    cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
+    """y[n, r] = row_scale[r] * sum_k e4m3(A[r, k]) x[n, k]; x bf16 [N, K] on
+    the GPU (N <= 64), y fp32 [N, M]."""
+    lib = library()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
+    N = x.shape[0]
+    if y is None:
+        y = torch.empty((N, A.M), dtype=torch.float32, device=x.device)
+    if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (N, A.M):
+        raise ValueError("y must be a contiguous fp32 [N, M] tensor")
+    d = A.desc()
+    c, cp = _cfg_ptr(cfg)
+    _check(lib.dak_splitk_gemm_fp8(C.byref(d), x.data_ptr(), N, y.data_ptr(), cp, _stream_handle(stream)))
     return y
 
 

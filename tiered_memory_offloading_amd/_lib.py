@@ -30,6 +30,11 @@ class SplitMatrixDesc(C.Structure):
                 ("m", C.c_int32), ("reserved", C.c_int32), ("h", C.c_int64)]
 
 
+class SplitMatrixFP8Desc(C.Structure):
+    _fields_ = [("host", C.c_void_p), ("hbm", C.c_void_p), ("M", C.c_int64), ("K", C.c_int64),
+                ("m", C.c_int32), ("reserved", C.c_int32), ("h", C.c_int64), ("row_scale", C.c_void_p)]
+
+
 class SplitKVDesc(C.Structure):
     _fields_ = [("k_host", C.c_void_p), ("v_host", C.c_void_p), ("k_hbm", C.c_void_p), ("v_hbm", C.c_void_p),
                 ("batch", C.c_int64), ("h", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
@@ -57,6 +62,8 @@ SIGNATURES = [
     ("dak_host_workgroups", C.c_int64, [C.c_int64, C.c_int32]),
     ("dak_splitk_gemm", C.c_int32, [C.POINTER(SplitMatrixDesc), C.c_void_p, C.c_int64, C.c_void_p,
                                     C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_splitk_gemm_fp8", C.c_int32, [C.POINTER(SplitMatrixFP8Desc), C.c_void_p, C.c_int64, C.c_void_p,
+                                        C.POINTER(LaunchCfg), C.c_void_p]),
     ("dak_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(SplitKVDesc), C.c_int32]),
     ("dak_splitk_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(SplitKVDesc), C.c_int32, C.c_float, C.c_void_p,
                                            C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),

@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdak.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-HIP_SOURCES = ["runtime.hip", "splitk_gemm.hip", "splitk_gemm_staged.hip", "splitk_gemm_tiled.hip", "split_attn.hip", "probe.hip"]
+HIP_SOURCES = ["runtime.hip", "splitk_gemm.hip", "splitk_gemm_staged.hip", "splitk_gemm_tiled.hip", "splitk_gemm_fp8.hip",
+               "split_attn.hip", "probe.hip"]
 CXX_SOURCES = ["errors.cpp", "planner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,353 @@
+// Split GEMM over FP8 weights: y = s . (x . e4m3(A)^T) with A's first h
+// tile-rows of e4m3 codes in pinned host memory, the rest in HBM, one fp32
+// scale per row and bf16 activations (1 <= N <= 64).
+//
+// DAK paper §4.1 "DAK Design": disjoint work-groups compute disjoint output
+// rows and each reads one tier (Fig. 5b); §4.3.2: a host tile is fetched by one
+// consumer, so one work-group covers every output column of its rows.  FP8
+// weights (the pages' models run in FP8) halve the bytes per tile-row, which is
+// what the split is priced in.
+//
+// CDNA4 design (the LDS-DMA ring of the bf16 skinny kernel, re-laid for one
+// byte per weight):
+//   * work item: R = 16 RB rows x all K x all N; K in chunks of 256, i.e. 256
+//     contiguous bytes per weight row (the host link reaches its rate with
+//     pieces of 256 bytes and more) and 512 per activation row;
+//   * each chunk's A rows (four per 1 KiB DMA instruction) and x rows (two
+//     per instruction) land in one slot of an LDS ring through
+//     global_load_lds_dwordx4; STAGES - 1 chunks are in flight;
+//   * a wave reads its A fragment (8 codes of one row) from LDS, widens it to
+//     bf16 with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value,
+//     subnormals included, is a bf16 normal), and runs
+//     v_mfma_f32_16x16x32_bf16 against the x fragment; every product of an
+//     e4m3 and a bf16 value is exact in fp32;
+//   * K steps of 32 are split over the P = 4 / RB waves sharing a 16-row block
+//     by phase (t mod P), their sums added in phase order, then multiplied by
+//     the row's scale.
+// Host and HBM work-groups differ only in the base pointer, so the bits do not
+// depend on the split, the host work-group count or the window.
+//
+// LDS slot: A rows of 256 bytes (16 pieces of 16 bytes, piece p of row r at
+// position p ^ (r & 15)), then x rows of 512 bytes (32 pieces, piece p of x
+// row j at p ^ (j & 15)); the 16 lanes that read one fragment (16 rows, one
+// piece each) hit 16 different bank groups.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device_common.hpp"
+
+namespace dak {
+namespace {
+
+constexpr int kF8Waves = 4;
+constexpr int kF8Threads = 64 * kF8Waves;
+constexpr int kF8KC = 256;             // k per chunk
+constexpr int kF8ARow = kF8KC;         // bytes per staged A row
+constexpr int kF8XRow = kF8KC * 2;     // bytes per staged x row
+constexpr int kF8Steps = kF8KC / 32;   // MFMA steps per chunk
+constexpr int64_t kF8MaxN = 64;
+
+template <int NB, int RB>
+struct F8Shape {
+  static constexpr int R = 16 * RB;                  // A rows per item
+  static constexpr int A_BYTES = R * kF8ARow;
+  static constexpr int X_BYTES = 16 * NB * kF8XRow;
+  static constexpr int SLOT = A_BYTES + X_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024;     // 4 A rows per instruction
+  static constexpr int INSTR = SLOT / 1024;
+  static constexpr int PER_WAVE = INSTR / kF8Waves;
+  static constexpr int P = kF8Waves / RB;            // k-phases
+  static_assert(INSTR % kF8Waves == 0, "every wave issues the same number of DMA instructions");
+  static_assert(PER_WAVE * 2 <= 63, "vmcnt range");
+};
+
+// Ring depth: three slots when they fit in half of the CU's LDS, else two.
+constexpr int f8_stages(int nb, int rb) { return 3 * (16 * rb * kF8ARow + 16 * nb * kF8XRow) <= (80 << 10) ? 3 : 2; }
+
+// Eight e4m3 codes (k ascending from the low byte) widened to eight bf16.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
+template <int NB, int RB, bool COUNT>
+struct F8Item {
+  using S = F8Shape<NB, RB>;
+
+  // DMA chunk c of the item whose first A row is `a` into `slot`.  Pieces past
+  // K and activation rows past N are fetched from an in-bounds address and
+  // masked (K) or never used (N).
+  static __device__ __forceinline__ void issue(unsigned char* slot, int64_t c, const unsigned char* __restrict__ a,
+                                               const uint16_t* __restrict__ x, int64_t N, int64_t K, int wave,
+                                               int lane, uint64_t& nbytes) {
+#pragma unroll
+    for (int j = 0; j < S::PER_WAVE; ++j) {
+      const int ins = wave * S::PER_WAVE + j;
+      const void* src;
+      if (ins < S::A_INSTR) {   // uniform
+        const int r = 4 * ins + (lane >> 4);
+        const int piece = (lane & 15) ^ (r & 15);
+        const int64_t k = c * kF8KC + piece * 16;
+        src = a + (int64_t)r * K + (k < K ? k : 0);
+        if (COUNT && k < K) nbytes += 16;
+      } else {
+        const int xr = 2 * (ins - S::A_INSTR) + (lane >> 5);
+        const int piece = (lane & 31) ^ (xr & 15);
+        const int64_t k = c * kF8KC + piece * 8;
+        src = x + (xr < N ? xr : 0) * K + (k < K ? k : 0);
+      }
+      dma16(src, slot + ins * 1024);
+    }
+  }
+
+  // The steps of chunk c that belong to this wave's phase.
+  static __device__ __forceinline__ void compute(const unsigned char* slot, int64_t c, int64_t K, int rb, int phase,
+                                                 int lane, f32x4_t (&acc)[NB]) {
+    const int i16 = lane & 15, g = lane >> 4;
+    const int ra = 16 * rb + i16;
+#pragma unroll
+    for (int t = 0; t < kF8Steps; ++t) {
+      if (t % S::P != phase) continue;   // uniform
+      // K is a multiple of 16, so a lane's 8 k values are all in or all out.
+      const bool kok = c * kF8KC + 32 * t + 8 * g < K;
+      const int pa = 2 * t + (g >> 1);
+      uint2 a8 = *reinterpret_cast<const uint2*>(slot + ra * kF8ARow + ((pa ^ (ra & 15)) << 4) + 8 * (g & 1));
+      if (!kok) a8 = make_uint2(0, 0);
+      const uint4 af = e4m3x8_to_bf16(a8);
+      const int px = 4 * t + g;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int xr = 16 * cb + i16;
+        uint4 xf = *reinterpret_cast<const uint4*>(slot + S::A_BYTES + xr * kF8XRow + ((px ^ (xr & 15)) << 4));
+        if (!kok) xf = make_uint4(0, 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc[cb], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int NB, int RB, int STAGES, bool COUNT>
+__global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
+    const unsigned char* __restrict__ a_host, const unsigned char* __restrict__ a_hbm, int64_t M, int64_t K,
+    int64_t host_rows, const float* __restrict__ row_scale, const uint16_t* __restrict__ x, int64_t N,
+    float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
+  using S = F8Shape<NB, RB>;
+  using I = F8Item<NB, RB, COUNT>;
+  __shared__ __attribute__((aligned(16))) unsigned char s0[S::SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char s1[S::SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char s2[STAGES > 2 ? S::SLOT : 16];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rb = wave % RB, phase = wave / RB;
+  const int64_t nch = (K + kF8KC - 1) / kF8KC;
+  uint64_t nbytes = 0;
+  const bool host_role = (int)blockIdx.x < host_wgs;
+  int64_t it = host_role ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - host_wgs;
+  const int64_t items = host_role ? host_items : hbm_items;
+  const int64_t stride = host_role ? host_wgs : items;   // HBM work-groups take one item
+  for (; it < items; it += stride) {
+    const int64_t lrow = it * S::R;
+    const unsigned char* a = (host_role ? a_host : a_hbm) + lrow * K;
+    const int64_t yrow = host_role ? lrow : host_rows + lrow;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    I::issue(s0, 0, a, x, N, K, wave, lane, nbytes);
+    if (STAGES > 2 && nch > 1) I::issue(s1, 1, a, x, N, K, wave, lane, nbytes);
+    // Step for chunk c = c0 + IDX: wait for its DMA (all waves, via the
+    // barrier, which also retires every read of the slot about to be refilled),
+    // refill that slot with chunk c + STAGES - 1, then consume chunk c.
+#define DAK_F8_STEP(IDX, RD, WR)                                                                 \
+  {                                                                                              \
+    const int64_t c = c0 + IDX;                                                                  \
+    if (c < nch) {                                                                               \
+      const int64_t later = std::min<int64_t>(nch - 1 - c, STAGES - 2);                          \
+      if (later >= 2) vm_wait<2 * S::PER_WAVE>();                                                \
+      else if (later == 1) vm_wait<S::PER_WAVE>();                                               \
+      else vm_wait<0>();                                                                         \
+      __builtin_amdgcn_s_barrier();                                                              \
+      if (c + STAGES - 1 < nch) I::issue(WR, c + STAGES - 1, a, x, N, K, wave, lane, nbytes);    \
+      I::compute(RD, c, K, rb, phase, lane, acc);                                                \
+    }                                                                                            \
+  }
+    for (int64_t c0 = 0; c0 < nch; c0 += STAGES) {
+      if constexpr (STAGES == 2) {
+        DAK_F8_STEP(0, s0, s1)
+        DAK_F8_STEP(1, s1, s0)
+      } else {
+        DAK_F8_STEP(0, s0, s2)
+        DAK_F8_STEP(1, s1, s0)
+        DAK_F8_STEP(2, s2, s1)
+      }
+    }
+#undef DAK_F8_STEP
+    const int i16 = lane & 15, g = lane >> 4;
+    // Rows 4 g .. 4 g + 3 of the lane's 16-row block: their scales.
+    const int64_t srow = yrow + 16 * rb + 4 * g;
+    const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(row_scale + srow);
+    if constexpr (S::P == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t n = 16 * cb + i16;
+        const f32x4_t t = acc[cb];
+        if (n < N) *reinterpret_cast<f32x4_t*>(y + n * M + srow) = f32x4_t{t[0] * sc[0], t[1] * sc[1], t[2] * sc[2], t[3] * sc[3]};
+      }
+    } else {
+      // Phase partials through slot 0 (every DMA has landed and every read of
+      // the ring has retired once all waves pass the barrier).
+      __syncthreads();
+      f32x4_t* part = reinterpret_cast<f32x4_t*>(s0);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) part[(wave * NB + cb) * 64 + lane] = acc[cb];
+      __syncthreads();
+      if (phase == 0) {
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          f32x4_t t = acc[cb];
+#pragma unroll
+          for (int p = 1; p < S::P; ++p) {
+            const f32x4_t q = part[((p * RB + rb) * NB + cb) * 64 + lane];
+            t[0] += q[0];
+            t[1] += q[1];
+            t[2] += q[2];
+            t[3] += q[3];
+          }
+          const int64_t n = 16 * cb + i16;
+          if (n < N) *reinterpret_cast<f32x4_t*>(y + n * M + srow) = f32x4_t{t[0] * sc[0], t[1] * sc[1], t[2] * sc[2], t[3] * sc[3]};
+        }
+      }
+    }
+    __syncthreads();   // the ring is reused by the next item
+  }
+  if (COUNT) {
+    uint64_t v = nbytes;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&counters[host_role ? 0 : 1], (unsigned long long)v);
+  }
+}
+
+struct F8Args {
+  const unsigned char *a_host, *a_hbm;
+  int64_t M, K, host_rows;
+  const float* row_scale;
+  const uint16_t* x;
+  int64_t N;
+  float* y;
+  int host_wgs;
+  int64_t host_items, hbm_items;
+  unsigned long long* counters;
+  hipStream_t stream;
+};
+
+template <int NB, int RB, bool COUNT>
+void launch_f8_nb_rb(const F8Args& g) {
+  constexpr int ST = f8_stages(NB, RB);
+  static_assert(ST * F8Shape<NB, RB>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
+  const int64_t grid = g.host_wgs + g.hbm_items;
+  hipLaunchKernelGGL((gemm_fp8_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.row_scale, g.x, g.N, g.y, g.host_wgs, g.host_items,
+                     g.hbm_items, g.counters);
+}
+
+template <int NB, bool COUNT>
+void launch_f8_nb(const F8Args& g, int rb) {
+  switch (rb) {
+    case 4: return launch_f8_nb_rb<NB, 4, COUNT>(g);
+    case 2: return launch_f8_nb_rb<NB, 2, COUNT>(g);
+    default: return launch_f8_nb_rb<NB, 1, COUNT>(g);
+  }
+}
+
+int f8_nb_of(int64_t N) { return N <= 16 ? 1 : N <= 32 ? 2 : 4; }
+
+template <bool COUNT>
+void launch_f8(const F8Args& g, int rb) {
+  switch (f8_nb_of(g.N)) {
+    case 1: return launch_f8_nb<1, COUNT>(g, rb);
+    case 2: return launch_f8_nb<2, COUNT>(g, rb);
+    default: return launch_f8_nb<4, COUNT>(g, rb);
+  }
+}
+
+// Rows per item: taller items share each staged activation chunk over more
+// weight rows, as long as at least 384 items remain to spread over the CUs.
+int f8_row_blocks(int64_t M, int64_t m) {
+  for (int r = 4; r >= 2; r >>= 1)
+    if (m % (16 * r) == 0 && M / (16 * r) >= 384) return r;
+  return 1;
+}
+
+// Host work-groups: enough that their chunks in flight cover the link's
+// bandwidth-delay product.
+int f8_host_cus(int64_t N, int rb) {
+  const uint64_t inflight = (uint64_t)(f8_stages(f8_nb_of(N), rb) - 1) * 16 * rb * kF8ARow;
+  const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
+  return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
+}
+
+}  // namespace
+}  // namespace dak
+
+extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
+                                          const dak_launch_cfg* cfg, void* stream) {
+  using namespace dak;
+  clear_error();
+  if (!A) return fail(DAK_EINVAL, "A is NULL");
+  const int64_t M = A->M, K = A->K, m = A->m, h = A->h;
+  if (M < 1 || K < 16 || (K & 15))
+    return fail(DAK_EINVAL, "need M >= 1 and K >= 16 with K %% 16 == 0 (M=%lld K=%lld)", (long long)M, (long long)K);
+  if (m < 16 || (m & 15)) return fail(DAK_EINVAL, "tile-row height m=%lld must be a positive multiple of 16", (long long)m);
+  if (M % m) return fail(DAK_EINVAL, "M=%lld is not a multiple of m=%lld", (long long)M, (long long)m);
+  const int64_t n_units = M / m;
+  if (h < 0 || h > n_units) return fail(DAK_EINVAL, "h=%lld outside [0, %lld]", (long long)h, (long long)n_units);
+  if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
+  if (N > kF8MaxN) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld for FP8 weights", (long long)N, (long long)kF8MaxN);
+  if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
+  const int rb = f8_row_blocks(M, m);
+  LaunchCfg lc;
+  dak_status st = resolve_cfg(cfg, HostDefaults{f8_host_cus(N, rb)}, &lc);
+  if (st) return st;
+
+  const int64_t host_rows = h * m;
+  const void *dh = nullptr, *dg = nullptr, *ds = nullptr, *dx = nullptr, *dy = nullptr;
+  if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K, Tier::kHost, "A.host", &dh))) return st;
+  if (host_rows < M && (st = check_tier_ptr(A->hbm, (uint64_t)(M - host_rows) * K, Tier::kDevice, "A.hbm", &dg)))
+    return st;
+  if ((st = check_tier_ptr(A->row_scale, (uint64_t)M * 4, Tier::kDevice, "A.row_scale", &ds))) return st;
+  if ((st = check_tier_ptr(x, (uint64_t)N * K * 2, Tier::kDevice, "x", &dx))) return st;
+  if ((st = check_tier_ptr(y, (uint64_t)N * M * 4, Tier::kDevice, "y", &dy))) return st;
+
+  F8Args g;
+  g.a_host = static_cast<const unsigned char*>(dh);
+  g.a_hbm = static_cast<const unsigned char*>(dg);
+  g.M = M;
+  g.K = K;
+  g.host_rows = host_rows;
+  g.row_scale = static_cast<const float*>(ds);
+  g.x = static_cast<const uint16_t*>(dx);
+  g.N = N;
+  g.y = y;
+  const int64_t item_rows = 16 * rb;
+  g.host_items = host_rows / item_rows;
+  g.hbm_items = (M - host_rows) / item_rows;
+  g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
+  g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+  g.stream = static_cast<hipStream_t>(stream);
+  if (g.host_wgs + g.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
+  if (g.host_wgs + g.hbm_items == 0) return DAK_OK;
+  if (lc.flags & DAK_FLAG_COUNT_BYTES)
+    launch_f8<true>(g, rb);
+  else
+    launch_f8<false>(g, rb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "fp8 gemm kernel launch");
+  return DAK_OK;
+}

@@ -528,6 +528,99 @@ def run_linears(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_fp8_linears(torch, dak, args, b_hbm, b_host):
+    """The Llama-8B decode linears (QKV 6144x4096, O 4096x4096, gate+up
+    28672x4096, down 4096x14336) with FP8 weights (e4m3 codes, one fp32 scale
+    per row, from N(0, 0.02) weights) at N in {1, 16, 64} and x = k/20 for
+    k in {0, 1, 2, 5, 10}, cold (at least 1 GiB of copies of the HBM part in
+    rotation), beside the bf16 kernel at x = 0 and 1/4 on the same shapes.
+    Each point is the mean over `--sweep-steps` rotations after one untimed
+    rotation; FP8 outputs at every x are checked bit-identical to x = 0."""
+    reps = max(1, args.sweep_steps)
+
+    def timed(fn, descs, x, y):
+        for S in descs:
+            fn(S, x, y=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for S in descs:
+                fn(S, x, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(descs))
+
+    points = []
+    for oi, (name, M, K) in enumerate(synth.LLAMA8B_LINEARS):
+        n = M // M_TILE
+        C8 = M * K
+        copies = max(2, -(-(1 << 30) // C8))
+        codes, scale, _ = synth.fp8_gemm_inputs(M, K, 1, seed=oi, device="cuda")
+        Cs = [codes] + [codes.clone() for _ in range(copies - 1)]
+        scale = scale.contiguous()
+        hmax = host_units(1, 2, n)
+        C_host = torch.empty((hmax * M_TILE, K), dtype=torch.uint8, pin_memory=True)
+        C_host.copy_(codes[:hmax * M_TILE])
+        A16 = synth.gemm_inputs(M, K, 1, seed=oi, device="cuda")[0]
+        copies16 = max(2, -(-(1 << 30) // (2 * C8)))
+        A16s = [A16] + [A16.clone() for _ in range(copies16 - 1)]
+        A16_host = torch.empty((host_units(1, 4, n) * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+        A16_host.copy_(A16[:A16_host.shape[0]])
+        for N in (1, 16, 64):
+            X = synth.gemm_inputs(M, K, N, seed=oi, device="cuda")[1].contiguous()
+            y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+            bf16_ms = {}
+            for k in (0, 5):
+                h = host_units(k, 20, n)
+                d16 = [dak.SplitMatrix(A16_host[:h * M_TILE] if h else None, a[h * M_TILE:], M, K, M_TILE, h)
+                       for a in A16s]
+                bf16_ms[k] = timed(dak.splitk_gemm, d16, X, y)
+            ref = None
+            for k in (0, 1, 2, 5, 10):
+                h = host_units(k, 20, n)
+                descs = [dak.SplitMatrixFP8(C_host[:h * M_TILE] if h else None, c[h * M_TILE:] if h < n else None,
+                                            scale, M, K, M_TILE, h) for c in Cs]
+                t = timed(dak.splitk_gemm_fp8, descs, X, y)
+                if ref is None:
+                    ref = y.clone()
+                same = bool(torch.equal(y, ref))
+                t_roof = max((n - h) * (C8 // n) / (b_hbm * 1e9), h * (C8 // n) / (b_host * 1e9)) * 1e3
+                pt = {"op": name, "M": M, "K": K, "N": N, "x": round(h / n, 4), "h": h, "ms": round(t, 5),
+                      "GBps": round(C8 / (t * 1e-3) / 1e9, 1), "frac_two_tier": round(t_roof / t, 4),
+                      "bit_identical_to_x0": same}
+                if k in bf16_ms:
+                    pt["bf16_ms"] = round(bf16_ms[k], 5)
+                    pt["speedup_over_bf16"] = round(bf16_ms[k] / t, 3)
+                points.append(pt)
+                log(f"fp8 {name} N={N} x={h / n:.3f}: {t * 1e3:.1f} us, {pt['GBps']:.0f} GB/s, "
+                    f"{pt['frac_two_tier']:.3f} of roofline"
+                    + (f", {pt['speedup_over_bf16']:.2f}x over bf16" if k in bf16_ms else "")
+                    + ("" if same else " BITS DIFFER"))
+            del X, y
+        del codes, Cs, C_host, A16, A16s, A16_host
+        torch.cuda.empty_cache()
+    pos = [p for p in points if p["x"] > 0]
+    res = {
+        "metric": "FP8-weight split GEMM: % of the two-tier roofline vs offload ratio x, and speedup over bf16",
+        "value": round(statistics.mean(p["frac_two_tier"] for p in pos), 4),
+        "unit": "mean fraction of the two-tier roofline over N in {1,16,64}, 4 ops, x = 0.05..0.5",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e4m3 weights, bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "Llama-8B decode linears QKV 6144x4096, O 4096x4096, gate+up 28672x4096, "
+                               "down 4096x14336 with FP8 weights at N in {1,16,64}, x in {0, .05, .1, .25, .5}, "
+                               "64-row tile-rows, cold"},
+        "frac_b_hbm_at_x0": {f"{p['op']}_N{p['N']}": p["frac_two_tier"] for p in points if p["h"] == 0},
+        "speedup_over_bf16": {f"{p['op']}_N{p['N']}_x{p['x']}": p["speedup_over_bf16"]
+                              for p in points if "speedup_over_bf16" in p},
+        "all_bit_identical_across_x": all(p["bit_identical_to_x0"] for p in points),
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "points": points,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def run_paged(torch, dak, args, b_hbm, b_host):
     """Paged against dense split decode attention at the Llama-8B decode size
     (batch 16, 32 query / 8 KV heads, head_dim 128, 32768 cached tokens; K, V
@@ -690,13 +783,14 @@ def main(argv=None):
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
     ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare",
-                                           "paged"),
+                                           "paged", "fp8-linears"),
                     default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
                          "at N in {1,16,64} over x = 0..0.5, cold; plan-compare: greedy per-op ratios against a "
                          "uniform ratio for one decoder layer at large batch; paged: paged against dense "
-                         "split attention (each prints its own JSON line)")
+                         "split attention; fp8-linears: the decode linears with FP8 weights (each prints its "
+                         "own JSON line)")
     ap.add_argument("--plan-batch", type=int, default=512, help="plan-compare: batch (activation rows N)")
     ap.add_argument("--plan-ctx", type=int, default=2048, help="plan-compare: tokens per request")
     ap.add_argument("--plan-x", type=float, nargs="+", default=[0.01, 0.02, 0.05],
@@ -735,6 +829,8 @@ def main(argv=None):
         return run_plan_compare(torch, dak, args, b_hbm, b_host)
     if args.workload == "paged":
         return run_paged(torch, dak, args, b_hbm, b_host)
+    if args.workload == "fp8-linears":
+        return run_fp8_linears(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

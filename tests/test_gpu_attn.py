@@ -220,3 +220,16 @@ def test_ragged_lengths_clamped():
     out = run_kv(q, K, V, 1, 0.1, lens=torch.tensor([0, -5, 10**6], dtype=torch.int32))
     assert torch.isnan(out[:2]).all()
     assert torch.equal(out[2], full[2])
+
+
+def test_head_units_and_ragged_lengths_at_eight_grouped_heads():
+    B, Hq, Hkv, D, ctx = 3, 64, 8, 128, 2100
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=45)
+    lens = torch.tensor([2100, 5, 1500], dtype=torch.int32)
+    scale = 1.0 / np.sqrt(D)
+    ref = oa.decode_attention_lens(to_f64(q), to_f64(K), to_f64(V), scale, lens.tolist())
+    base = run_kv(q, K, V, 0, scale, lens=lens)
+    for b in range(B):
+        assert normwise_error(base[b].numpy(), ref[b]) <= TOL
+    for h in (1, 7, 8, 13, 24):
+        assert torch.equal(run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_HEAD, lens=lens), base), h

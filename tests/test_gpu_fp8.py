@@ -108,3 +108,17 @@ def test_fp8_arguments_checked():
     S2 = dak.place_matrix_fp8(codes2, scale2, 64, 0)
     with pytest.raises(dak.DakError):
         dak.splitk_gemm_fp8(S2, x2.cuda())
+
+
+@pytest.mark.parametrize("M, K, m, N", [(16, 16, 16, 1), (16, 16, 16, 64), (48, 32, 16, 7), (96, 4112, 32, 40)])
+def test_small_and_ragged_shapes(M, K, m, N):
+    # One 16-row item, a single half step of K, odd row counts per tile-row,
+    # and K = 4096 + 16 (a chunk with one 16-wide piece).
+    codes = synth.fp8_all_codes(M, K, seed=M + K)
+    scale = torch.linspace(0.01, 0.02, M)
+    x = synth.gemm_inputs(16, K, N, seed=N)[1]
+    ref = of.gemm_fp8(codes, scale, x)
+    base = run(codes, scale, x, m, 0)
+    assert normwise_error(base.numpy(), ref) <= TOL
+    for h in range(1, M // m + 1):
+        assert torch.equal(run(codes, scale, x, m, h), base), h

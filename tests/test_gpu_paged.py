@@ -143,3 +143,20 @@ def test_paged_arguments_checked():
     kv = dak.place_paged_kv(K, V, lens, 16)
     with pytest.raises(dak.DakError):
         dak.paged_decode_attn(q.cuda()[:, :3].contiguous(), kv, 0.1)   # 3 query heads over 2 KV heads
+
+
+def test_eight_grouped_heads_and_largest_page():
+    # The 70B grouping (64 query / 8 KV heads) and a page of 2^20 tokens
+    # (every unit has one page, the chunk lies inside it).
+    B, Hq, Hkv, D, ctx = 2, 64, 8, 128, 2200
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=56)
+    lens = torch.tensor([2200, 700], dtype=torch.int32)
+    scale = 1.0 / np.sqrt(D)
+    ref = oa.decode_attention_lens(to_f64(q), to_f64(K), to_f64(V), scale, lens.tolist())
+    base = dense(q, K, V, lens, scale)
+    for b in range(B):
+        assert normwise_error(base[b].numpy(), ref[b]) <= TOL
+    for page, hu in ((16, [3, 9, 12]), (1 << 20, [0, 15])):
+        assert torch.equal(paged(q, K, V, lens, scale, page, hu, seed=page % 97), base), page
+    kv = dak.place_paged_kv(K, V, lens, 1 << 20)
+    assert kv.max_pages == 1

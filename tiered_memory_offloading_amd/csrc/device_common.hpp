@@ -37,6 +37,20 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// row16_sum of n independent values, one row-sum step at a time across all of
+// them (the same four steps per value as row16_sum).
+template <int n>
+__device__ __forceinline__ void row16_sum_all(float* v) {
+#pragma unroll
+  for (int j = 0; j < n; ++j) v[j] = dpp_add<0xB1>(v[j]);
+#pragma unroll
+  for (int j = 0; j < n; ++j) v[j] = dpp_add<0x4E>(v[j]);
+#pragma unroll
+  for (int j = 0; j < n; ++j) v[j] = dpp_add<0x141>(v[j]);
+#pragma unroll
+  for (int j = 0; j < n; ++j) v[j] = dpp_add<0x140>(v[j]);
+}
+
 // Dot product of two bf16 pairs accumulated into fp32 (v_dot2c_f32_bf16).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

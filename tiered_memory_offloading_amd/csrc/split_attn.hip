@@ -110,19 +110,30 @@ template <int G>
 __device__ __forceinline__ void attn_tile(const uint4 (&kv)[4], const uint4 (&vv)[4], int64_t ts, int64_t te, int grp,
                                           const uint32_t (&qb)[G][4], float qscale, float (&m)[G], float (&l)[G],
                                           float (&o)[G][8]) {
+  // Scores, stage by stage over all 4 G independent values (each value sees
+  // the same operations in the same order as a chain-by-chain walk): the
+  // dot products, then each of the four row-sum steps, so the DPP steps of
+  // different values interleave instead of waiting on each other.
   float s[4][G];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[i][h] = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t kw = q == 0 ? kv[i].x : q == 1 ? kv[i].y : q == 2 ? kv[i].z : kv[i].w;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = dot2_bf16(kw, qb[h][q], s[i][h]);
+    }
+  }
+  row16_sum_all<4 * G>(&s[0][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = ts + 4 * i + grp;
-    const uint32_t kw[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) p = dot2_bf16(kw[q], qb[h][q], p);
-      p = row16_sum(p) * qscale;
-      s[i][h] = (t < te) ? p : kNegInf;
-    }
+    for (int h = 0; h < G; ++h) s[i][h] = (t < te) ? s[i][h] * qscale : kNegInf;
   }
   float vf[4][8];
 #pragma unroll

@@ -676,6 +676,28 @@ def run_paged(torch, dak, args, b_hbm, b_host):
             points[-1]["bit_identical_to_dense"] = points[-2]["bit_identical_to_dense"] = same
             del kvd, kvp, wsd, wsp
             torch.cuda.empty_cache()
+    del q, K, V
+    torch.cuda.empty_cache()
+    # Granularity at a small batch: 4 requests, a host-share target of 1/10.
+    # Whole requests step in quarters (h = ceil(0.1 * 4) = 1 request, 25 % of
+    # the cache on the host); (request, KV head) units step in 1/32 (h = 4,
+    # 12.5 %).  Time against the all-HBM time and the two-tier roofline.
+    Bs = 4
+    q4, K4, V4 = synth.attn_inputs(Bs, Hq, Hkv, D, ctx, seed=8, device="cuda")
+    total4 = Bs * Hkv * ctx * D * 2 * 2
+    gran = []
+    for label, unit, h in (("all HBM", dak.KV_UNIT_REQUEST, 0), ("request units", dak.KV_UNIT_REQUEST, 1),
+                           ("head units", dak.KV_UNIT_HEAD, 4)):
+        kv4 = dak.place_kv(K4, V4, h, unit=unit)
+        o4 = torch.empty((Bs, Hq, D), dtype=torch.float32, device="cuda")
+        ws4 = torch.empty(dak.decode_attn_workspace_bytes(kv4, Hq), dtype=torch.uint8, device="cuda")
+        t = timed(lambda: dak.splitk_decode_attn(q4, kv4, scale, out=o4, ws=ws4))
+        hb = kv4.host_bytes
+        t_roof = max((total4 - hb) / (b_hbm * 1e9), hb / (b_host * 1e9)) * 1e3
+        gran.append({"placement": label, "host_units": h, "host_share": round(hb / total4, 4), "ms": round(t, 4),
+                     "frac_two_tier": round(t_roof / t, 4)})
+        log(f"batch 4, target x = 0.1: {label}: host share {hb / total4:.3f}, {t:.3f} ms")
+        del kv4, ws4
     paged_pts = [p for p in points if p["kind"] == "paged"]
     ratios = [p["ms"] / d["ms"] for p, d in zip(points[1::2], points[0::2])]
     res = {
@@ -690,6 +712,7 @@ def run_paged(torch, dak, args, b_hbm, b_host):
         "paged_over_dense_time": {"mean": round(statistics.mean(ratios), 4), "max": round(max(ratios), 4)},
         "all_bit_identical_to_dense": all(p["bit_identical_to_dense"] for p in points),
         "ragged_lengths": mixes["ragged"],
+        "granularity_batch4_target_x0.1": gran,
         "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "points": points,
     }
     print(json.dumps(res), flush=True)

@@ -6,8 +6,9 @@ Three measurements, all through the C ABI:
   * congestion (Fig. 7 analogue): HBM-role and host-role durations of one
     concurrent streaming launch while the number of host work-groups and their
     window vary, against the HBM role alone;
-  * per-operator host throughput: split GEMM (N in {1, 16, 64}) and split decode
-    attention with all units on the host, over host work-groups x window;
+  * per-operator host throughput: split GEMM (N in {1, 16, 64}; bf16 and FP8
+    weights) and split decode attention with all units on the host, over host
+    work-groups x window;
   * the chosen (host_cus, window) per operator class, written as JSON.
 
 Run:  python -m tiered_memory_offloading_amd.tune --out tuning.json
@@ -28,7 +29,7 @@ import time
 import torch
 
 from . import LaunchConfig, place_kv, probe_read, probe_read_concurrent, splitk_decode_attn, splitk_gemm
-from . import SplitMatrix, SplitKV, library
+from . import SplitMatrix, SplitMatrixFP8, SplitKV, library, splitk_gemm_fp8
 
 HOST_CUS = (4, 8, 12, 16, 24, 32, 48, 64)
 WINDOWS = (1, 2, 4, 8)
@@ -91,6 +92,26 @@ def gemm_host_sweep(N, M=8192, K=4096, reps=3, log=print):
     return res
 
 
+def gemm_fp8_host_sweep(N, M=8192, K=8192, reps=3, log=print):
+    """FP8 weights, all tile-rows on the host: host GB/s per host_cus (the
+    FP8 kernel's ring has a fixed depth, so the window does not apply)."""
+    codes = torch.randint(0, 0x7E, (M, K), dtype=torch.uint8, device="cuda")
+    C_host = torch.empty((M, K), dtype=torch.uint8, pin_memory=True)
+    C_host.copy_(codes)
+    scale = torch.full((M,), 1e-3, dtype=torch.float32, device="cuda")
+    S = SplitMatrixFP8(C_host, None, scale, M, K, 64, M // 64)
+    x = torch.randn((N, K), device="cuda").to(torch.bfloat16)
+    y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    res = []
+    for hc in HOST_CUS:
+        cfg = LaunchConfig(host_cus=hc)
+        ms = _time(lambda: splitk_gemm_fp8(S, x, y=y, cfg=cfg), reps)
+        res.append({"host_cus": hc, "window": 0, "ms": ms, "host_GBps": M * K / ms / 1e6})
+    log(f"gemm fp8 N={N}: " + ", ".join(f"{r['host_cus']}={r['host_GBps']:.1f}" for r in res))
+    del codes, C_host
+    return res
+
+
 def attn_host_sweep(B=2, ctx=32768, reps=3, log=print):
     """All requests on the host: host GB/s per (host_cus, window)."""
     Hq, Hkv, D = 32, 8, 128
@@ -135,6 +156,10 @@ def main(argv=None):
     for N in (1, 16, 64):
         res = gemm_host_sweep(N, log=log)
         table["gemm"][str(N)] = {"best": _best(res), "sweep": res}
+    table["gemm_fp8"] = {}
+    for N in (1, 16, 64):
+        res = gemm_fp8_host_sweep(N, log=log)
+        table["gemm_fp8"][str(N)] = {"best": _best(res), "sweep": res}
     res = attn_host_sweep(log=log)
     table["attn"] = {"best": _best(res), "sweep": res}
     table["wall_s"] = time.time() - t0
@@ -143,7 +168,8 @@ def main(argv=None):
         with open(args.out, "w") as f:
             f.write(s)
     print(json.dumps({k: (v["best"] if isinstance(v, dict) and "best" in v else None)
-                      for k, v in [("attn", table["attn"])] + [(f"gemm{n}", table["gemm"][n]) for n in table["gemm"]]}))
+                      for k, v in [("attn", table["attn"])] + [(f"gemm{n}", table["gemm"][n]) for n in table["gemm"]]
+                      + [(f"gemm_fp8_{n}", table["gemm_fp8"][n]) for n in table["gemm_fp8"]]}))
     return 0
 
 

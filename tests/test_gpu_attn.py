@@ -233,3 +233,12 @@ def test_head_units_and_ragged_lengths_at_eight_grouped_heads():
         assert normwise_error(base[b].numpy(), ref[b]) <= TOL
     for h in (1, 7, 8, 13, 24):
         assert torch.equal(run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_HEAD, lens=lens), base), h
+
+
+def test_output_layout_checked_by_the_binding():
+    q, K, V = synth.attn_inputs(2, 4, 1, 128, 64, seed=8)
+    kv = dak.place_kv(K, V, 1)
+    with pytest.raises(ValueError):
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1, out=torch.empty((2, 4, 128), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1, out=torch.empty((2, 128, 4), device="cuda").transpose(1, 2))

@@ -323,6 +323,16 @@ def decode_attn_workspace_bytes(kv: SplitKV, n_q_heads: int) -> int:
     return int(library().dak_decode_attn_workspace_bytes(C.byref(d), int(n_q_heads)))
 
 
+def _check_attn_buffers(q: torch.Tensor, out: torch.Tensor, ws: torch.Tensor) -> None:
+    # Layout only: the library checks that each buffer is device memory of
+    # the size it needs, but it sees a base pointer, not a view's strides.
+    B, Hq, D = q.shape
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be a contiguous fp32 tensor [B, Hq, D]")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+
+
 def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None, cfg: Optional[LaunchConfig] = None,
                        stream=None) -> torch.Tensor:
@@ -336,6 +346,7 @@ def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional
     need = decode_attn_workspace_bytes(kv, Hq)
     if ws is None:
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _check_attn_buffers(q, out, ws)
     d = kv.desc()
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_splitk_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
@@ -463,6 +474,7 @@ def paged_decode_attn(q: torch.Tensor, kv: PagedKV, scale: float, out: Optional[
     need = paged_decode_attn_workspace_bytes(kv, Hq)
     if ws is None:
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _check_attn_buffers(q, out, ws)
     d = kv.desc()
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_paged_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),

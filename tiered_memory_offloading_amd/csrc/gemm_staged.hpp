@@ -17,6 +17,7 @@ struct StagedArgs {
   float* y;
   int host_wgs;
   int64_t host_items, hbm_items;
+  int cus;   // compute units of the device (picks the ring depth at N > 32)
   unsigned long long* counters;
   hipStream_t stream;
 };
@@ -29,7 +30,8 @@ int staged_row_blocks(int64_t M, int64_t m, int64_t N);
 // Default host work-group cap: enough groups that their in-flight chunks
 // cover the host link's bandwidth-delay product.
 int staged_host_cus(int64_t N, int row_blocks);
-// Launch (the ring depth is fixed by the shape).
+// Launch.  The ring depth never changes the arithmetic (a step's k-phase is
+// its index within K), so it may depend on the split: see stages_for_launch.
 void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count);
 
 }  // namespace dak

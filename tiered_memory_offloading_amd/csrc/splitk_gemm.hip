@@ -523,6 +523,7 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     t.host_items = host_rows / item_rows;
     t.hbm_items = (M - host_rows) / item_rows;
     t.host_wgs = (int)host_workgroups(t.host_items, lc.host_cus);
+    if ((st = device_cus(&t.cus))) return st;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.stream = static_cast<hipStream_t>(stream);
     if (t.host_wgs + t.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");

@@ -243,18 +243,36 @@ struct F8Args {
   float* y;
   int host_wgs;
   int64_t host_items, hbm_items;
+  int cus;
   unsigned long long* counters;
   hipStream_t stream;
 };
 
-template <int NB, int RB, bool COUNT>
-void launch_f8_nb_rb(const F8Args& g) {
-  constexpr int ST = f8_stages(NB, RB);
+template <int NB, int RB, int ST, bool COUNT>
+void launch_f8_nb_rb_st(const F8Args& g) {
   static_assert(ST * F8Shape<NB, RB>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_fp8_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.row_scale, g.x, g.N, g.y, g.host_wgs, g.host_items,
                      g.hbm_items, g.counters);
+}
+
+// Three slots where two is the default (they need the whole CU), when there
+// is a host role, the grid still runs in one round of one work-group per CU,
+// and the host role's weight bytes in flight stay within the link's
+// bandwidth-delay product (measured at N = 64 on the 4096-row ops: 1/16 of
+// the rows on the host 0.56 -> 0.65 and 0.63 -> 0.74 of the two-tier
+// roofline; without host rows the deeper ring was 4 % slower, so it is kept
+// to launches with a host role).  The depth changes no arithmetic.
+template <int NB, int RB, bool COUNT>
+void launch_f8_nb_rb(const F8Args& g) {
+  constexpr int ST = f8_stages(NB, RB);
+  if constexpr (ST == 2 && 3 * F8Shape<NB, RB>::SLOT <= (160 << 10)) {
+    const uint64_t host_inflight = (uint64_t)g.host_wgs * 2 * 16 * RB * kF8ARow;
+    if (g.host_wgs > 0 && g.host_wgs + g.hbm_items <= g.cus && host_inflight <= kHostInflightBytes)
+      return launch_f8_nb_rb_st<NB, RB, 3, COUNT>(g);
+  }
+  launch_f8_nb_rb_st<NB, RB, ST, COUNT>(g);
 }
 
 template <int NB, bool COUNT>
@@ -339,6 +357,7 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
   g.host_items = host_rows / item_rows;
   g.hbm_items = (M - host_rows) / item_rows;
   g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
+  if ((st = device_cus(&g.cus))) return st;
   g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   g.stream = static_cast<hipStream_t>(stream);
   if (g.host_wgs + g.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");

@@ -212,16 +212,39 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
 }
 
 // Ring depth: three slots when they fit in half of the CU's LDS (two resident
-// work-groups per CU), else two.  A function of the shape only.
+// work-groups per CU), else two.
 constexpr int stages_for(int nb, int rb) { return 3 * (16 * rb + 16 * nb) * kRowB <= (80 << 10) ? 3 : 2; }
 
-template <int NB, int RB, bool COUNT>
-void launch_nb_rb(const StagedArgs& g) {
-  constexpr int ST = stages_for(NB, RB);
+// Three slots also where they need the whole CU (N > 32, items of 16 or 32
+// rows: 120 or 144 KiB), provided the grid then still runs in one round of one
+// work-group per CU, and the host role's weight bytes in flight (two chunks
+// per host work-group) stay within the link's bandwidth-delay product (the
+// congestion window of DAK §4.3.1).  Every work-group then keeps twice the
+// bytes in flight and no item waits for a second round (measured at N = 64:
+// 4096-row ops 5-9 % faster at x = 0 and 6-9 % at a 1/16 host share; 6144
+// rows, which would need a second round, lose 40 %).  The depth changes no
+// arithmetic.
+bool deep_ring(int nb, int rb, const StagedArgs& g) {
+  const uint64_t host_inflight = (uint64_t)g.host_wgs * 2 * 16 * rb * kRowB;
+  return stages_for(nb, rb) == 2 && 3 * (16 * rb + 16 * nb) * kRowB <= (160 << 10) &&
+         g.host_wgs + g.hbm_items <= g.cus && host_inflight <= kHostInflightBytes;
+}
+
+template <int NB, int RB, int ST, bool COUNT>
+void launch_nb_rb_st(const StagedArgs& g) {
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items, g.hbm_items,
                      g.counters);
+}
+
+template <int NB, int RB, bool COUNT>
+void launch_nb_rb(const StagedArgs& g) {
+  constexpr int ST = stages_for(NB, RB);
+  if constexpr (ST == 2 && 3 * (16 * RB + 16 * NB) * kRowB <= (160 << 10)) {
+    if (deep_ring(NB, RB, g)) return launch_nb_rb_st<NB, RB, 3, COUNT>(g);
+  }
+  launch_nb_rb_st<NB, RB, ST, COUNT>(g);
 }
 
 template <int NB, bool COUNT>

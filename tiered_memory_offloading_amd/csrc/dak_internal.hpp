@@ -50,6 +50,7 @@ inline int auto_window(int64_t host_wgs, uint64_t bytes_per_step_per_wg, int max
 // Resolved launch configuration.
 struct LaunchCfg {
   int host_cus;
+  bool host_cus_default;   // no cap given by the caller
   int window;
   int flags;
   uint64_t* byte_counters;
@@ -61,5 +62,17 @@ dak_status device_cus(int* cus);
 
 // Host work-group count under a cap (fewest waves, then fewest groups).
 int64_t host_workgroups(int64_t items, int32_t cap);
+
+// The skinny GEMMs' host work-groups.  Under the default cap, a host share
+// whose items, one work-group each, keep at most 1.25x the link's
+// bandwidth-delay product in flight (inflight_per_wg: the least a host
+// work-group has in flight) runs in one round instead of paying a second
+// pipeline fill; otherwise, and for a cap the caller gives, the capped count.
+// The count never changes the arithmetic.
+inline int64_t gemm_host_workgroups(int64_t items, const LaunchCfg& lc, uint64_t inflight_per_wg) {
+  if (lc.host_cus_default && items > lc.host_cus && (uint64_t)items * inflight_per_wg <= kHostInflightBytes / 4 * 5)
+    return items;
+  return host_workgroups(items, lc.host_cus);
+}
 
 }  // namespace dak

@@ -34,13 +34,17 @@ void clear_error() {
 
 dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* out) {
   out->host_cus = def.host_cus;
+  out->host_cus_default = true;
   out->window = 0;   // 0: sized by the operator from kHostInflightBytes
   out->flags = 0;
   out->byte_counters = nullptr;
   if (!cfg) return DAK_OK;
   if (cfg->host_cus < 0 || cfg->host_cus > 1024)
     return fail(DAK_EINVAL, "host_cus %d outside [0, 1024]", cfg->host_cus);
-  if (cfg->host_cus) out->host_cus = cfg->host_cus;
+  if (cfg->host_cus) {
+    out->host_cus = cfg->host_cus;
+    out->host_cus_default = false;
+  }
   if (cfg->window) {
     if (cfg->window != 1 && cfg->window != 2 && cfg->window != 4 && cfg->window != 8)
       return fail(DAK_EINVAL, "window %d is not 0, 1, 2, 4 or 8", cfg->window);

@@ -30,6 +30,8 @@ int staged_row_blocks(int64_t M, int64_t m, int64_t N);
 // Default host work-group cap: enough groups that their in-flight chunks
 // cover the host link's bandwidth-delay product.
 int staged_host_cus(int64_t N, int row_blocks);
+// Weight bytes one host work-group keeps in flight with the default ring.
+uint64_t staged_host_inflight(int64_t N, int row_blocks);
 // Launch.  The ring depth never changes the arithmetic (a step's k-phase is
 // its index within K), so it may depend on the split: see stages_for_launch.
 void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count);

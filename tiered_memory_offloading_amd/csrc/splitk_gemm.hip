@@ -522,7 +522,7 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     const int64_t item_rows = 16 * rbw;
     t.host_items = host_rows / item_rows;
     t.hbm_items = (M - host_rows) / item_rows;
-    t.host_wgs = (int)host_workgroups(t.host_items, lc.host_cus);
+    t.host_wgs = (int)gemm_host_workgroups(t.host_items, lc, staged_host_inflight(N, rbw));
     if ((st = device_cus(&t.cus))) return st;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.stream = static_cast<hipStream_t>(stream);
@@ -561,7 +561,9 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   g.y = y;
   g.host_items = host_rows / host_item_rows;
   g.hbm_items = (M - host_rows) / hbm_item_rows;
-  g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
+  // Least bytes a host work-group keeps in flight: one step of 4 waves x 4 rows
+  // x 1 KiB (FMA path, window 1) or one 256-k chunk of 16 rows (MFMA path).
+  g.host_wgs = (int)gemm_host_workgroups(g.host_items, lc, fma ? (16u << 10) : (8u << 10));
   g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   g.stream = static_cast<hipStream_t>(stream);
   if (g.host_wgs + g.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");

@@ -280,10 +280,14 @@ int staged_row_blocks(int64_t M, int64_t m, int64_t N) {
   return 1;
 }
 
+uint64_t staged_host_inflight(int64_t N, int row_blocks) {
+  return (uint64_t)(stages_for(nb_of(N), row_blocks) - 1) * 16 * row_blocks * kRowB;
+}
+
 int staged_host_cus(int64_t N, int row_blocks) {
   // Enough host work-groups that the chunks they have in flight cover the
   // link's bandwidth-delay product.
-  const uint64_t inflight = (uint64_t)(stages_for(nb_of(N), row_blocks) - 1) * 16 * row_blocks * kRowB;
+  const uint64_t inflight = staged_host_inflight(N, row_blocks);
   const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
   return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
 }

@@ -129,11 +129,18 @@ __device__ __forceinline__ void attn_tile(const uint4 (&kv)[4], const uint4 (&vv
     }
   }
   row16_sum_all<4 * G>(&s[0][0]);
+  if (ts + kTile <= te) {   // uniform: every token of the tile is valid
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = ts + 4 * i + grp;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[i][h] = (t < te) ? s[i][h] * qscale : kNegInf;
+      for (int h = 0; h < G; ++h) s[i][h] = s[i][h] * qscale;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = ts + 4 * i + grp;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = (t < te) ? s[i][h] * qscale : kNegInf;
+    }
   }
   float vf[4][8];
 #pragma unroll

@@ -289,15 +289,21 @@ def cpu_baseline(wl, reps=5):
 
 def run_llama70b(torch, dak, args, b_hbm, b_host):
     """70B-shaped decode step (80 layers, hidden 8192, GQA 64/8, hd 128, FFN
-    28672, batch 16 x 32768 tokens): the planner spreads the ~309 GB footprint
-    over HBM and pinned host memory; the step is timed against its model."""
+    28672, `--b70-batch` requests (16) x 32768 tokens): the planner spreads the
+    footprint (~309 GB at batch 16 with bf16 weights) over HBM and pinned host
+    memory; the step is timed against its model.  `--b70-weights fp8` stores
+    the weights as e4m3 codes with per-row scales; `--b70-kv-unit head` lets
+    the planner place single (request, KV head) KV blocks."""
     from tiered_memory_offloading_amd.model import LLAMA70B, DecodeModel
 
     free, total = torch.cuda.mem_get_info()
     reserve = int(args.hbm_reserve_gib * (1 << 30))
     H = free - reserve
     log(f"HBM free {free / 2**30:.2f} GiB of {total / 2**30:.2f} GiB; planning with H = {H / 2**30:.2f} GiB")
-    model = DecodeModel(LLAMA70B, 16, 32768, b_hbm * 1e9, b_host * 1e9, H, log=log)
+    B = args.b70_batch
+    kv_unit = dak.KV_UNIT_HEAD if args.b70_kv_unit == "head" else dak.KV_UNIT_REQUEST
+    model = DecodeModel(LLAMA70B, B, 32768, b_hbm * 1e9, b_host * 1e9, H, log=log, weights=args.b70_weights,
+                        kv_unit=kv_unit)
     for _ in range(args.warmup):
         model.step()
     torch.cuda.synchronize()
@@ -328,11 +334,12 @@ def run_llama70b(torch, dak, args, b_hbm, b_host):
         "metric": "effective GB/s (HBM+host) of a 70B-shaped decode step at the planned ratios",
         "value": round(model.footprint / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
-        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "dtype": ("e4m3 weights, " if args.b70_weights == "fp8" else "") + "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
         "config": {"workload": "Llama-70B-shaped decode step: 80 layers x {QKV 10240x8192, split-KV attention "
-                               "64q/8kv hd128, O 8192x8192, gate+up 57344x8192, down 8192x28672}, batch 16, "
-                               "32768 ctx/request", "footprint_bytes": model.footprint,
-                   "hbm_budget_bytes": H, "hbm_reserve_bytes": reserve},
+                               f"64q/8kv hd128, O 8192x8192, gate+up 57344x8192, down 8192x28672}}, batch {B}, "
+                               "32768 ctx/request", "weights": args.b70_weights, "kv_unit": args.b70_kv_unit,
+                   "footprint_bytes": model.footprint, "hbm_budget_bytes": H, "hbm_reserve_bytes": reserve},
         "x_global": round(model.x_global, 6), "host_bytes": model.host_bytes, "ops": n,
         "ops_with_host_units": ops_with_host, "modeled_ms": round(model.modeled_s * 1e3, 3),
         "frac_of_model": round(model.modeled_s * 1e3 / ms, 4),
@@ -818,6 +825,10 @@ def main(argv=None):
     ap.add_argument("--plan-ctx", type=int, default=2048, help="plan-compare: tokens per request")
     ap.add_argument("--plan-x", type=float, nargs="+", default=[0.01, 0.02, 0.05],
                     help="plan-compare: global host shares to compare at")
+    ap.add_argument("--b70-batch", type=int, default=16, help="llama70b: requests (activation rows N)")
+    ap.add_argument("--b70-weights", choices=("bf16", "fp8"), default="bf16", help="llama70b: weight format")
+    ap.add_argument("--b70-kv-unit", choices=("request", "head"), default="request",
+                    help="llama70b: KV host unit (whole requests or single (request, KV head) pairs)")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,
                     help="HBM kept free for activations, outputs and workspace in the llama70b plan")
     ap.add_argument("--n-act", type=int, default=BATCH,

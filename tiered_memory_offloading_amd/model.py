@@ -16,7 +16,11 @@ split operators read.
 
 Weights ~ N(0, 0.02) and KV ~ N(0, 1) are generated on the GPU with a seeded
 device generator, in chunks (HBM is nearly full): fp32 normals, scaled, rounded
-to bf16.
+to bf16.  With FP8 weights (the pages run their models in FP8), each weight is
+an e4m3 code of N(0, 1) / 16 (cast by torch, round to nearest even) and every
+row's scale is 0.02 * 16, so the logical weights are again ~N(0, 0.02); a
+tile-row then holds m * K bytes.  The KV cache's host units are whole requests
+or, with kv_unit = KV_UNIT_HEAD, single (request, KV head) pairs.
 """
 from __future__ import annotations
 
@@ -28,7 +32,7 @@ from typing import List, Optional
 import torch
 
 from . import Op, SplitKV, SplitMatrix, plan_offload, min_offload_ratio, splitk_decode_attn, splitk_gemm
-from . import decode_attn_workspace_bytes
+from . import KV_UNIT_HEAD, KV_UNIT_REQUEST, SplitMatrixFP8, decode_attn_workspace_bytes, splitk_gemm_fp8
 
 
 @dataclass(frozen=True)
@@ -68,9 +72,9 @@ class OpSlot:
 
 
 def _fill_normal_(t: torch.Tensor, std: float, gen: torch.Generator, stage: torch.Tensor):
-    """Fill a bf16 tensor (device or pinned host) with std * N(0, 1), one
-    staging-buffer chunk at a time (fp32 normals drawn into `stage`, scaled,
-    rounded to bf16 by the copy)."""
+    """Fill a bf16 tensor (device or pinned host) with std * N(0, 1), or a
+    uint8 tensor with the e4m3 codes of std * N(0, 1), one staging-buffer chunk
+    at a time (fp32 normals drawn into `stage`, scaled, rounded by the cast)."""
     flat = t.view(-1)
     n = flat.numel()
     chunk = stage.numel()
@@ -80,7 +84,10 @@ def _fill_normal_(t: torch.Tensor, std: float, gen: torch.Generator, stage: torc
         torch.randn((m,), generator=gen, out=v)
         if std != 1.0:
             v.mul_(std)
-        flat[i:i + m].copy_(v)
+        if t.dtype == torch.uint8:
+            flat[i:i + m].copy_(v.to(torch.float8_e4m3fn).view(torch.uint8))
+        else:
+            flat[i:i + m].copy_(v)
 
 
 class DecodeModel:
@@ -88,18 +95,28 @@ class DecodeModel:
 
     def __init__(self, shape: DecoderShape, batch: int, ctx: int, b_hbm: float, b_host: float,
                  hbm_bytes: int, m: int = 64, seed: int = 0, t_comp=None, log=print,
-                 x_global: Optional[float] = None, policy: str = "greedy"):
+                 x_global: Optional[float] = None, policy: str = "greedy", weights: str = "bf16",
+                 kv_unit: int = KV_UNIT_REQUEST):
+        if weights not in ("bf16", "fp8"):
+            raise ValueError("weights must be 'bf16' or 'fp8'")
+        if kv_unit not in (KV_UNIT_REQUEST, KV_UNIT_HEAD):
+            raise ValueError("kv_unit must be KV_UNIT_REQUEST or KV_UNIT_HEAD")
+        if weights == "fp8" and batch > 64:
+            raise ValueError("the FP8 split GEMM takes N <= 64 activations")
         self.shape, self.batch, self.ctx, self.m = shape, batch, ctx, m
         self.b_hbm, self.b_host = b_hbm, b_host
+        self.weights, self.kv_unit = weights, kv_unit
         s = shape
-        kv_unit = 2 * s.n_kv_heads * ctx * s.head_dim * 2      # K and V of one request, one layer
+        kv_req = 2 * s.n_kv_heads * ctx * s.head_dim * 2       # K and V of one request, one layer
+        attn_units = batch if kv_unit == KV_UNIT_REQUEST else batch * s.n_kv_heads
+        wbytes = 1 if weights == "fp8" else 2
         self.slots: List[OpSlot] = []
         lin = s.linears()
         for layer in range(s.layers):
             for name, M, K in lin:
                 if name == "o":
-                    self.slots.append(OpSlot(layer, "attn", batch, kv_unit))
-                self.slots.append(OpSlot(layer, name, M // m, m * K * 2))
+                    self.slots.append(OpSlot(layer, "attn", attn_units, kv_req * batch // attn_units))
+                self.slots.append(OpSlot(layer, name, M // m, m * K * wbytes))
         # order within a layer: qkv, attn, o, gate_up, down
         self.footprint = sum(o.bytes for o in self.slots)
         self.hbm_bytes = hbm_bytes
@@ -138,29 +155,41 @@ class DecodeModel:
         stage = torch.empty((1 << 26,), dtype=torch.float32, device=dev)
         lin = {name: (M, K) for name, M, K in s.linears()}
         fills = []
+        fp8 = self.weights == "fp8"
+        wdt = torch.uint8 if fp8 else torch.bfloat16
+        scales = {}
         for i, o in enumerate(self.slots):
             if o.kind == "attn":
-                shp = (s.n_kv_heads, self.ctx, s.head_dim)
-                h = o.host_units
+                # unit blocks [ctx, D] in (request, KV head) order either way
+                shp = (self.ctx, s.head_dim)
+                units = self.batch * s.n_kv_heads
+                hu = o.host_units * (s.n_kv_heads if self.kv_unit == KV_UNIT_REQUEST else 1)
                 kh = vh = kg = vg = None
-                if h:
-                    kh = torch.empty((h,) + shp, dtype=torch.bfloat16, pin_memory=True)
-                    vh = torch.empty((h,) + shp, dtype=torch.bfloat16, pin_memory=True)
-                if h < self.batch:
-                    kg = torch.empty((self.batch - h,) + shp, dtype=torch.bfloat16, device=dev)
-                    vg = torch.empty((self.batch - h,) + shp, dtype=torch.bfloat16, device=dev)
+                if hu:
+                    kh = torch.empty((hu,) + shp, dtype=torch.bfloat16, pin_memory=True)
+                    vh = torch.empty((hu,) + shp, dtype=torch.bfloat16, pin_memory=True)
+                if hu < units:
+                    kg = torch.empty((units - hu,) + shp, dtype=torch.bfloat16, device=dev)
+                    vg = torch.empty((units - hu,) + shp, dtype=torch.bfloat16, device=dev)
                 fills += [(t, 1.0) for t in (kh, vh, kg, vg) if t is not None]
-                o.desc = SplitKV(kh, vh, kg, vg, self.batch, h, s.n_kv_heads, s.head_dim, self.ctx)
+                o.desc = SplitKV(kh, vh, kg, vg, self.batch, o.host_units, s.n_kv_heads, s.head_dim, self.ctx,
+                                 self.kv_unit)
             else:
                 M, K = lin[o.kind]
                 rows = o.host_units * self.m
                 ah = ag = None
                 if rows:
-                    ah = torch.empty((rows, K), dtype=torch.bfloat16, pin_memory=True)
+                    ah = torch.empty((rows, K), dtype=wdt, pin_memory=True)
                 if rows < M:
-                    ag = torch.empty((M - rows, K), dtype=torch.bfloat16, device=dev)
-                fills += [(t, 0.02) for t in (ah, ag) if t is not None]
-                o.desc = SplitMatrix(ah, ag, M, K, self.m, o.host_units)
+                    ag = torch.empty((M - rows, K), dtype=wdt, device=dev)
+                # FP8: codes of N(0, 1) / 16 (well inside e4m3's range), row scale 0.02 * 16
+                fills += [(t, 1.0 / 16 if fp8 else 0.02) for t in (ah, ag) if t is not None]
+                if fp8:
+                    if M not in scales:
+                        scales[M] = torch.full((M,), 0.02 * 16, dtype=torch.float32, device=dev)
+                    o.desc = SplitMatrixFP8(ah, ag, scales[M], M, K, self.m, o.host_units)
+                else:
+                    o.desc = SplitMatrix(ah, ag, M, K, self.m, o.host_units)
         log(f"  allocated {len(self.slots)} ops; filling {len(fills)} tensors")
         for i, (t, std) in enumerate(fills):
             _fill_normal_(t, std, gen, stage)
@@ -189,6 +218,8 @@ class DecodeModel:
                 events[i][0].record()
             if o.kind == "attn":
                 splitk_decode_attn(self.q, o.desc, self.scale, out=self.out, ws=self.ws)
+            elif self.weights == "fp8":
+                splitk_gemm_fp8(o.desc, self.x[o.kind], y=self.y[o.kind])
             else:
                 splitk_gemm(o.desc, self.x[o.kind], y=self.y[o.kind])
             if events is not None:

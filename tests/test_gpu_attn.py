@@ -242,3 +242,18 @@ def test_output_layout_checked_by_the_binding():
         dak.splitk_decode_attn(q.cuda(), kv, 0.1, out=torch.empty((2, 4, 128), dtype=torch.float16, device="cuda"))
     with pytest.raises(ValueError):
         dak.splitk_decode_attn(q.cuda(), kv, 0.1, out=torch.empty((2, 128, 4), device="cuda").transpose(1, 2))
+
+
+def test_eight_head_kv_bytes_read_once():
+    # Eight grouped heads: one wave of a token half loads K, the other V.
+    B, Hq, Hkv, D, ctx = 3, 16, 2, 128, 3100
+    q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=46)
+    lens = torch.tensor([3100, 1030, 1], dtype=torch.int32)
+    for unit, h in ((dak.KV_UNIT_REQUEST, 1), (dak.KV_UNIT_HEAD, 3)):
+        kv = dak.place_kv(K, V, h, unit=unit, ctx_lens=lens)
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        dak.splitk_decode_attn(q.cuda(), kv, 0.1, cfg=dak.LaunchConfig(byte_counters=cnt))
+        torch.cuda.synchronize()
+        per_unit = [int(lens[u // Hkv]) * D * 2 * 2 for u in range(B * Hkv)]
+        hu = kv.host_units
+        assert cnt.tolist() == [sum(per_unit[:hu]), sum(per_unit[hu:])]

@@ -30,7 +30,7 @@ def run(codes, scale, x, m, h, cfg=None):
     return y.cpu()
 
 
-@pytest.mark.parametrize("N", [1, 4, 5, 16, 17, 33, 64])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 9, 16, 17, 33, 64])
 def test_every_code_and_split(N):
     # Every finite code, K not a multiple of 32 (a half step at the end).
     M, K, m = 192, 528, 64
@@ -46,6 +46,20 @@ def test_every_code_and_split(N):
     for h in range(1, M // m + 1):
         assert torch.equal(run(codes, scale, x, m, h), base), h
 
+
+
+def test_columns_do_not_depend_on_the_batch():
+    # Output column n is the same MFMA sequence on the same activation row for
+    # any N > n: small batches stage fewer activation rows (the others are
+    # recomputed from staged rows and dropped), which must not change a bit.
+    M, K, m = 256, 1040, 64
+    codes = synth.fp8_all_codes(M, K, seed=3)
+    scale = torch.rand(M, generator=torch.Generator().manual_seed(3)) * 0.01 + 1e-3
+    x = synth.gemm_inputs(16, K, 64, seed=3)[1]
+    for h in (0, 2):
+        full = run(codes, scale, x, m, h)
+        for N in (1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63):
+            assert torch.equal(run(codes, scale, x[:N], m, h), full[:N]), (h, N)
 
 def test_power_of_two_scales_exact():
     # Integer-valued codes, power-of-two scales and integer activations: every

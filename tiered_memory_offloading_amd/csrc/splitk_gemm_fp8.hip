@@ -15,7 +15,11 @@
 //     pieces of 256 bytes and more) and 512 per activation row;
 //   * each chunk's A rows (four per 1 KiB DMA instruction) and x rows (two
 //     per instruction) land in one slot of an LDS ring through
-//     global_load_lds_dwordx4; STAGES - 1 chunks are in flight;
+//     global_load_lds_dwordx4; STAGES - 1 chunks are in flight.  Below 16
+//     activation rows only XR = 2, 4 or 8 x rows are staged (the smallest
+//     power of two >= N): the MFMA's other columns read those rows again and
+//     are never stored, and every staged x line is an L2 request that an A
+//     line could have used;
 //   * a wave reads its A fragment (8 codes of one row) from LDS, widens it to
 //     bf16 with v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value,
 //     subnormals included, is a bf16 normal), and runs
@@ -48,22 +52,41 @@ constexpr int kF8XRow = kF8KC * 2;     // bytes per staged x row
 constexpr int kF8Steps = kF8KC / 32;   // MFMA steps per chunk
 constexpr int64_t kF8MaxN = 64;
 
-template <int NB, int RB>
+// XR: activation rows staged per chunk when NB = 1 (2, 4, 8 or 16); NB > 1
+// stages all 16 NB rows.
+template <int NB, int RB, int XR = 16>
 struct F8Shape {
+  static_assert(NB == 1 || XR == 16, "partial activation blocks only for one column block");
+  static_assert(XR == 2 || XR == 4 || XR == 8 || XR == 16, "XR is a power of two");
   static constexpr int R = 16 * RB;                  // A rows per item
+  static constexpr int XROWS = NB == 1 ? XR : 16 * NB;
   static constexpr int A_BYTES = R * kF8ARow;
-  static constexpr int X_BYTES = 16 * NB * kF8XRow;
+  static constexpr int X_BYTES = XROWS * kF8XRow;
   static constexpr int SLOT = A_BYTES + X_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024;     // 4 A rows per instruction
   static constexpr int INSTR = SLOT / 1024;
-  static constexpr int PER_WAVE = INSTR / kF8Waves;
+  // Wave w issues instructions w, w + 4, ...: LO or LO + 1 of them per chunk.
+  static constexpr int LO = INSTR / kF8Waves;
+  static constexpr int HI_WAVES = INSTR % kF8Waves;  // waves [0, HI_WAVES) issue LO + 1
+  static constexpr int MAX_PER_WAVE = LO + (HI_WAVES ? 1 : 0);
   static constexpr int P = kF8Waves / RB;            // k-phases
-  static_assert(INSTR % kF8Waves == 0, "every wave issues the same number of DMA instructions");
-  static_assert(PER_WAVE * 2 <= 63, "vmcnt range");
+  static_assert(MAX_PER_WAVE * 2 <= 63, "vmcnt range");
+  static_assert(kF8Waves * NB * 64 * 16 <= SLOT, "the phase partials fit in one slot");
 };
 
+constexpr int f8_slot_bytes(int nb, int rb, int xr) { return 16 * rb * kF8ARow + (nb == 1 ? xr : 16 * nb) * kF8XRow; }
+
 // Ring depth: three slots when they fit in half of the CU's LDS, else two.
-constexpr int f8_stages(int nb, int rb) { return 3 * (16 * rb * kF8ARow + 16 * nb * kF8XRow) <= (80 << 10) ? 3 : 2; }
+constexpr int f8_stages(int nb, int rb, int xr = 16) { return 3 * f8_slot_bytes(nb, rb, xr) <= (80 << 10) ? 3 : 2; }
+
+// Wait until at most `later` chunks' DMA instructions of this wave are still
+// in flight (a wave issues PW instructions per chunk).
+template <int PW>
+__device__ __forceinline__ void f8_wait_later(int64_t later) {
+  if (later >= 2) vm_wait<2 * PW>();
+  else if (later == 1) vm_wait<PW>();
+  else vm_wait<0>();
+}
 
 // Eight e4m3 codes (k ascending from the low byte) widened to eight bf16.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
@@ -75,9 +98,9 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
 
-template <int NB, int RB, bool COUNT>
+template <int NB, int RB, int XR, bool COUNT>
 struct F8Item {
-  using S = F8Shape<NB, RB>;
+  using S = F8Shape<NB, RB, XR>;
 
   // DMA chunk c of the item whose first A row is `a` into `slot`.  Pieces past
   // K and activation rows past N are fetched from an in-bounds address and
@@ -86,8 +109,9 @@ struct F8Item {
                                                const uint16_t* __restrict__ x, int64_t N, int64_t K, int wave,
                                                int lane, uint64_t& nbytes) {
 #pragma unroll
-    for (int j = 0; j < S::PER_WAVE; ++j) {
-      const int ins = wave * S::PER_WAVE + j;
+    for (int j = 0; j < S::MAX_PER_WAVE; ++j) {
+      const int ins = wave + kF8Waves * j;
+      if (ins >= S::INSTR) break;   // uniform
       const void* src;
       if (ins < S::A_INSTR) {   // uniform
         const int r = 4 * ins + (lane >> 4);
@@ -122,7 +146,7 @@ struct F8Item {
       const int px = 4 * t + g;
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        const int xr = 16 * cb + i16;
+        const int xr = NB == 1 ? (i16 & (XR - 1)) : 16 * cb + i16;   // staged row of column 16 cb + i16
         uint4 xf = *reinterpret_cast<const uint4*>(slot + S::A_BYTES + xr * kF8XRow + ((px ^ (xr & 15)) << 4));
         if (!kok) xf = make_uint4(0, 0, 0, 0);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc[cb], 0, 0, 0);
@@ -131,14 +155,14 @@ struct F8Item {
   }
 };
 
-template <int NB, int RB, int STAGES, bool COUNT>
+template <int NB, int RB, int XR, int STAGES, bool COUNT>
 __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
     const unsigned char* __restrict__ a_host, const unsigned char* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const float* __restrict__ row_scale, const uint16_t* __restrict__ x, int64_t N,
     float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
     unsigned long long* __restrict__ counters) {
-  using S = F8Shape<NB, RB>;
-  using I = F8Item<NB, RB, COUNT>;
+  using S = F8Shape<NB, RB, XR>;
+  using I = F8Item<NB, RB, XR, COUNT>;
   __shared__ __attribute__((aligned(16))) unsigned char s0[S::SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char s1[S::SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char s2[STAGES > 2 ? S::SLOT : 16];
@@ -169,9 +193,8 @@ __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
     const int64_t c = c0 + IDX;                                                                  \
     if (c < nch) {                                                                               \
       const int64_t later = std::min<int64_t>(nch - 1 - c, STAGES - 2);                          \
-      if (later >= 2) vm_wait<2 * S::PER_WAVE>();                                                \
-      else if (later == 1) vm_wait<S::PER_WAVE>();                                               \
-      else vm_wait<0>();                                                                         \
+      if (wave < S::HI_WAVES) f8_wait_later<S::LO + 1>(later);                                   \
+      else f8_wait_later<S::LO>(later);                                                          \
       __builtin_amdgcn_s_barrier();                                                              \
       if (c + STAGES - 1 < nch) I::issue(WR, c + STAGES - 1, a, x, N, K, wave, lane, nbytes);    \
       I::compute(RD, c, K, rb, phase, lane, acc);                                                \
@@ -248,11 +271,11 @@ struct F8Args {
   hipStream_t stream;
 };
 
-template <int NB, int RB, int ST, bool COUNT>
+template <int NB, int RB, int XR, int ST, bool COUNT>
 void launch_f8_nb_rb_st(const F8Args& g) {
-  static_assert(ST * F8Shape<NB, RB>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
+  static_assert(ST * F8Shape<NB, RB, XR>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
   const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_fp8_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
+  hipLaunchKernelGGL((gemm_fp8_split<NB, RB, XR, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.row_scale, g.x, g.N, g.y, g.host_wgs, g.host_items,
                      g.hbm_items, g.counters);
 }
@@ -264,34 +287,43 @@ void launch_f8_nb_rb_st(const F8Args& g) {
 // the rows on the host 0.56 -> 0.65 and 0.63 -> 0.74 of the two-tier
 // roofline; without host rows the deeper ring was 4 % slower, so it is kept
 // to launches with a host role).  The depth changes no arithmetic.
-template <int NB, int RB, bool COUNT>
+template <int NB, int RB, int XR, bool COUNT>
 void launch_f8_nb_rb(const F8Args& g) {
-  constexpr int ST = f8_stages(NB, RB);
-  if constexpr (ST == 2 && 3 * F8Shape<NB, RB>::SLOT <= (160 << 10)) {
+  constexpr int ST = f8_stages(NB, RB, XR);
+  if constexpr (ST == 2 && 3 * F8Shape<NB, RB, XR>::SLOT <= (160 << 10)) {
     const uint64_t host_inflight = (uint64_t)g.host_wgs * 2 * 16 * RB * kF8ARow;
     if (g.host_wgs > 0 && g.host_wgs + g.hbm_items <= g.cus && host_inflight <= kHostInflightBytes)
-      return launch_f8_nb_rb_st<NB, RB, 3, COUNT>(g);
+      return launch_f8_nb_rb_st<NB, RB, XR, 3, COUNT>(g);
   }
-  launch_f8_nb_rb_st<NB, RB, ST, COUNT>(g);
+  launch_f8_nb_rb_st<NB, RB, XR, ST, COUNT>(g);
 }
 
-template <int NB, bool COUNT>
+template <int NB, int XR, bool COUNT>
 void launch_f8_nb(const F8Args& g, int rb) {
   switch (rb) {
-    case 4: return launch_f8_nb_rb<NB, 4, COUNT>(g);
-    case 2: return launch_f8_nb_rb<NB, 2, COUNT>(g);
-    default: return launch_f8_nb_rb<NB, 1, COUNT>(g);
+    case 4: return launch_f8_nb_rb<NB, 4, XR, COUNT>(g);
+    case 2: return launch_f8_nb_rb<NB, 2, XR, COUNT>(g);
+    default: return launch_f8_nb_rb<NB, 1, XR, COUNT>(g);
   }
 }
 
 int f8_nb_of(int64_t N) { return N <= 16 ? 1 : N <= 32 ? 2 : 4; }
 
+// Activation rows staged per chunk: the smallest power of two >= N, at least 2.
+int f8_xr_of(int64_t N) { return N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16; }
+
 template <bool COUNT>
 void launch_f8(const F8Args& g, int rb) {
   switch (f8_nb_of(g.N)) {
-    case 1: return launch_f8_nb<1, COUNT>(g, rb);
-    case 2: return launch_f8_nb<2, COUNT>(g, rb);
-    default: return launch_f8_nb<4, COUNT>(g, rb);
+    case 1:
+      switch (f8_xr_of(g.N)) {
+        case 2: return launch_f8_nb<1, 2, COUNT>(g, rb);
+        case 4: return launch_f8_nb<1, 4, COUNT>(g, rb);
+        case 8: return launch_f8_nb<1, 8, COUNT>(g, rb);
+        default: return launch_f8_nb<1, 16, COUNT>(g, rb);
+      }
+    case 2: return launch_f8_nb<2, 16, COUNT>(g, rb);
+    default: return launch_f8_nb<4, 16, COUNT>(g, rb);
   }
 }
 
@@ -306,7 +338,8 @@ int f8_row_blocks(int64_t M, int64_t m) {
 // Host work-groups: enough that their chunks in flight cover the link's
 // bandwidth-delay product.
 int f8_host_cus(int64_t N, int rb) {
-  const uint64_t inflight = (uint64_t)(f8_stages(f8_nb_of(N), rb) - 1) * 16 * rb * kF8ARow;
+  const int nb = f8_nb_of(N);
+  const uint64_t inflight = (uint64_t)(f8_stages(nb, rb, nb == 1 ? f8_xr_of(N) : 16) - 1) * 16 * rb * kF8ARow;
   const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
   return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
 }

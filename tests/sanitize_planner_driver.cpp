@@ -22,6 +22,33 @@ static int fails = 0;
     }                                                                 \
   } while (0)
 
+// T_i(h) = max(T_comp, (n - h) u / B_g, h u / B_h) in the planner's double
+// order (DAK paper §4.2.1), and its first and last minimisers over every h
+// (§4.2.2): the reference the library's turning points must equal.
+static double cost(const dak_op_desc& op, uint64_t h, double b_g, double b_h) {
+  const double tg = static_cast<double>((op.units - h) * op.unit_bytes) / b_g;
+  const double th = static_cast<double>(h * op.unit_bytes) / b_h;
+  double t = op.t_comp_s;
+  if (tg > t) t = tg;
+  if (th > t) t = th;
+  return t;
+}
+static void scan(const dak_op_desc& op, double b_g, double b_h, uint64_t* a, uint64_t* b) {
+  double best = cost(op, 0, b_g, b_h);
+  uint64_t first = 0, last = 0;
+  for (uint64_t h = 1; h <= op.units; ++h) {
+    const double t = cost(op, h, b_g, b_h);
+    if (t < best) {
+      best = t;
+      first = last = h;
+    } else if (t == best) {
+      last = h;
+    }
+  }
+  *a = first;
+  *b = last;
+}
+
 int main() {
   std::mt19937_64 rng(12345);
   auto uni = [&](uint64_t lo, uint64_t hi) { return lo + rng() % (hi - lo + 1); };
@@ -58,6 +85,43 @@ int main() {
       EXPECT(a <= b && b <= ops[i].units && (mb == 0 || mb == 1));
       EXPECT(dak_op_turning_points(&ops[i], bg, bh, nullptr, nullptr, nullptr) == DAK_OK);
     }
+  }
+  // Turning points equal the scan on tie-heavy ops: dyadic sizes and
+  // bandwidths, T_comp at one side's time for some h, or above both.
+  for (int trial = 0; trial < 200000; ++trial) {
+    dak_op_desc op;
+    const int kind = (int)(rng() % 6);
+    op.units = uni(1, kind == 0 ? 4 : kind == 1 ? 64 : 3000);
+    op.unit_bytes = kind == 2 ? (1ull << (rng() % 30)) : uni(1, 1u << 26);
+    const double bg = kind == 2 ? std::ldexp(1.0, 20 + (int)(rng() % 20)) : 1e6 * (double)uni(1, 8000);
+    const double bh = kind == 2 ? std::ldexp(1.0, 10 + (int)(rng() % 20)) : 1e6 * (double)uni(1, 64);
+    const double full = static_cast<double>(op.units * op.unit_bytes) / bg;
+    switch (rng() % 5) {
+      case 0: op.t_comp_s = 0.0; break;
+      case 1: op.t_comp_s = 2.0 * full; break;
+      case 2: op.t_comp_s = full * (double)uni(0, 999) / 1000.0; break;
+      case 3: op.t_comp_s = static_cast<double>((op.units - uni(0, op.units - 1)) * op.unit_bytes) / bh; break;
+      default: op.t_comp_s = std::ldexp(1.0, -(int)(rng() % 40)); break;
+    }
+    uint64_t a0, b0, a1 = 7, b1 = 7;
+    scan(op, bg, bh, &a0, &b0);
+    EXPECT(dak_op_turning_points(&op, bg, bh, &a1, &b1, nullptr) == DAK_OK && a0 == a1 && b0 == b1);
+    if (fails) break;
+  }
+  // Ops of 2^30..2^40 units (too many to scan): plans return, within bounds.
+  for (int trial = 0; trial < 2000; ++trial) {
+    const size_t n = uni(1, 6);
+    std::vector<dak_op_desc> ops(n);
+    for (auto& op : ops) {
+      op.units = uni(1ull << 30, 1ull << 40);
+      op.unit_bytes = uni(1, 1024);   // six ops stay under the 2^53-byte total
+      op.t_comp_s = (rng() % 2) ? 0.0 : std::ldexp((double)uni(1, 1000), -(int)uni(0, 10));
+    }
+    std::vector<uint64_t> h(n + 1, 777);
+    EXPECT(dak_plan_offload(ops.data(), n, 6.4e12, 5.76e10, (double)uni(0, 1000) / 1000.0, h.data(), nullptr) ==
+           DAK_OK);
+    for (size_t i = 0; i < n; ++i) EXPECT(h[i] <= ops[i].units);
+    EXPECT(h[n] == 777);
   }
   // Argument errors: every one reported, with a message, no crash.
   dak_op_desc good{4, 100, 0.0};

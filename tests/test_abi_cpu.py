@@ -76,6 +76,48 @@ def test_turning_points_match_oracle():
         assert mb == op.memory_bound(o, bg, bh)
 
 
+
+def test_turning_points_match_oracle_on_plateaus():
+    # Dyadic sizes and bandwidths make T_i(h) hit exact ties, and T_comp set to
+    # one side's time at some h makes flat stretches: the first and last
+    # minimisers must still be the oracle's (a scan of every h).
+    rng = random.Random(23)
+    for _ in range(400):
+        n = rng.choice([1, 2, 3, 7, 64, 333])
+        u = 1 << rng.randint(0, 24)
+        bg, bh = 2.0 ** rng.randint(30, 43), 2.0 ** rng.randint(20, 36)
+        k = rng.randint(0, n)
+        tc = rng.choice([0.0, (n - k) * u / bg, k * u / bh, 2.0 * n * u / bg, 2.0 ** -rng.randint(5, 40)])
+        o = op.Op(n, u, tc)
+        a, b, mb = dak.op_turning_points(dak.Op(n, u, tc), bg, bh)
+        assert (a, b) == op.argmin_range(o, bg, bh), (n, u, tc, bg, bh)
+        assert mb == op.memory_bound(o, bg, bh)
+
+
+def test_turning_points_of_a_huge_op_are_minimisers():
+    # 2^40 units: too many to scan.  The library's answer must be minimal at
+    # both ends, strictly worse one unit outside, no better at sampled h, and
+    # (with T_comp = 0) sit where (n - h) / B_g = h / B_h, i.e. h* = n B_h / (B_g + B_h).
+    n, u = 1 << 40, 4096
+    bg, bh = 6.4e12, 5.76e10
+    t = lambda h, tc: op.unit_time(n, u, h, tc, bg, bh)
+    for tc in (0.0, 1e-3, 500.0, 1e6):
+        a, b, _ = dak.op_turning_points(dak.Op(n, u, tc), bg, bh)
+        assert 0 <= a <= b <= n
+        best = t(a, tc)
+        assert t(b, tc) == best
+        if a > 0:
+            assert t(a - 1, tc) > best
+        if b < n:
+            assert t(b + 1, tc) > best
+        rng = random.Random(int(tc * 1000) + 1)
+        for h in [rng.randint(0, n) for _ in range(2000)] + [0, n, (a + b) // 2]:
+            assert t(h, tc) >= best
+        if tc == 0.0:
+            assert abs(a - n * bh / (bg + bh)) <= 2 and b - a <= 2
+        if tc == 1e6:   # above both sides' time at every split (n u / B_h = 7.8e4 s): every h ties
+            assert (a, b) == (0, n)
+
 def test_decode_step_plan_of_a_70b_shape_matches_oracle():
     # 80 layers x {QKV, attention, O, gate+up, down} with 64-row tile-rows and
     # one request per attention unit; KV for 16 requests of 32768 tokens.

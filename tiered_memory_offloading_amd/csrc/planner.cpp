@@ -12,28 +12,63 @@
 namespace {
 
 // T_i(h) = max(T_comp, (n - h) u / B_g, h u / B_h): integer byte counts,
-// converted to double once, then divided by the bandwidth.
+// converted to double once, then divided by the bandwidth.  Split as
+// T_i(h) = max(D(h), G(h)) with D(h) = max(T_comp, (n - h) u / B_g) and
+// G(h) = max(T_comp, h u / B_h); max is exact, so this is the same double.
+inline double hbm_side(const dak_op_desc& op, uint64_t h, double b_g) {
+  const double tg = static_cast<double>((op.units - h) * op.unit_bytes) / b_g;
+  return tg > op.t_comp_s ? tg : op.t_comp_s;
+}
+inline double host_side(const dak_op_desc& op, uint64_t h, double b_h) {
+  const double th = static_cast<double>(h * op.unit_bytes) / b_h;
+  return th > op.t_comp_s ? th : op.t_comp_s;
+}
 inline double unit_time(const dak_op_desc& op, uint64_t h, double b_g, double b_h) {
-  double tg = static_cast<double>((op.units - h) * op.unit_bytes) / b_g;
-  double th = static_cast<double>(h * op.unit_bytes) / b_h;
-  double t = op.t_comp_s;
-  if (tg > t) t = tg;
-  if (th > t) t = th;
-  return t;
+  const double d = hbm_side(op, h, b_g), g = host_side(op, h, b_h);
+  return g > d ? g : d;
 }
 
-// First and last h in [0, n] at which T_i is minimal.
+// First and last h in [0, n] at which T_i is minimal: the same pair as a scan
+// of every h, found by bisection.  Integer-to-double conversion and a
+// correctly rounded division by a positive bandwidth are monotone, so D is
+// non-increasing and G non-decreasing in h, exactly as computed.  With k the
+// first h where D(h) <= G(h) (k <= n, as D(n) = T_comp <= G(n)), T = D on
+// [0, k) and T = G on [k, n] (for h > k, D(h) <= D(k) <= G(k) <= G(h)): the
+// minimum is min(D(k - 1), G(k)), the minimisers form one interval, and its
+// ends are the first h with D(h) <= min and the last h with G(h) <= min.
 void argmin_range(const dak_op_desc& op, double b_g, double b_h, uint64_t* a, uint64_t* b) {
-  double best = unit_time(op, 0, b_g, b_h);
-  uint64_t first = 0, last = 0;
-  for (uint64_t h = 1; h <= op.units; ++h) {
-    double t = unit_time(op, h, b_g, b_h);
-    if (t < best) {
-      best = t;
-      first = last = h;
-    } else if (t == best) {
-      last = h;
+  const uint64_t n = op.units;
+  uint64_t lo = 0, hi = n;
+  while (lo < hi) {   // first h with D(h) <= G(h)
+    const uint64_t mid = lo + (hi - lo) / 2;
+    if (hbm_side(op, mid, b_g) <= host_side(op, mid, b_h)) hi = mid;
+    else lo = mid + 1;
+  }
+  const uint64_t k = lo;
+  const double right = host_side(op, k, b_h);
+  const bool has_left = k > 0;
+  const double left = has_left ? hbm_side(op, k - 1, b_g) : right;
+  const double best = has_left && left < right ? left : right;
+  uint64_t first = k, last = k - 1;   // last is set below whenever right is minimal
+  if (has_left && left <= right) {   // minimisers in [0, k): first h with D(h) <= best
+    lo = 0;
+    hi = k - 1;
+    while (lo < hi) {
+      const uint64_t mid = lo + (hi - lo) / 2;
+      if (hbm_side(op, mid, b_g) <= best) hi = mid;
+      else lo = mid + 1;
     }
+    first = lo;
+  }
+  if (right <= best) {   // minimisers in [k, n]: last h with G(h) <= best
+    lo = k;
+    hi = n;
+    while (lo < hi) {
+      const uint64_t mid = lo + (hi - lo + 1) / 2;
+      if (host_side(op, mid, b_h) <= best) lo = mid;
+      else hi = mid - 1;
+    }
+    last = lo;
   }
   *a = first;
   *b = last;

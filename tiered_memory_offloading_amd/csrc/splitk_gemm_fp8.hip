@@ -17,7 +17,7 @@
 //     per instruction) land in one slot of an LDS ring through
 //     global_load_lds_dwordx4; STAGES - 1 chunks are in flight.  Below 16
 //     activation rows only XR = 2, 4 or 8 x rows are staged (the smallest
-//     power of two >= N): the MFMA's other columns read those rows again and
+//     power of two >= max(N, 2)): the MFMA's other columns read those rows again and
 //     are never stored, and every staged x line is an L2 request that an A
 //     line could have used;
 //   * a wave reads its A fragment (8 codes of one row) from LDS, widens it to

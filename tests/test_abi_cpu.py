@@ -118,6 +118,42 @@ def test_turning_points_of_a_huge_op_are_minimisers():
         if tc == 1e6:   # above both sides' time at every split (n u / B_h = 7.8e4 s): every h ties
             assert (a, b) == (0, n)
 
+
+def test_error_messages_stay_with_their_thread():
+    # The last error is thread-local: threads that fail in different ways at
+    # the same time, between successful calls, each read back their own message.
+    import threading
+    good = [dak.Op(8, 1 << 20, 0.0), dak.Op(3, 4096, 1e-6)]
+    cases = [
+        ("must lie in [0, 1]", lambda: dak.plan_offload(good, 6.4e12, 5.76e10, 1.5)),
+        ("bandwidths must be positive", lambda: dak.plan_offload(good, -1.0, 5.76e10, 0.1)),
+        ("units and unit_bytes", lambda: dak.plan_offload([dak.Op(0, 8, 0.0)], 6.4e12, 5.76e10, 0.1)),
+        ("t_comp_s must be finite", lambda: dak.plan_offload([dak.Op(4, 8, float("nan"))], 6.4e12, 5.76e10, 0.1)),
+    ]
+    bad = []
+
+    def worker(k):
+        want, call = cases[k % len(cases)]
+        for i in range(400):
+            if i % 2:
+                h, _ = dak.plan_offload(good, 6.4e12, 5.76e10, 0.25)
+                if sum(hi * o.unit_bytes for hi, o in zip(h, good)) < 0.25 * sum(o.units * o.unit_bytes for o in good):
+                    bad.append((k, "budget"))
+                continue
+            try:
+                call()
+                bad.append((k, "no error"))
+            except dak.DakError as e:
+                if want not in str(e):
+                    bad.append((k, str(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:5]
+
 def test_decode_step_plan_of_a_70b_shape_matches_oracle():
     # 80 layers x {QKV, attention, O, gate+up, down} with 64-row tile-rows and
     # one request per attention unit; KV for 16 requests of 32768 tokens.

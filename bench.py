@@ -18,7 +18,7 @@ Inputs are seeded synthetic tensors drawn with the recipe of synth.py (std
 are held in both tiers, so every ratio of the sweep is a different descriptor
 over the same buffers.
 
-Prints ONE JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints ONE JSON line.  --gpus above 1 is refused: the library runs on one GPU (no collectives or sharding).
 """
 from __future__ import annotations
 
@@ -839,7 +839,7 @@ def main(argv=None):
                     help="time one operator of the step (for profiling); the JSON then covers that op only")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no collectives or sharding); use --gpus 1",
+        print("bench.py: the library runs on one GPU (no collectives or sharding); use --gpus 1",
               file=sys.stderr)
         return 2
 

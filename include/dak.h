@@ -42,7 +42,7 @@ enum {
   DAK_EINVAL = -1,        /* bad argument (shape, pointer, alignment, range) */
   DAK_EINFEASIBLE = -2,   /* the host budget exceeds what the ops hold */
   DAK_EHIP = -3,          /* a HIP runtime call failed; see dak_last_hip_error() */
-  DAK_EUNSUPPORTED = -4   /* a valid request this build does not implement */
+  DAK_EUNSUPPORTED = -4   /* a valid request the library does not implement */
 };
 
 /* Message describing the last error on the calling thread ("" if none). */

@@ -34,7 +34,7 @@
 namespace dak {
 namespace {
 
-constexpr int kD = 128;                 // head_dim handled by this build
+constexpr int kD = 128;                 // the only head_dim the kernels handle
 constexpr int kChunk = 2048;            // tokens per work item
 constexpr int kAttnWaves = 4;
 constexpr int kWaveTokens = kChunk / kAttnWaves;

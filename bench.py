@@ -477,7 +477,7 @@ def run_linears(torch, dak, args, b_hbm, b_host):
         return e0.elapsed_time(e1) / (reps * len(descs))
 
     points = []
-    ops = [("gemv_cfg1", 1024, 1024)] + list(synth.LLAMA8B_LINEARS)
+    ops = [("gemv_1024x1024", 1024, 1024)] + list(synth.LLAMA8B_LINEARS)
     for oi, (name, M, K) in enumerate(ops):
         n = M // M_TILE
         C = M * K * 2
@@ -487,8 +487,8 @@ def run_linears(torch, dak, args, b_hbm, b_host):
         hmax = host_units(1, 2, n)
         A_host = torch.empty((hmax * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
         A_host.copy_(A[:hmax * M_TILE])
-        ns = (1,) if name == "gemv_cfg1" else (1, 16, 64)
-        ks = (0, 5) if name == "gemv_cfg1" else tuple(range(11))
+        ns = (1,) if name == "gemv_1024x1024" else (1, 16, 64)
+        ks = (0, 5) if name == "gemv_1024x1024" else tuple(range(11))
         for N in ns:
             X = synth.gemm_inputs(M, K, N, seed=oi, device="cuda")[1].contiguous()
             y = torch.empty((N, M), dtype=torch.float32, device="cuda")
@@ -506,7 +506,7 @@ def run_linears(torch, dak, args, b_hbm, b_host):
                       "GBps": round(C / (t * 1e-3) / 1e9, 2), "frac_two_tier": round(t_roof / t, 4),
                       "frac_b_hbm_at_x0": round(t_roof / t, 4) if h == 0 else None, "bit_identical_to_x0": same,
                       "cold_copies": copies}
-                if name == "gemv_cfg1":
+                if name == "gemv_1024x1024":
                     pt["hot_ms"] = round(timed(descs[:1], X, y), 5)
                 points.append(pt)
                 log(f"{name} N={N} x={h / n:.3f}: {t * 1e3:.1f} us, {pt['GBps']:.0f} GB/s, "
@@ -514,12 +514,12 @@ def run_linears(torch, dak, args, b_hbm, b_host):
             del X, y
         del A, As, A_host
         torch.cuda.empty_cache()
-    cfg2 = [p for p in points if p["op"] != "gemv_cfg1"]
-    worst_x_pos = min(p["frac_two_tier"] for p in cfg2 if p["x"] > 0)
-    x0 = [p for p in cfg2 if p["h"] == 0]
+    llama_points = [p for p in points if p["op"] != "gemv_1024x1024"]
+    worst_x_pos = min(p["frac_two_tier"] for p in llama_points if p["x"] > 0)
+    x0 = [p for p in llama_points if p["h"] == 0]
     res = {
         "metric": "effective GB/s (HBM+host) and % of two-tier roofline vs offload ratio x, per decode linear",
-        "value": round(statistics.mean(p["frac_two_tier"] for p in cfg2 if p["x"] > 0), 4),
+        "value": round(statistics.mean(p["frac_two_tier"] for p in llama_points if p["x"] > 0), 4),
         "unit": "mean fraction of the two-tier roofline over N in {1,16,64}, 4 ops, x = 0.05..0.5",
         "n_gpus": 1, "steps": reps, "warmup": 1, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",

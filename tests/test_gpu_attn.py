@@ -43,7 +43,7 @@ def test_small_shapes_all_splits(G, ctx):
         assert torch.equal(outs[h], outs[0]), f"h={h}"
 
 
-def test_config3_full_size():
+def test_llama8b_attention_16x32768_full_size():
     # 16 requests x 32768 tokens, 32 query heads on 8 KV heads, hd 128, 25 % of
     # the requests' KV in pinned host memory.
     B, Hq, Hkv, D, ctx = 16, 32, 8, 128, 32768

@@ -36,7 +36,7 @@ def ref_of(A, X):
     return og.gemm(og.to_f64(A), og.to_f64(X))
 
 
-def test_config1_gemv_quarter_on_host():
+def test_gemv_1024x1024_quarter_on_host():
     # A 1024x1024 ~N(0,0.02), B 1024x1 ~N(0,1), m = 64, first 4 tile-rows on the host.
     A, X = synth.gemm_inputs(1024, 1024, 1, seed=0)
     h = og.host_units(0.25, 1024 // 64)

@@ -4,8 +4,9 @@ A decode step is replayed as a captured graph in serving (and `bench.py` times
 its step that way).  The entry points allocate nothing and only launch kernels
 on the caller's stream, so a captured step must reproduce the eager results
 bit for bit, replay after replay, with eager work in between.  Every GEMM path
-(FMA, staged, register MFMA, tiled) and the attention are captured, each with
-a host share."""
+(FMA, staged, register MFMA, tiled), the FP8 GEMM, the dense attention and the
+paged attention (ragged lengths, random pool pages) are captured, each with a
+host share."""
 import pytest
 import torch
 
@@ -28,15 +29,27 @@ def test_graph_replays_match_eager_launches():
     out = torch.empty((4, 8, 128), dtype=torch.float32, device="cuda")
     ws = torch.empty((dak.decode_attn_workspace_bytes(kv, 8),), dtype=torch.uint8, device="cuda")
     scale = 128 ** -0.5
+    f8 = []
+    for M, K, N, h in [(320, 1024, 1, 2), (512, 1024, 64, 3)]:
+        codes, rs, X = synth.fp8_gemm_inputs(M, K, N, seed=M + N + 1)
+        f8.append((dak.place_matrix_fp8(codes, rs, 64, h), X.cuda(),
+                   torch.empty((N, M), dtype=torch.float32, device="cuda")))
+    lens = torch.tensor([1000, 17, 640, 333], dtype=torch.int32)
+    pkv = dak.place_paged_kv(Kc, Vc, lens, 16, host_units=[1, 6], seed=4)
+    pout = torch.empty((4, 8, 128), dtype=torch.float32, device="cuda")
+    pws = torch.empty((dak.paged_decode_attn_workspace_bytes(pkv, 8),), dtype=torch.uint8, device="cuda")
 
     def step():
         for S, x, y in mats:
             dak.splitk_gemm(S, x, y=y)
+        for S, x, y in f8:
+            dak.splitk_gemm_fp8(S, x, y=y)
         dak.splitk_decode_attn(qd, kv, scale, out=out, ws=ws)
+        dak.paged_decode_attn(qd, pkv, scale, out=pout, ws=pws)
 
     step()
     torch.cuda.synchronize()
-    ref = [y.clone() for _, _, y in mats] + [out.clone()]
+    ref = [y.clone() for _, _, y in mats] + [y.clone() for _, _, y in f8] + [out.clone(), pout.clone()]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -49,7 +62,7 @@ def test_graph_replays_match_eager_launches():
         step()
     torch.cuda.synchronize()
 
-    outs = [y for _, _, y in mats] + [out]
+    outs = [y for _, _, y in mats] + [y for _, _, y in f8] + [out, pout]
     for rep in range(4):
         for t in outs:
             t.fill_(float("nan"))

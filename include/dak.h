@@ -98,6 +98,26 @@ dak_status dak_plan_offload(const dak_op_desc* ops, size_t n_ops, double b_hbm, 
                             double x_global, uint64_t* host_units_out,
                             double* modeled_time_s_out);
 
+/* The planner's modelled time of one op with h of its units on the host.
+ * DAK paper §4.2.1 (the offload cost model; walkthrough, the offload-ratio
+ * model): T_i(h) = max(T_comp,i, (n_i - h) u_i / b_hbm, h u_i / b_host), byte
+ * counts converted to double before dividing, exactly as dak_plan_offload
+ * evaluates it.
+ *   op       as for dak_plan_offload; 0 <= h <= op->units
+ *   t_out    receives T_i(h) in seconds
+ * Errors: DAK_EINVAL on bad arguments (t_out untouched). */
+dak_status dak_op_time(const dak_op_desc* op, uint64_t h, double b_hbm, double b_host, double* t_out);
+
+/* The uniform policy the greedy planner is measured against (DAK paper
+ * §4.2.1, "The Suboptimality of Uniform Offloading"): every op offloads the
+ * same ratio x, h_i = min(n_i, ceil(x * n_i)) with x * n_i one double
+ * multiply (the rounding rule of dak_plan_offload's budget W), and the
+ * modelled time sum_i T_i(h_i) accumulated in op order.
+ * Arguments and errors as for dak_plan_offload, with x in [0, 1] in place of
+ * x_global (the uniform plan never fails once the arguments are valid). */
+dak_status dak_plan_uniform(const dak_op_desc* ops, size_t n_ops, double b_hbm, double b_host, double x,
+                            uint64_t* host_units_out, double* modeled_time_s_out);
+
 /* The per-op quantities the planner uses: a_i, b_i (as above) and whether the
  * op is memory-bound.  Any output pointer may be NULL. */
 dak_status dak_op_turning_points(const dak_op_desc* op, double b_hbm, double b_host,
@@ -337,7 +357,9 @@ dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t
  * Contents of the device arrays are checked by the kernel, which never reads
  * outside a pool: a unit with a page index outside its pool gets NaN rows;
  * an entry of unit_order outside [0, units) is skipped.  If unit_order is not
- * a permutation, the rows of the units it misses are unspecified.
+ * a permutation, the units it misses get NaN rows (every chunk record of the
+ * call is marked unwritten before the partial kernel runs), and a unit it
+ * lists twice is computed twice into the same records with the same bits.
  * All pointers 16-byte aligned. */
 typedef struct {
   const void* k_host;

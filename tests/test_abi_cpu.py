@@ -271,3 +271,40 @@ def test_binding_structs_match_the_header_layout(tmp_path):
         assert got[(cname, "sizeof")] == C.sizeof(py), cname
         for f, _ in py._fields_:
             assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_op_time_is_bit_exact_with_oracle():
+    # The library's T_i(h) (DAK §4.2.1) against the oracle's, every h of
+    # random ops, including compute-bound ones and huge byte counts.
+    from oracle import cost_model as cm
+    rng = random.Random(31)
+    for _ in range(300):
+        n = rng.randint(1, 400)
+        u = rng.choice([1, 7, 512, 1 << 20, 7 << 19, 3 << 26, (1 << 44) // 401])
+        tc = rng.choice([0.0, rng.random() * 1e-3, rng.uniform(0, 3) * n * u / 6.4e12])
+        bg, bh = rng.uniform(1e12, 8e12), rng.uniform(2e10, 5e11)
+        o = dak.Op(n, u, tc)
+        for h in sorted({0, n, rng.randint(0, n), rng.randint(0, n)}):
+            assert dak.op_time(o, h, bg, bh) == cm.unit_time(n, u, h, tc, bg, bh)
+    with pytest.raises(dak.DakError) as e:
+        dak.op_time(dak.Op(4, 10, 0.0), 5, 4.0, 1.0)
+    assert e.value.status == L.DAK_EINVAL
+
+
+def test_uniform_plan_is_bit_exact_with_oracle():
+    # The uniform baseline of DAK §4.2.1: h_i = ceil(x n_i), and the
+    # modelled time summed in op order, against the oracle.
+    rng = random.Random(32)
+    for _ in range(150):
+        ops = _rand_instance(rng)
+        bg, bh = rng.uniform(1e12, 8e12), rng.uniform(2e10, 5e11)
+        x = rng.choice([0.0, 1.0, rng.random(), rng.random() * 0.05, 0.05, 0.1, 0.3, 1 / 3, 5e-324])
+        ref_h = op.uniform_plan(ops, x)
+        ref_t = op.modeled_time(ops, ref_h, bg, bh)
+        got_h, got_t = dak.plan_uniform([dak.Op(o.units, o.unit_bytes, o.t_comp) for o in ops], bg, bh, x)
+        assert got_h == ref_h
+        assert got_t == ref_t
+    with pytest.raises(dak.DakError) as e:
+        dak.plan_uniform([dak.Op(4, 10, 0.0)], 4.0, 1.0, 1.5)
+    assert e.value.status == L.DAK_EINVAL
+

@@ -117,8 +117,18 @@ def test_attention_pointer_validation():
     with pytest.raises(dak.DakError):
         dak.splitk_decode_attn(q.cuda(), bad, 0.1)
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(dak.DakError):
+    with pytest.raises(ValueError, match="ws holds"):        # the binding's size check
         dak.splitk_decode_attn(q.cuda(), kv, 0.1, ws=small)
+    # the library's own check of the byte count it is given
+    import ctypes as C
+    from tiered_memory_offloading_amd import _lib as L
+    lib = dak.library()
+    qd = q.cuda()
+    out = torch.empty((2, 4, 128), dtype=torch.float32, device="cuda")
+    d = kv.desc()
+    st = lib.dak_splitk_decode_attn(qd.data_ptr(), C.byref(d), 4, C.c_float(0.1), out.data_ptr(), small.data_ptr(),
+                                    16, None, None)
+    assert st == L.DAK_EINVAL and b"workspace" in lib.dak_last_error()
 
 
 def test_llama70b_attention_full_size():

@@ -164,8 +164,15 @@ def test_pointer_validation_rejects_wrong_tiers():
     # host part shorter than h tile-rows
     short = torch.empty((32, 256), dtype=torch.bfloat16, pin_memory=True)
     bad = dak.SplitMatrix(short, S.hbm, 128, 256, 64, 1)
-    with pytest.raises(dak.DakError):
+    with pytest.raises(ValueError, match="A.host"):     # the binding's size check
         dak.splitk_gemm(bad, x)
+    # the library's check of the same, through the C ABI directly
+    import ctypes as C
+    from tiered_memory_offloading_amd import _lib as L
+    lib = dak.library()
+    y = torch.empty((1, 128), dtype=torch.float32, device="cuda")
+    d = bad.desc()
+    assert lib.dak_splitk_gemm(C.byref(d), x.data_ptr(), 1, y.data_ptr(), None, None) == L.DAK_EINVAL
     # activations in pageable host memory, through the C ABI directly (the
     # binding already refuses CPU tensors before calling the library)
     import ctypes as C

@@ -5,9 +5,10 @@ runs in the library's HIP kernels; this module only marshals arguments and uses
 PyTorch to allocate device and pinned host memory and to name streams.
 
 Entry points (same names as the C ABI, without the ``dak_`` prefix):
-  min_offload_ratio, plan_offload, op_turning_points, host_workgroups,
-  splitk_gemm, decode_attn_workspace_bytes, splitk_decode_attn,
-  probe_read, probe_read_concurrent.
+  min_offload_ratio, plan_offload, plan_uniform, op_time, op_turning_points,
+  host_workgroups, splitk_gemm, splitk_gemm_fp8, decode_attn_workspace_bytes,
+  splitk_decode_attn, paged_decode_attn, probe_read,
+  probe_read_concurrent, probe_mfma.
 Placement (DAK paper §4.1 "Data Partition"; §5 batch split of the KV cache):
   place_matrix, place_kv.
 """
@@ -23,10 +24,11 @@ from . import _lib as L
 
 __all__ = [
     "DakError", "LaunchConfig", "SplitMatrix", "SplitKV", "Op",
-    "min_offload_ratio", "plan_offload", "op_turning_points", "host_workgroups",
+    "min_offload_ratio", "plan_offload", "plan_uniform", "op_time", "op_turning_points", "host_workgroups",
     "place_matrix", "place_kv", "KV_UNIT_REQUEST", "KV_UNIT_HEAD", "splitk_gemm", "decode_attn_workspace_bytes",
     "SplitMatrixFP8", "place_matrix_fp8", "splitk_gemm_fp8",
-    "splitk_decode_attn", "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
+    "splitk_decode_attn",
+    "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
     "probe_read", "probe_read_concurrent", "library",
 ]
 
@@ -79,6 +81,24 @@ def plan_offload(ops: Sequence[Op], b_hbm: float, b_host: float, x_global: float
     return [int(v) for v in out], t.value
 
 
+def op_time(op: Op, h: int, b_hbm: float, b_host: float) -> float:
+    """Modelled seconds of one op with h units on the host (the planner's T_i(h))."""
+    d = L.OpDesc(op.units, op.unit_bytes, op.t_comp_s)
+    t = C.c_double()
+    _check(library().dak_op_time(C.byref(d), int(h), float(b_hbm), float(b_host), C.byref(t)))
+    return t.value
+
+
+def plan_uniform(ops: Sequence[Op], b_hbm: float, b_host: float, x: float):
+    """(host units per op at one uniform ratio x, modelled time in seconds)."""
+    lib = library()
+    arr = (L.OpDesc * len(ops))(*[L.OpDesc(o.units, o.unit_bytes, o.t_comp_s) for o in ops])
+    out = (C.c_uint64 * len(ops))()
+    t = C.c_double()
+    _check(lib.dak_plan_uniform(arr, len(ops), float(b_hbm), float(b_host), float(x), out, C.byref(t)))
+    return [int(v) for v in out], t.value
+
+
 def op_turning_points(op: Op, b_hbm: float, b_host: float):
     """(a, b, memory_bound) of one op."""
     lib = library()
@@ -120,6 +140,24 @@ def _cfg_ptr(cfg: Optional[LaunchConfig]):
     return c, C.byref(c)
 
 
+def _check_buf(t: Optional[torch.Tensor], name: str, numel: int, dtype) -> None:
+    """A descriptor's tensor must hold at least `numel` elements of `dtype`,
+    contiguously.  The library checks each pointer's tier and that the bytes
+    it needs lie inside the allocation holding the pointer; under PyTorch's
+    caching allocator that allocation is a whole pool segment, so a short view
+    would otherwise let a kernel read or write its neighbours."""
+    if numel <= 0:
+        return
+    if t is None:
+        raise ValueError(f"{name} is missing ({numel} elements needed)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+
+
 # ----------------------------------------------------------------------------
 # Placement (tile-rows and requests across the two tiers)
 # ----------------------------------------------------------------------------
@@ -142,6 +180,12 @@ class SplitMatrix:
     @property
     def host_bytes(self) -> int:
         return self.h * self.m * self.K * 2
+
+    def check(self) -> None:
+        """Both tiers hold the rows the descriptor names."""
+        rows = self.h * self.m
+        _check_buf(self.host, "A.host", rows * self.K, torch.bfloat16)
+        _check_buf(self.hbm, "A.hbm", (self.M - rows) * self.K, torch.bfloat16)
 
 
 def _pinned_like(n_rows: int, K: int) -> torch.Tensor:
@@ -203,6 +247,22 @@ class SplitKV:
         """Bytes of K and V stored on the host."""
         return 2 * self.host_units * self.ctx * self.head_dim * 2
 
+    def check(self) -> None:
+        """Both tiers hold the unit blocks the descriptor names."""
+        if self.unit not in (KV_UNIT_REQUEST, KV_UNIT_HEAD):
+            return   # the library refuses the unit code itself
+        units = self.batch * self.n_kv_heads
+        blk = self.ctx * self.head_dim
+        hu = self.host_units
+        if not 0 <= hu <= units:
+            raise ValueError(f"{hu} host units of {units}")
+        for n, t in (("k_host", self.k_host), ("v_host", self.v_host)):
+            _check_buf(t, n, hu * blk, torch.bfloat16)
+        for n, t in (("k_hbm", self.k_hbm), ("v_hbm", self.v_hbm)):
+            _check_buf(t, n, (units - hu) * blk, torch.bfloat16)
+        if self.ctx_lens is not None:
+            _check_buf(self.ctx_lens, "ctx_lens", self.batch, torch.int32)
+
 
 def place_kv(K: torch.Tensor, V: torch.Tensor, h: int, device=None, unit: int = KV_UNIT_REQUEST,
              ctx_lens: Optional[torch.Tensor] = None) -> SplitKV:
@@ -242,6 +302,9 @@ def splitk_gemm(A: SplitMatrix, x: torch.Tensor, y: Optional[torch.Tensor] = Non
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
     N = x.shape[0]
+    if x.shape[1] != A.K:
+        raise ValueError(f"x has {x.shape[1]} columns, A has K = {A.K}")
+    A.check()
     if y is None:
         y = torch.empty((N, A.M), dtype=torch.float32, device=x.device)
     if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (N, A.M):
@@ -272,6 +335,13 @@ class SplitMatrixFP8:
     @property
     def host_bytes(self) -> int:
         return self.h * self.m * self.K
+
+    def check(self) -> None:
+        """Both tiers hold the code rows the descriptor names, and every row has a scale."""
+        rows = self.h * self.m
+        _check_buf(self.host, "A.host", rows * self.K, torch.uint8)
+        _check_buf(self.hbm, "A.hbm", (self.M - rows) * self.K, torch.uint8)
+        _check_buf(self.row_scale, "A.row_scale", self.M, torch.float32)
 
 
 def place_matrix_fp8(codes: torch.Tensor, row_scale: torch.Tensor, m: int, h: int, device=None) -> SplitMatrixFP8:
@@ -308,6 +378,9 @@ def splitk_gemm_fp8(A: SplitMatrixFP8, x: torch.Tensor, y: Optional[torch.Tensor
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
     N = x.shape[0]
+    if x.shape[1] != A.K:
+        raise ValueError(f"x has {x.shape[1]} columns, A has K = {A.K}")
+    A.check()
     if y is None:
         y = torch.empty((N, A.M), dtype=torch.float32, device=x.device)
     if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (N, A.M):
@@ -323,14 +396,25 @@ def decode_attn_workspace_bytes(kv: SplitKV, n_q_heads: int) -> int:
     return int(library().dak_decode_attn_workspace_bytes(C.byref(d), int(n_q_heads)))
 
 
-def _check_attn_buffers(q: torch.Tensor, out: torch.Tensor, ws: torch.Tensor) -> None:
-    # Layout only: the library checks that each buffer is device memory of
-    # the size it needs, but it sees a base pointer, not a view's strides.
+def _check_q(q: torch.Tensor, batch: int, n_kv_heads: int, head_dim: int) -> None:
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 CUDA tensor [B, Hq, D]")
     B, Hq, D = q.shape
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
-        raise ValueError("out must be a contiguous fp32 tensor [B, Hq, D]")
-    if not ws.is_contiguous():
-        raise ValueError("ws must be contiguous")
+    if B != batch or D != head_dim or Hq % n_kv_heads:
+        raise ValueError(f"q is {tuple(q.shape)}; the KV cache needs [{batch}, a multiple of {n_kv_heads}, {head_dim}]")
+
+
+def _check_attn_buffers(q: torch.Tensor, out: torch.Tensor, ws: Optional[torch.Tensor], need: int) -> None:
+    # The library checks that each buffer lies in a device allocation of the
+    # size it needs, but it sees a base pointer, not a view's strides or size.
+    B, Hq, D = q.shape
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D) or not out.is_cuda:
+        raise ValueError("out must be a contiguous fp32 CUDA tensor [B, Hq, D]")
+    if ws is not None:
+        if not ws.is_contiguous() or not ws.is_cuda:
+            raise ValueError("ws must be a contiguous CUDA tensor")
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"ws holds {ws.numel() * ws.element_size()} bytes, {need} needed")
 
 
 def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional[torch.Tensor] = None,
@@ -338,15 +422,15 @@ def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional
                        stream=None) -> torch.Tensor:
     """out [B, Hq, D] fp32 from q bf16 [B, Hq, D] on the GPU."""
     lib = library()
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 CUDA tensor [B, Hq, D]")
+    _check_q(q, kv.batch, kv.n_kv_heads, kv.head_dim)
+    kv.check()
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     need = decode_attn_workspace_bytes(kv, Hq)
     if ws is None:
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    _check_attn_buffers(q, out, ws)
+    _check_attn_buffers(q, out, ws, need)
     d = kv.desc()
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_splitk_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
@@ -388,6 +472,30 @@ class PagedKV:
     @property
     def host_bytes(self) -> int:
         return 2 * self.host_pages * self.page * self.head_dim * 2
+
+    def check(self) -> None:
+        """Pools, page table, lengths and unit order have the shapes the
+        descriptor names (their contents are checked by the kernel)."""
+        units = self.batch * self.n_kv_heads
+        for n, t in (("k_host", self.k_host), ("v_host", self.v_host), ("k_hbm", self.k_hbm),
+                     ("v_hbm", self.v_hbm)):
+            if t is not None:
+                # the descriptor takes the pool's page count from its first dimension
+                if t.dim() != 3:
+                    raise ValueError(f"{n} must be [pages, page, head_dim]")
+                _check_buf(t, n, t.shape[0] * self.page * self.head_dim, torch.bfloat16)
+        if (self.k_host is None) != (self.v_host is None) or (self.k_hbm is None) != (self.v_hbm is None):
+            raise ValueError("K and V pools must come in pairs")
+        for a, b in ((self.k_host, self.v_host), (self.k_hbm, self.v_hbm)):
+            if a is not None and a.shape != b.shape:
+                raise ValueError("K and V pools of a tier must have equal shapes")
+        if self.page_table.dim() != 2 or self.page_table.shape[0] != units:
+            raise ValueError(f"page_table must be [{units}, max_pages]")
+        _check_buf(self.page_table, "page_table", self.page_table.numel(), torch.int32)
+        _check_buf(self.ctx_lens, "ctx_lens", self.batch, torch.int32)
+        if self.unit_order.numel() != units:
+            raise ValueError(f"unit_order must hold {units} entries")
+        _check_buf(self.unit_order, "unit_order", units, torch.int32)
 
     def desc(self) -> L.PagedKVDesc:
         def p(t):
@@ -466,15 +574,15 @@ def paged_decode_attn(q: torch.Tensor, kv: PagedKV, scale: float, out: Optional[
                       stream=None) -> torch.Tensor:
     """out [B, Hq, D] fp32 from q bf16 [B, Hq, D] over a paged split KV cache."""
     lib = library()
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 CUDA tensor [B, Hq, D]")
+    _check_q(q, kv.batch, kv.n_kv_heads, kv.head_dim)
+    kv.check()
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     need = paged_decode_attn_workspace_bytes(kv, Hq)
     if ws is None:
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    _check_attn_buffers(q, out, ws)
+    _check_attn_buffers(q, out, ws, need)
     d = kv.desc()
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_paged_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),

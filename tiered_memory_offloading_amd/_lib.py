@@ -57,6 +57,9 @@ SIGNATURES = [
     ("dak_min_offload_ratio", C.c_double, [C.c_uint64, C.c_uint64]),
     ("dak_plan_offload", C.c_int32, [C.POINTER(OpDesc), C.c_size_t, C.c_double, C.c_double, C.c_double,
                                      C.POINTER(C.c_uint64), C.POINTER(C.c_double)]),
+    ("dak_op_time", C.c_int32, [C.POINTER(OpDesc), C.c_uint64, C.c_double, C.c_double, C.POINTER(C.c_double)]),
+    ("dak_plan_uniform", C.c_int32, [C.POINTER(OpDesc), C.c_size_t, C.c_double, C.c_double, C.c_double,
+                                     C.POINTER(C.c_uint64), C.POINTER(C.c_double)]),
     ("dak_op_turning_points", C.c_int32, [C.POINTER(OpDesc), C.c_double, C.c_double, C.POINTER(C.c_uint64),
                                           C.POINTER(C.c_uint64), C.POINTER(C.c_int32)]),
     ("dak_host_workgroups", C.c_int64, [C.c_int64, C.c_int32]),

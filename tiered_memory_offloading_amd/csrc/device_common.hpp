@@ -67,10 +67,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane (the
 // LDS-DMA form of the global load).  Issued through inline assembly so that
 // the compiler adds no conservative waits for the pending LDS writes; callers
-// order them with their own vmcnt waits and barriers.
+// order them with their own vmcnt waits and barriers.  The LDS base goes in
+// as an operand bound to m0, so the compiler itself writes m0 and knows what
+// it holds afterwards; the s_nop is the wait state an m0 write needs before
+// the DMA reads it.
 __device__ __forceinline__ void dma16(const void* g, unsigned char* lds) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m) : "memory");
 }
 
 // Wait until at most N vector-memory instructions of this wave are pending.

@@ -118,6 +118,43 @@ dak_status dak_op_turning_points(const dak_op_desc* op, double b_hbm, double b_h
   return DAK_OK;
 }
 
+dak_status dak_op_time(const dak_op_desc* op, uint64_t h, double b_hbm, double b_host, double* t_out) {
+  dak::clear_error();
+  if (!op || !t_out) return dak::fail(DAK_EINVAL, "op and t_out must be non-NULL");
+  dak_status st = check_bandwidths(b_hbm, b_host);
+  if (st) return st;
+  if ((st = check_op(*op, 0))) return st;
+  if (h > op->units)
+    return dak::fail(DAK_EINVAL, "h = %llu exceeds the op's %llu units", (unsigned long long)h,
+                     (unsigned long long)op->units);
+  *t_out = unit_time(*op, h, b_hbm, b_host);
+  return DAK_OK;
+}
+
+dak_status dak_plan_uniform(const dak_op_desc* ops, size_t n_ops, double b_hbm, double b_host, double x,
+                            uint64_t* host_units_out, double* modeled_time_s_out) {
+  dak::clear_error();
+  if (!ops || n_ops == 0 || !host_units_out)
+    return dak::fail(DAK_EINVAL, "ops and host_units_out must be non-NULL and n_ops >= 1");
+  dak_status st = check_bandwidths(b_hbm, b_host);
+  if (st) return st;
+  if (!(x >= 0.0 && x <= 1.0)) return dak::fail(DAK_EINVAL, "x must lie in [0, 1]");
+  std::vector<uint64_t> h(n_ops);
+  for (size_t i = 0; i < n_ops; ++i) {
+    if ((st = check_op(ops[i], i))) return st;
+    // h = ceil(x * n): one double multiply (n < 2^53 converts exactly), then
+    // round up, the rule the greedy planner applies to its budget W.
+    const double v = std::ceil(x * static_cast<double>(ops[i].units));
+    const uint64_t hv = static_cast<uint64_t>(v);
+    h[i] = hv < ops[i].units ? hv : ops[i].units;
+  }
+  double t = 0.0;
+  for (size_t i = 0; i < n_ops; ++i) t += unit_time(ops[i], h[i], b_hbm, b_host);
+  std::memcpy(host_units_out, h.data(), n_ops * sizeof(uint64_t));
+  if (modeled_time_s_out) *modeled_time_s_out = t;
+  return DAK_OK;
+}
+
 dak_status dak_plan_offload(const dak_op_desc* ops, size_t n_ops, double b_hbm, double b_host,
                             double x_global, uint64_t* host_units_out,
                             double* modeled_time_s_out) {

@@ -507,6 +507,17 @@ __global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_w
   out[row * kD + d] = O / L;
 }
 
+// Marks the n chunk records of a paged call as unwritten (l = NaN) before the
+// partial kernel runs.  unit_order is device data the host cannot check; if
+// it misses a unit (an entry out of range, or another unit listed twice), no
+// item writes that unit's records and the combine then yields NaN rows for
+// it rather than whatever an earlier call left in the workspace.  A unit
+// listed twice is computed twice into the same records with the same bits.
+__global__ __launch_bounds__(256) void attn_mark_records(float* __restrict__ ml_ws, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ml_ws[i * 2 + 1] = __builtin_nanf("");
+}
+
 struct AttnArgs {
   const uint16_t *q, *k_host, *v_host, *k_hbm, *v_hbm;
   int64_t batch, h_units;
@@ -807,8 +818,13 @@ extern "C" dak_status dak_paged_decode_attn(const void* q, const dak_paged_kv* k
   a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   a.stream = static_cast<hipStream_t>(stream);
   if (a.host_wgs + a.hbm_items > 0x7fffffff || B * n_q_heads > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
-  launch_partial_w<PagedLaunch>(a, G, attn_window(lc.window, a.host_wgs, G), (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+  const int64_t records = B * n_q_heads * (int64_t)a.C;
+  hipLaunchKernelGGL(attn_mark_records, dim3((unsigned)((records + 255) / 256)), dim3(256), 0, a.stream, a.ml_ws,
+                     records);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip((int)e, "paged attention record marking launch");
+  launch_partial_w<PagedLaunch>(a, G, attn_window(lc.window, a.host_wgs, G), (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+  e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "paged attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
                      n_q_heads, (int64_t)kv->max_pages * kv->page, a.ctx_lens, out);

@@ -26,12 +26,12 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from fractions import Fraction
 from typing import List, Optional
 
 import torch
 
-from . import Op, SplitKV, SplitMatrix, plan_offload, min_offload_ratio, splitk_decode_attn, splitk_gemm
+from . import Op, SplitKV, SplitMatrix, op_time, plan_offload, plan_uniform, min_offload_ratio, splitk_decode_attn
+from . import splitk_gemm
 from . import KV_UNIT_HEAD, KV_UNIT_REQUEST, SplitMatrixFP8, decode_attn_workspace_bytes, splitk_gemm_fp8
 
 
@@ -124,15 +124,14 @@ class DecodeModel:
         tc = t_comp or (lambda slot: 0.0)
         self.t_comp = [float(tc(o)) for o in self.slots]
         ops = [Op(o.units, o.unit_bytes, t) for o, t in zip(self.slots, self.t_comp)]
+        self._ops = ops
         if policy == "greedy":
             # DAK §4.2.2: the greedy per-op ratios under the global budget.
             self.host_units, self.modeled_s = plan_offload(ops, b_hbm, b_host, self.x_global)
         elif policy == "uniform":
-            # Every op at the global ratio, h = ceil(x n) (the baseline the
-            # pages' greedy planner is measured against).
-            r = Fraction(repr(self.x_global))
-            self.host_units = [min(o.units, -((-r.numerator * o.units) // r.denominator)) for o in self.slots]
-            self.modeled_s = sum(self._op_time(i, h) for i, h in enumerate(self.host_units))
+            # Every op at the global ratio (the baseline the pages' greedy
+            # planner is measured against).
+            self.host_units, self.modeled_s = plan_uniform(ops, b_hbm, b_host, self.x_global)
         else:
             raise ValueError("policy must be 'greedy' or 'uniform'")
         self.policy = policy
@@ -225,11 +224,6 @@ class DecodeModel:
             if events is not None:
                 events[i][1].record()
 
-    def _op_time(self, i: int, h: int) -> float:
-        """DAK §4.2.1: T_i(h) = max(T_comp, (n - h) u / B_hbm, h u / B_host)."""
-        o = self.slots[i]
-        return max(self.t_comp[i], (o.units - h) * o.unit_bytes / self.b_hbm, h * o.unit_bytes / self.b_host)
-
     def op_model_s(self, i: int) -> float:
-        """Modelled time of op i at its planned host units."""
-        return self._op_time(i, self.slots[i].host_units)
+        """Modelled time of op i at its planned host units (the library's T_i(h))."""
+        return op_time(self._ops[i], self.slots[i].host_units, self.b_hbm, self.b_host)

@@ -327,6 +327,25 @@ dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t
                                   float scale, float* out, void* ws, size_t ws_bytes,
                                   const dak_launch_cfg* cfg, void* stream);
 
+/* dak_splitk_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, hosts that forbid hipMalloc):
+ * the same kernels, with the workspace taken from a fixed array the library
+ * holds on every device it runs on (dak_decode_attn_scratch_max_bytes()
+ * bytes, 16 MiB, kept until the process ends).  Nothing is allocated or
+ * freed by the call.  Arguments, results, determinism and errors are those of
+ * dak_splitk_decode_attn without ws/ws_bytes; in addition DAK_EINVAL when
+ * dak_decode_attn_workspace_bytes(kv, n_q_heads) exceeds the array (e.g.
+ * batch * n_q_heads * ceil(ctx / 2048) above 32263 records of 520 bytes).
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (different streams, or different host threads without
+ * ordering between their streams) race on it and their outputs are then
+ * unspecified; calls ordered on one stream are safe.  No part of the array
+ * needs clearing between calls (each call writes every record it reads). */
+dak_status dak_splitk_decode_attn_noalloc(const void* q, const dak_split_kv* kv, int32_t n_q_heads, float scale,
+                                          float* out, const dak_launch_cfg* cfg, void* stream);
+/* Size in bytes of the per-device array dak_splitk_decode_attn_noalloc uses. */
+size_t dak_decode_attn_scratch_max_bytes(void);
+
 /* A paged KV cache split between two page pools.  Paged attention keeps each
  * request's cache in fixed-size pages drawn from a free pool; BOOST §3.3 and
  * §4.3 ("Block-level KV Head Chunk Partitioning", "Wave-aware Block

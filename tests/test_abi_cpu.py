@@ -308,3 +308,20 @@ def test_uniform_plan_is_bit_exact_with_oracle():
         dak.plan_uniform([dak.Op(4, 10, 0.0)], 4.0, 1.0, 1.5)
     assert e.value.status == L.DAK_EINVAL
 
+
+def test_noalloc_attention_rejects_shapes_beyond_its_scratch_before_any_launch():
+    lib = dak.library()
+    cap = lib.dak_decode_attn_scratch_max_bytes()
+    assert cap == 16 << 20
+    # 16 requests x 64 query heads x 32768 tokens: 16 * 64 * 16 records of 520 bytes fit
+    kv = L.SplitKVDesc(None, None, None, None, 16, 0, 8, 128, 32768)
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 64) <= cap
+    # twice the batch does not
+    kv = L.SplitKVDesc(None, None, None, None, 32, 0, 8, 128, 32768)
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 64) > cap
+    st = lib.dak_splitk_decode_attn_noalloc(None, C.byref(kv), 64, C.c_float(0.1), None, None, None)
+    assert st == L.DAK_EINVAL
+    assert b"scratch" in lib.dak_last_error()
+    # the workspace entry point still refuses a NULL workspace
+    assert lib.dak_splitk_decode_attn(None, C.byref(kv), 64, C.c_float(0.1), None, None, 1 << 30, None,
+                                      None) == L.DAK_EINVAL

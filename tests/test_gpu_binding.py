@@ -72,6 +72,9 @@ def test_attention_refuses_short_q_kv_and_workspace():
     short = dak.SplitKV(kv.k_host, kv.v_host[:1], kv.k_hbm, kv.v_hbm, B, 1, Hkv, D, ctx)
     with pytest.raises(ValueError, match="v_host"):
         dak.splitk_decode_attn(qd, short, 0.1)
+    with pytest.raises(ValueError, match="q is"):
+        dak.splitk_decode_attn_noalloc(pool[: B - 1].contiguous(), kv, 0.1,
+                                       torch.empty((B - 1, Hq, D), dtype=torch.float32, device="cuda"))
     out = dak.splitk_decode_attn(qd, kv, 0.1)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()

@@ -7,7 +7,7 @@ PyTorch to allocate device and pinned host memory and to name streams.
 Entry points (same names as the C ABI, without the ``dak_`` prefix):
   min_offload_ratio, plan_offload, plan_uniform, op_time, op_turning_points,
   host_workgroups, splitk_gemm, splitk_gemm_fp8, decode_attn_workspace_bytes,
-  splitk_decode_attn, paged_decode_attn, probe_read,
+  splitk_decode_attn, splitk_decode_attn_noalloc, paged_decode_attn, probe_read,
   probe_read_concurrent, probe_mfma.
 Placement (DAK paper §4.1 "Data Partition"; §5 batch split of the KV cache):
   place_matrix, place_kv.
@@ -27,7 +27,7 @@ __all__ = [
     "min_offload_ratio", "plan_offload", "plan_uniform", "op_time", "op_turning_points", "host_workgroups",
     "place_matrix", "place_kv", "KV_UNIT_REQUEST", "KV_UNIT_HEAD", "splitk_gemm", "decode_attn_workspace_bytes",
     "SplitMatrixFP8", "place_matrix_fp8", "splitk_gemm_fp8",
-    "splitk_decode_attn",
+    "splitk_decode_attn", "splitk_decode_attn_noalloc", "decode_attn_scratch_max_bytes",
     "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
     "probe_read", "probe_read_concurrent", "library",
 ]
@@ -435,6 +435,27 @@ def splitk_decode_attn(q: torch.Tensor, kv: SplitKV, scale: float, out: Optional
     c, cp = _cfg_ptr(cfg)
     _check(lib.dak_splitk_decode_attn(q.data_ptr(), C.byref(d), Hq, C.c_float(scale), out.data_ptr(),
                                       ws.data_ptr(), ws.numel() * ws.element_size(), cp, _stream_handle(stream)))
+    return out
+
+
+def decode_attn_scratch_max_bytes() -> int:
+    """Bytes of the per-device array splitk_decode_attn_noalloc works in."""
+    return int(library().dak_decode_attn_scratch_max_bytes())
+
+
+def splitk_decode_attn_noalloc(q: torch.Tensor, kv: SplitKV, scale: float, out: torch.Tensor,
+                               cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
+    """splitk_decode_attn for callers that cannot allocate: the caller passes
+    `out`, and the workspace is the library's fixed per-device array (calls
+    that overlap on one device race on it)."""
+    lib = library()
+    _check_q(q, kv.batch, kv.n_kv_heads, kv.head_dim)
+    kv.check()
+    _check_attn_buffers(q, out, None, 0)
+    d = kv.desc()
+    c, cp = _cfg_ptr(cfg)
+    _check(lib.dak_splitk_decode_attn_noalloc(q.data_ptr(), C.byref(d), q.shape[1], C.c_float(scale),
+                                              out.data_ptr(), cp, _stream_handle(stream)))
     return out
 
 

@@ -70,6 +70,9 @@ SIGNATURES = [
     ("dak_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(SplitKVDesc), C.c_int32]),
     ("dak_splitk_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(SplitKVDesc), C.c_int32, C.c_float, C.c_void_p,
                                            C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_splitk_decode_attn_noalloc", C.c_int32, [C.c_void_p, C.POINTER(SplitKVDesc), C.c_int32, C.c_float,
+                                                   C.c_void_p, C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_decode_attn_scratch_max_bytes", C.c_size_t, []),
     ("dak_paged_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(PagedKVDesc), C.c_int32]),
     ("dak_paged_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(PagedKVDesc), C.c_int32, C.c_float, C.c_void_p,
                                           C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),

@@ -27,7 +27,9 @@
 // are bit-identical whatever the number of host requests.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "device_common.hpp"
 
@@ -649,11 +651,50 @@ extern "C" size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_
   return (size_t)(kv->batch * n_q_heads * C) * (kD + 2) * sizeof(float);
 }
 
-extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads, float scale,
-                                             float* out, void* ws, size_t ws_bytes, const dak_launch_cfg* cfg,
-                                             void* stream) {
-  using namespace dak;
-  clear_error();
+namespace dak {
+namespace {
+
+// Workspace of the entry point that allocates nothing: one array per device
+// (each GPU that loads the library holds its own copy until the process
+// ends), reached from host code only through the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current).
+dak_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip((int)e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DAK_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                                                 kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return fail_hip((int)e, "hipGetSymbolAddress(scratch)");
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DAK_OK;
+}
+
+// Split decode attention with the caller's workspace `ws` of `ws_bytes`
+// bytes, or, with use_scratch, the current device's scratch array (no
+// allocation).
+dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads, float scale, float* out, void* ws,
+                       size_t ws_bytes, bool use_scratch, const dak_launch_cfg* cfg, void* stream) {
   if (!kv) return fail(DAK_EINVAL, "kv is NULL");
   if (kv->head_dim != kD) return fail(DAK_EUNSUPPORTED, "head_dim %d (only 128 is built)", kv->head_dim);
   if (!attn_shapes_ok(kv, n_q_heads))
@@ -666,7 +707,10 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   dak_status st = resolve_cfg(cfg, kAttnDefaults, &lc);
   if (st) return st;
   const size_t need = dak_decode_attn_workspace_bytes(kv, n_q_heads);
-  if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  if (use_scratch && need > kScratchBytes)
+    return fail(DAK_EINVAL, "these shapes need %zu bytes of workspace, above the %zu-byte scratch array", need,
+                kScratchBytes);
+  if (!use_scratch && ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 
   const int64_t B = kv->batch, Hkv = kv->n_kv_heads, ctx = kv->ctx;
   const int64_t hu = host_units_of(kv), units = B * Hkv;   // host units in (request, KV head) pairs
@@ -686,7 +730,12 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   if (kv->ctx_lens && (st = check_tier_ptr(kv->ctx_lens, (uint64_t)B * 4, Tier::kDevice, "ctx_lens", &dlens)))
     return st;
   if ((st = check_tier_ptr(out, (uint64_t)B * n_q_heads * kD * 4, Tier::kDevice, "out", &dout))) return st;
-  if ((st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws))) return st;
+  if (use_scratch) {
+    if ((st = scratch_ptr(&ws))) return st;
+    dws = ws;
+  } else if ((st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws))) {
+    return st;
+  }
 
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(dq);
@@ -719,6 +768,25 @@ extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* 
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");
   return DAK_OK;
+}
+
+}  // namespace
+}  // namespace dak
+
+extern "C" dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads, float scale,
+                                             float* out, void* ws, size_t ws_bytes, const dak_launch_cfg* cfg,
+                                             void* stream) {
+  dak::clear_error();
+  return dak::decode_attn(q, kv, n_q_heads, scale, out, ws, ws_bytes, false, cfg, stream);
+}
+
+extern "C" size_t dak_decode_attn_scratch_max_bytes(void) { return dak::kScratchBytes; }
+
+extern "C" dak_status dak_splitk_decode_attn_noalloc(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
+                                                     float scale, float* out, const dak_launch_cfg* cfg,
+                                                     void* stream) {
+  dak::clear_error();
+  return dak::decode_attn(q, kv, n_q_heads, scale, out, nullptr, 0, true, cfg, stream);
 }
 
 namespace dak {

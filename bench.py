@@ -287,6 +287,79 @@ def cpu_baseline(wl, reps=5):
     }
 
 
+def cpu_baseline_llama70b(torch, model, seed=0):
+    """The oracle on a bounded sample of the 70B-shaped step: 256 seeded rows
+    of each GEMM kind (all batch columns; layers drawn at random) and two
+    seeded (request, KV head) pairs of every layer's attention (all their
+    query heads).  Each sampled op runs alone on the GPU and its output is
+    compared with the fp64 oracle on inputs read back from the placed tiers
+    (both untimed); the oracle's own time gives the rate.  Returns the
+    cpu_baseline object with the worst normwise error of each kind."""
+    import numpy as np  # noqa: F401
+    from oracle import attention as oa
+    from oracle import fp8 as of
+    from oracle import gemm as og
+
+    g = torch.Generator().manual_seed(seed)
+    s = model.shape
+    G = s.n_q_heads // s.n_kv_heads
+    by_op = {}
+    layers = s.layers
+    for kind in ("qkv", "o", "gate_up", "down"):
+        idx = [i for i, o in enumerate(model.slots) if o.kind == kind]
+        M = model.slots[idx[0]].units * model.m
+        for _ in range(256):
+            li = int(torch.randint(0, layers, (1,), generator=g))
+            by_op.setdefault(idx[li], []).append(int(torch.randint(0, M, (1,), generator=g)))
+    for i, o in enumerate(model.slots):
+        if o.kind == "attn":
+            by_op[i] = [(int(torch.randint(0, model.batch, (1,), generator=g)),
+                         int(torch.randint(0, s.n_kv_heads, (1,), generator=g))) for _ in range(2)]
+    worst, t_oracle, nbytes = {}, 0.0, 0
+    q = None
+    for i in sorted(by_op):
+        o = model.slots[i]
+        model.run_op(i)
+        torch.cuda.synchronize()
+        if o.kind == "attn":
+            out = model.out.cpu()
+            if q is None:
+                q = og.to_f64(model.q)
+            for b, kvh in by_op[i]:
+                Kb, Vb = model.kv_block(i, b, kvh)
+                t0 = time.perf_counter()
+                Kf, Vf = og.to_f64(Kb), og.to_f64(Vb)
+                refs = [oa.attend_one(q[b, j], Kf, Vf, model.scale) for j in range(kvh * G, (kvh + 1) * G)]
+                t_oracle += time.perf_counter() - t0
+                nbytes += 2 * Kb.numel() * 2
+                for j, ref in zip(range(kvh * G, (kvh + 1) * G), refs):
+                    worst["attn"] = max(worst.get("attn", 0.0), og.normwise_error(out[b, j].numpy(), ref))
+        else:
+            rows = sorted(set(by_op[i]))
+            y = model.y[o.kind].cpu()[:, rows].numpy()
+            W, sc = model.weight_rows(i, rows)
+            x = model.x[o.kind].cpu()
+            t0 = time.perf_counter()
+            ref = of.gemm_fp8(W, sc, x) if model.weights == "fp8" else og.gemm_rows(og.to_f64(W), og.to_f64(x))
+            t_oracle += time.perf_counter() - t0
+            nbytes += W.numel() * W.element_size()
+            worst[o.kind] = max(worst.get(o.kind, 0.0), og.normwise_error(y, ref))
+    n_rows = sum(len(set(v)) for i, v in by_op.items() if model.slots[i].kind != "attn")
+    n_pairs = sum(len(v) for i, v in by_op.items() if model.slots[i].kind == "attn")
+    return {
+        "value": round(nbytes / t_oracle / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"{n_rows} seeded weight rows (256 draws per GEMM kind over the {layers} layers, all "
+                   f"{model.batch} columns) and {n_pairs} seeded (request, KV head) pairs (2 per layer, "
+                   f"{G} query heads each, {model.ctx} tokens) of the planned step; fp64 numpy oracle on "
+                   f"inputs read back from the placed tiers; {nbytes / 1e9:.3f} GB of weights and KV in "
+                   f"{t_oracle:.2f} s"),
+        "seconds": round(t_oracle, 3),
+        "worst_normwise_error": {k: float(f"{v:.3e}") for k, v in worst.items()},
+        "parity_ok": max(worst.values()) <= 1e-2,
+    }
+
+
 def run_llama70b(torch, dak, args, b_hbm, b_host):
     """70B-shaped decode step (80 layers, hidden 8192, GQA 64/8, hd 128, FFN
     28672, `--b70-batch` requests (16) x 32768 tokens): the planner spreads the
@@ -345,6 +418,10 @@ def run_llama70b(torch, dak, args, b_hbm, b_host):
         "frac_of_model": round(model.modeled_s * 1e3 / ms, 4),
         "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "per_kind": per_kind,
     }
+    if not args.no_cpu_baseline:
+        log("checking sampled rows and KV pairs of the planned step against the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline_llama70b(torch, model)
+        log(f"worst normwise error per kind: {res['cpu_baseline']['worst_normwise_error']}")
     print(json.dumps(res), flush=True)
     return 0
 

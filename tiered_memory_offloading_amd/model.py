@@ -210,19 +210,55 @@ class DecodeModel:
         torch.cuda.synchronize()
 
     # ------------------------------------------------------------------
+    def run_op(self, i: int):
+        """Launch op i alone; its output lands in self.out (attention) or
+        self.y[kind] (the GEMMs), which every layer's op of that kind shares."""
+        o = self.slots[i]
+        if o.kind == "attn":
+            splitk_decode_attn(self.q, o.desc, self.scale, out=self.out, ws=self.ws)
+        elif self.weights == "fp8":
+            splitk_gemm_fp8(o.desc, self.x[o.kind], y=self.y[o.kind])
+        else:
+            splitk_gemm(o.desc, self.x[o.kind], y=self.y[o.kind])
+
     def step(self, events=None):
         """One decode step: every layer's five split operators, in order."""
-        for i, o in enumerate(self.slots):
+        for i in range(len(self.slots)):
             if events is not None:
                 events[i][0].record()
-            if o.kind == "attn":
-                splitk_decode_attn(self.q, o.desc, self.scale, out=self.out, ws=self.ws)
-            elif self.weights == "fp8":
-                splitk_gemm_fp8(o.desc, self.x[o.kind], y=self.y[o.kind])
-            else:
-                splitk_gemm(o.desc, self.x[o.kind], y=self.y[o.kind])
+            self.run_op(i)
             if events is not None:
                 events[i][1].record()
+
+    def weight_rows(self, i: int, rows):
+        """Rows `rows` of GEMM op i's logical weight matrix, read back from
+        whichever tier holds each, as a CPU tensor (bf16, or uint8 e4m3
+        codes), with the rows' fp32 scales for FP8 weights (else None)."""
+        o = self.slots[i]
+        d = o.desc
+        split = d.h * d.m
+        rows = [int(r) for r in rows]
+        idx_h = [r for r in rows if r < split]
+        idx_g = [r - split for r in rows if r >= split]
+        parts = {}
+        if idx_h:
+            parts.update(zip(idx_h, d.host[torch.tensor(idx_h)]))
+        if idx_g:
+            got = d.hbm[torch.tensor(idx_g, device=d.hbm.device)].cpu()
+            parts.update(zip([r + split for r in idx_g], got))
+        out = torch.stack([parts[r] for r in rows])
+        scale = d.row_scale[torch.tensor(rows, device=d.row_scale.device)].cpu() if self.weights == "fp8" else None
+        return out, scale
+
+    def kv_block(self, i: int, b: int, g: int):
+        """(K, V) [ctx, head_dim] bf16 of request b's KV head g in attention
+        op i, read back from whichever tier holds that unit."""
+        d = self.slots[i].desc
+        u = b * self.shape.n_kv_heads + g
+        hu = d.host_units
+        if u < hu:
+            return d.k_host[u].clone(), d.v_host[u].clone()
+        return d.k_hbm[u - hu].cpu(), d.v_hbm[u - hu].cpu()
 
     def op_model_s(self, i: int) -> float:
         """Modelled time of op i at its planned host units (the library's T_i(h))."""

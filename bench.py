@@ -878,6 +878,114 @@ def run_plan_compare(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_prefetch(torch, dak, args, b_hbm, b_host):
+    """Direct access against copy-based prefetch on the same step (DAK paper
+    §1 Fig. 1 and §2.3 Fig. 2; BOOST §2.5).  For each x the Llama-8B decode
+    layer's split operators run twice on the same placement: directly (host
+    units read in place over the link) and prefetched (the host units of each
+    op copied into a two-slot HBM staging buffer one op ahead by the DMA
+    engine, then the op run from HBM).  Beside them: the direct two-tier
+    roofline, sum_i max(x_i C_i / B_host, (1 - x_i) C_i / B_hbm), and the
+    theoretical prefetch bound with perfect overlap, sum_i max(x_i C_i /
+    B_host, (1 + x_i) C_i / B_hbm) (each prefetched byte is written into HBM
+    and read back).  Then the copy-interference probe: a 4 GiB HBM streaming
+    read alone and beside a 1 GiB host-to-HBM copy."""
+    from tiered_memory_offloading_amd.prefetch import PrefetchStep, concurrent_copy_stream
+
+    log("building the workload on the GPU")
+    wl = Workload(torch, dak, n_act=args.n_act)
+    ops = wl.op_bytes()
+    step_bytes = sum(C for _, C, _ in ops)
+
+    def op_list(plan):
+        mats, kv = plan
+        seq = []
+        for L, S in mats:
+            seq.append((S, lambda S_, cfg, L=L: dak.splitk_gemm(S_, L["x"], y=L["y"], cfg=cfg)))
+        seq.insert(1, (kv, lambda kv_, cfg: dak.splitk_decode_attn(wl.q, kv_, wl.scale, out=wl.out, ws=wl.ws,
+                                                                   cfg=cfg)))
+        return seq
+
+    def timed(fn, steps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            runs.append((time.perf_counter() - t0) / steps * 1e3)
+        return statistics.median(runs)
+
+    den = 20
+    rows = []
+    # one copy stream for every prefetcher and the probe, checked to run beside
+    # the compute stream (streams that share its hardware queue serialize)
+    side = concurrent_copy_stream()
+    for k in range(0, 11):
+        plan = wl.plan(k, den)
+        seq = op_list(plan)
+        direct_ms = timed(lambda: [fn(op, None) for op, fn in seq], args.sweep_steps)
+        pf = PrefetchStep(seq, copy_stream=side)
+        prefetch_ms = timed(pf.step, args.sweep_steps)
+        t_pf = t_da = 0.0
+        for name, C, n in ops:
+            h = host_units(k, den, n)
+            hb = h * (C // n)
+            t_pf += max(hb / (b_host * 1e9), (C + hb) / (b_hbm * 1e9))
+            t_da += max(hb / (b_host * 1e9), (C - hb) / (b_hbm * 1e9))
+        row = {"x": k / den, "direct_ms": round(direct_ms, 4), "prefetch_ms": round(prefetch_ms, 4),
+               "theory_direct_ms": round(t_da * 1e3, 4), "theory_prefetch_ms": round(t_pf * 1e3, 4),
+               "direct_GBps": round(step_bytes / (direct_ms * 1e-3) / 1e9, 2),
+               "prefetch_GBps": round(step_bytes / (prefetch_ms * 1e-3) / 1e9, 2),
+               "speedup_direct": round(prefetch_ms / direct_ms, 4),
+               "staging_bytes": pf.staging_bytes, "host_bytes": host_bytes(wl, k, den)}
+        rows.append(row)
+        log(f"x={k / den:.2f}: direct {direct_ms:.3f} ms (theory {t_da * 1e3:.3f}), prefetch {prefetch_ms:.3f} ms "
+            f"(theory {t_pf * 1e3:.3f}), staging {pf.staging_bytes / 2**20:.0f} MiB")
+        del pf
+        torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    log("copy interference: a 4 GiB HBM read alone and beside a 1 GiB host-to-HBM copy")
+    g = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    interference = []
+    for wg, w in ((1024, 2), (512, 4)):
+        alone, beside, copy_ms, n = dak.probe_copy_interference(g, wg, w, src, dst, reps=32, copy_stream=side)
+        interference.append({"workgroups": wg, "window": w, "read_alone_ms": round(alone, 4),
+                             "read_beside_copy_ms": round(beside, 4), "reads_overlapped": n,
+                             "read_GBps_alone": round(g.numel() / alone / 1e6, 1),
+                             "read_GBps_beside_copy": round(g.numel() / beside / 1e6, 1) if beside else None,
+                             "hbm_bandwidth_loss": round(1 - alone / beside, 4) if beside else None,
+                             "copy_ms": round(copy_ms, 3), "copy_GBps": round(src.numel() / copy_ms / 1e6, 2)})
+        log(f"  {wg} WGs x {w}: {interference[-1]}")
+    del g, src, dst
+    torch.cuda.empty_cache()
+
+    sp = [r["speedup_direct"] for r in rows if r["x"] > 0]
+    res = {
+        "metric": "step time of direct access vs copy-based prefetch over offload ratio x",
+        "value": round(math.exp(sum(math.log(v) for v in sp) / len(sp)), 4),
+        "unit": "geometric-mean speedup of direct access (prefetch ms / direct ms) over x = 0.05..0.5",
+        "n_gpus": 1, "steps": args.sweep_steps, "warmup": 2, "higher_is_better": True, "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "Llama-8B decode layer split operators, batch 16 (as the headline step); prefetch: "
+                               "two-slot HBM staging buffer, copies one op ahead on a second stream",
+                   "step_bytes": step_bytes},
+        "b_hbm_GBps": round(b_hbm, 1), "b_host_GBps": round(b_host, 3), "sweep": rows,
+        "copy_interference": interference,
+        "pages_context": {"gh200_speedup_over_prefetch": "up to 3x", "pcie_speedup_over_prefetch": "up to 1.8x",
+                          "gh200_local_bandwidth_loss_from_background_copy": "up to ~10 %",
+                          "pcie_gpu_local_bandwidth_loss": "4-7 %"},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -890,14 +998,15 @@ def main(argv=None):
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
     ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare",
-                                           "paged", "fp8-linears"),
+                                           "paged", "fp8-linears", "prefetch"),
                     default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
                          "at N in {1,16,64} over x = 0..0.5, cold; plan-compare: greedy per-op ratios against a "
                          "uniform ratio for one decoder layer at large batch; paged: paged against dense "
-                         "split attention; fp8-linears: the decode linears with FP8 weights (each prints its "
-                         "own JSON line)")
+                         "split attention; fp8-linears: the decode linears with FP8 weights; prefetch: direct "
+                         "access against copy-based prefetch of the host units, and the copy-interference probe "
+                         "(each prints its own JSON line)")
     ap.add_argument("--plan-batch", type=int, default=512, help="plan-compare: batch (activation rows N)")
     ap.add_argument("--plan-ctx", type=int, default=2048, help="plan-compare: tokens per request")
     ap.add_argument("--plan-x", type=float, nargs="+", default=[0.01, 0.02, 0.05],
@@ -942,6 +1051,8 @@ def main(argv=None):
         return run_paged(torch, dak, args, b_hbm, b_host)
     if args.workload == "fp8-linears":
         return run_fp8_linears(torch, dak, args, b_hbm, b_host)
+    if args.workload == "prefetch":
+        return run_prefetch(torch, dak, args, b_hbm, b_host)
     log("building the workload on the GPU")
     wl = Workload(torch, dak, n_act=args.n_act)
     ops = wl.op_bytes()

@@ -176,6 +176,18 @@ typedef struct {
 } dak_launch_cfg;
 
 #define DAK_FLAG_COUNT_BYTES 1
+/* The host part of the operand (dak_split_matrix.host, dak_split_matrix_fp8.host,
+ * or dak_split_kv.k_host and v_host) is not in pinned host memory: it is a
+ * device-memory copy of the host units, staged in HBM by a copy-based
+ * prefetcher ahead of the call (the baseline DAK paper §2.3 and Fig. 2
+ * compare against: the host bytes are copied over the link into an HBM
+ * staging buffer, then read from HBM).  Every work-group then reads device
+ * memory: the call runs as if h were 0, with the first h units taken from the
+ * staged buffer, and its result is bit-identical to the direct split.  Split
+ * GEMM with N <= 256 and dense split attention only (DAK_EUNSUPPORTED for
+ * N > 256 and for paged attention); the byte counters count every byte as
+ * HBM. */
+#define DAK_FLAG_STAGED_HOST 2
 
 /* ------------------------------------------------------------------------ */
 /* Split GEMM: y = x . A^T with A split by tile-rows across the two tiers      */
@@ -434,6 +446,28 @@ dak_status dak_probe_read_concurrent(const void* hbm, size_t hbm_bytes, int32_t 
                                      int32_t hbm_window, const void* host, size_t host_bytes,
                                      int32_t host_wgs, int32_t host_window, void* stream,
                                      float* ms_total, float* ms_hbm, float* ms_host);
+
+/* What a copy-based prefetcher's background copy costs the kernels it runs
+ * beside (DAK paper §2.3 "Limitation of Copy-Based Offloading" and Fig. 2:
+ * host-to-HBM copies write the HBM that compute kernels read; the pages
+ * measure up to about 10 % less local bandwidth on GH200 and 4-7 % on a PCIe
+ * GPU).  The streaming read of dak_probe_read over `hbm_bytes` of the device
+ * buffer `hbm` (`workgroups`, `window` as there) runs `reps` times alone on
+ * `stream`; then hipMemcpyAsync copies `copy_bytes` from pinned `host_src` to
+ * device `dev_dst` on `copy_stream` (a different stream, of the same
+ * priority) while the read runs `reps` more times on `stream`.  One untimed
+ * copy and one untimed read come first.  Synchronizes both streams.
+ * Outputs: *ms_alone, the median read alone; *ms_with_copy, the median over
+ * the reads that started after the copy started and ended before it ended
+ * (0 if none did); *copy_ms, the copy's own duration; *n_overlapped, how many
+ * reads the second median covers.  Choose copy_bytes so that the copy
+ * outlasts several reads (e.g. 1 GiB against a 4 GiB read).
+ * Errors: DAK_EINVAL for NULL outputs, sizes or counts outside the limits,
+ * pointers outside their tiers, or copy_stream == stream. */
+dak_status dak_probe_copy_interference(const void* hbm, size_t hbm_bytes, int32_t workgroups, int32_t window,
+                                       const void* host_src, void* dev_dst, size_t copy_bytes, int32_t reps,
+                                       void* stream, void* copy_stream, float* ms_alone, float* ms_with_copy,
+                                       float* copy_ms, int32_t* n_overlapped);
 
 /* Matrix-core peak probe, the compute roof of the compute-bound split GEMM
  * (DAK paper §4.2.1 prices such ops by T_comp): `workgroups` work-groups of 4

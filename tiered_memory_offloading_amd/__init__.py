@@ -29,7 +29,8 @@ __all__ = [
     "SplitMatrixFP8", "place_matrix_fp8", "splitk_gemm_fp8",
     "splitk_decode_attn", "splitk_decode_attn_noalloc", "decode_attn_scratch_max_bytes",
     "PagedKV", "place_paged_kv", "paged_decode_attn_workspace_bytes", "paged_decode_attn",
-    "probe_read", "probe_read_concurrent", "library",
+    "probe_read", "probe_read_concurrent", "probe_copy_interference", "probe_mfma", "library",
+    "FLAG_STAGED_HOST",
 ]
 
 
@@ -115,14 +116,18 @@ def host_workgroups(items: int, cap: int) -> int:
 # ----------------------------------------------------------------------------
 # Launch configuration
 # ----------------------------------------------------------------------------
+FLAG_STAGED_HOST = L.DAK_FLAG_STAGED_HOST
+
+
 @dataclass
 class LaunchConfig:
     host_cus: int = 0              # 0 = library default
     window: int = 0                # 0 = library default
     byte_counters: Optional[torch.Tensor] = None   # int64 [2] on the GPU: host, HBM bytes loaded
+    staged_host: bool = False      # the host part is a device copy staged by a prefetcher
 
     def as_c(self) -> L.LaunchCfg:
-        flags = 0
+        flags = L.DAK_FLAG_STAGED_HOST if self.staged_host else 0
         ptr = None
         if self.byte_counters is not None:
             t = self.byte_counters
@@ -632,6 +637,24 @@ def probe_mfma(workgroups: int = 1024, iters: int = 4096, reps: int = 5, stream=
     _check(lib.dak_probe_mfma(int(workgroups), int(iters), int(reps), _stream_handle(stream), C.byref(ms),
                               C.byref(tf)))
     return ms.value, tf.value
+
+
+def probe_copy_interference(hbm: torch.Tensor, workgroups: int, window: int, host_src: torch.Tensor,
+                            dev_dst: torch.Tensor, reps: int = 24, stream=None, copy_stream=None):
+    """(ms of the HBM read alone, ms beside a host-to-HBM copy of host_src into
+    dev_dst, ms of the copy, reads that overlapped the copy)."""
+    lib = library()
+    nb = host_src.numel() * host_src.element_size()
+    if dev_dst.numel() * dev_dst.element_size() < nb:
+        raise ValueError("dev_dst is smaller than host_src")
+    if copy_stream is None:
+        raise ValueError("copy_stream: the copy needs a stream of its own")
+    a, w, c, n = C.c_float(), C.c_float(), C.c_float(), C.c_int32()
+    _check(lib.dak_probe_copy_interference(hbm.data_ptr(), hbm.numel() * hbm.element_size(), int(workgroups),
+                                           int(window), host_src.data_ptr(), dev_dst.data_ptr(), nb, int(reps),
+                                           _stream_handle(stream), _stream_handle(copy_stream), C.byref(a),
+                                           C.byref(w), C.byref(c), C.byref(n)))
+    return a.value, w.value, c.value, n.value
 
 
 def probe_read_concurrent(hbm: torch.Tensor, hbm_wgs: int, hbm_window: int, host: torch.Tensor, host_wgs: int,

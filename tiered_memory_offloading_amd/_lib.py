@@ -13,6 +13,7 @@ DAK_EINFEASIBLE = -2
 DAK_EHIP = -3
 DAK_EUNSUPPORTED = -4
 DAK_FLAG_COUNT_BYTES = 1
+DAK_FLAG_STAGED_HOST = 2
 ABI_VERSION = 2
 
 
@@ -81,6 +82,10 @@ SIGNATURES = [
     ("dak_probe_read_concurrent", C.c_int32, [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
                                               C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
                                               C.POINTER(C.c_float), C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    ("dak_probe_copy_interference", C.c_int32, [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_void_p,
+                                                C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p, C.c_void_p,
+                                                C.POINTER(C.c_float), C.POINTER(C.c_float), C.POINTER(C.c_float),
+                                                C.POINTER(C.c_int32)]),
     ("dak_probe_mfma", C.c_int32, [C.c_int32, C.c_int64, C.c_int32, C.c_void_p, C.POINTER(C.c_float),
                                    C.POINTER(C.c_double)]),
 ]

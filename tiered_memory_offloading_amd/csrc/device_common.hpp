@@ -82,6 +82,16 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Base of the HBM role's row (or unit) `lrow`, counted from the first row the
+// role owns: rows [0, stage_rows) lie in `stage`, a device-memory copy of the
+// host part staged by a copy-based prefetcher (DAK_FLAG_STAGED_HOST), the
+// rest in `hbm`.  Launches without staging pass stage_rows = 0.
+template <class T>
+__device__ __forceinline__ const T* hbm_row(const T* __restrict__ stage, int64_t stage_rows,
+                                            const T* __restrict__ hbm, int64_t lrow, int64_t ld) {
+  return lrow < stage_rows ? stage + lrow * ld : hbm + (lrow - stage_rows) * ld;
+}
+
 // Host-side validation of a caller pointer covering `bytes` bytes.
 enum class Tier { kHost, kDevice };
 // Checks that [p, p + bytes) lies inside one pinned host allocation (kHost) or

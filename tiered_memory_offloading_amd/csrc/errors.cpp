@@ -50,7 +50,8 @@ dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* o
       return fail(DAK_EINVAL, "window %d is not 0, 1, 2, 4 or 8", cfg->window);
     out->window = cfg->window;
   }
-  if (cfg->flags & ~DAK_FLAG_COUNT_BYTES) return fail(DAK_EINVAL, "unknown flag bits 0x%x", cfg->flags);
+  if (cfg->flags & ~(DAK_FLAG_COUNT_BYTES | DAK_FLAG_STAGED_HOST))
+    return fail(DAK_EINVAL, "unknown flag bits 0x%x", cfg->flags);
   out->flags = cfg->flags;
   if ((cfg->flags & DAK_FLAG_COUNT_BYTES) && (!cfg->byte_counters || ((uintptr_t)cfg->byte_counters & 7)))
     return fail(DAK_EINVAL, "DAK_FLAG_COUNT_BYTES needs an 8-byte aligned byte_counters pointer");

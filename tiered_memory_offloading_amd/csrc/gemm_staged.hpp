@@ -12,6 +12,8 @@ struct StagedArgs {
   const uint16_t* a_host;
   const uint16_t* a_hbm;
   int64_t M, K, host_rows;
+  const uint16_t* a_stage;   // staged copy of the host rows (DAK_FLAG_STAGED_HOST), else unused
+  int64_t stage_rows;        // rows of the HBM role taken from a_stage (0 without staging)
   const uint16_t* x;
   int64_t N;
   float* y;

@@ -152,6 +152,113 @@ struct Events {
 }  // namespace
 }  // namespace dak
 
+namespace dak {
+namespace {
+
+// Events destroyed with their owner.
+struct EventList {
+  std::vector<hipEvent_t> ev;
+  ~EventList() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  hipError_t make(size_t n) {
+    ev.assign(n, nullptr);
+    for (auto& e : ev) {
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+};
+
+}  // namespace
+}  // namespace dak
+
+extern "C" dak_status dak_probe_copy_interference(const void* hbm, size_t hbm_bytes, int32_t workgroups,
+                                                  int32_t window, const void* host_src, void* dev_dst,
+                                                  size_t copy_bytes, int32_t reps, void* stream, void* copy_stream,
+                                                  float* ms_alone, float* ms_with_copy, float* copy_ms,
+                                                  int32_t* n_overlapped) {
+  using namespace dak;
+  clear_error();
+  if (!ms_alone || !ms_with_copy || !copy_ms || !n_overlapped) return fail(DAK_EINVAL, "an output pointer is NULL");
+  if (hbm_bytes < 16 || (hbm_bytes & 15)) return fail(DAK_EINVAL, "hbm_bytes must be a positive multiple of 16");
+  if (copy_bytes < 1) return fail(DAK_EINVAL, "copy_bytes must be positive");
+  if (workgroups < 1 || workgroups > 65536) return fail(DAK_EINVAL, "workgroups outside [1, 65536]");
+  if (!window_ok(window)) return fail(DAK_EINVAL, "window must be 1, 2, 4, 8 or 16");
+  if (reps < 1 || reps > 4096) return fail(DAK_EINVAL, "reps outside [1, 4096]");
+  if (stream == copy_stream) return fail(DAK_EINVAL, "the copy needs a stream of its own");
+  const void *dg = nullptr, *dh = nullptr, *dd = nullptr;
+  dak_status st;
+  if ((st = check_tier_ptr(hbm, hbm_bytes, Tier::kDevice, "hbm", &dg))) return st;
+  if ((st = check_tier_ptr(host_src, copy_bytes, Tier::kHost, "host_src", &dh))) return st;
+  if ((st = check_tier_ptr(dev_dst, copy_bytes, Tier::kDevice, "dev_dst", &dd))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+  const size_t n16 = hbm_bytes / 16;
+  // Events: [0, 2 reps) the reads alone, [2 reps, 4 reps) the reads beside the
+  // copy, then the copy's start and end.
+  EventList el;
+  hipError_t e = el.make(4 * (size_t)reps + 2);
+  if (e != hipSuccess) return fail_hip((int)e, "hipEventCreate");
+  std::vector<hipEvent_t>& ev = el.ev;
+  // Warm-up of both: the first copy out of a freshly pinned buffer spends
+  // tens of ms in the host runtime before it is queued (measured: 170 ms for
+  // 256 MiB), which would leave the reads nothing to overlap.
+  if ((e = hipMemcpyAsync(dev_dst, host_src, copy_bytes, hipMemcpyHostToDevice, cs)) != hipSuccess)
+    return fail_hip((int)e, "hipMemcpyAsync");
+  if ((e = hipStreamSynchronize(cs)) != hipSuccess) return fail_hip((int)e, "hipStreamSynchronize");
+  launch_read(window, workgroups, dg, n16, s);
+  if ((e = hipGetLastError()) != hipSuccess) return fail_hip((int)e, "probe launch");
+  for (int r = 0; r < reps; ++r) {
+    if ((e = hipEventRecord(ev[2 * r], s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+    launch_read(window, workgroups, dg, n16, s);
+    if ((e = hipGetLastError()) != hipSuccess) return fail_hip((int)e, "probe launch");
+    if ((e = hipEventRecord(ev[2 * r + 1], s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail_hip((int)e, "hipStreamSynchronize");
+  // The copy on its own stream, then the same reads on the probe stream.
+  hipEvent_t c0 = ev[4 * (size_t)reps], c1 = ev[4 * (size_t)reps + 1];
+  if ((e = hipEventRecord(c0, cs)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+  if ((e = hipMemcpyAsync(dev_dst, host_src, copy_bytes, hipMemcpyHostToDevice, cs)) != hipSuccess)
+    return fail_hip((int)e, "hipMemcpyAsync");
+  if ((e = hipEventRecord(c1, cs)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+  for (int r = 0; r < reps; ++r) {
+    if ((e = hipEventRecord(ev[2 * (reps + r)], s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+    launch_read(window, workgroups, dg, n16, s);
+    if ((e = hipGetLastError()) != hipSuccess) return fail_hip((int)e, "probe launch");
+    if ((e = hipEventRecord(ev[2 * (reps + r) + 1], s)) != hipSuccess) return fail_hip((int)e, "hipEventRecord");
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail_hip((int)e, "hipStreamSynchronize");
+  if ((e = hipStreamSynchronize(cs)) != hipSuccess) return fail_hip((int)e, "hipStreamSynchronize");
+  std::vector<float> alone, beside;
+  for (int r = 0; r < reps; ++r) {
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1])) != hipSuccess)
+      return fail_hip((int)e, "hipEventElapsedTime");
+    alone.push_back(ms);
+  }
+  // Only reads that began after the copy began and ended before it ended.
+  for (int r = 0; r < reps; ++r) {
+    float ms = 0.f, after_start = 0.f, before_end = 0.f;
+    hipEvent_t a = ev[2 * (reps + r)], b = ev[2 * (reps + r) + 1];
+    if ((e = hipEventElapsedTime(&ms, a, b)) != hipSuccess ||
+        (e = hipEventElapsedTime(&after_start, c0, a)) != hipSuccess ||
+        (e = hipEventElapsedTime(&before_end, b, c1)) != hipSuccess)
+      return fail_hip((int)e, "hipEventElapsedTime");
+    if (after_start > 0.f && before_end > 0.f) beside.push_back(ms);
+  }
+  float cms = 0.f;
+  if ((e = hipEventElapsedTime(&cms, c0, c1)) != hipSuccess) return fail_hip((int)e, "hipEventElapsedTime");
+  std::sort(alone.begin(), alone.end());
+  std::sort(beside.begin(), beside.end());
+  *ms_alone = alone[alone.size() / 2];
+  *ms_with_copy = beside.empty() ? 0.f : beside[beside.size() / 2];
+  *copy_ms = cms;
+  *n_overlapped = (int32_t)beside.size();
+  return DAK_OK;
+}
+
 extern "C" dak_status dak_probe_read(const void* buf, size_t bytes, int32_t workgroups, int32_t window, int32_t reps,
                                      void* stream, float* ms_out) {
   using namespace dak;

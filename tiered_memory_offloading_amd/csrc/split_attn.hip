@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_host, const uint16_t* __restrict__ v_host,
     const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t h_units, int Hkv, int Hq,
     int64_t ctx, int C, const int32_t* __restrict__ ctx_lens, float qscale, float* __restrict__ o_ws,
-    float* __restrict__ ml_ws, int host_wgs, int64_t host_items, int64_t hbm_items,
+    float* __restrict__ ml_ws, int host_wgs, int64_t host_items, int64_t hbm_items, int64_t stage_units,
     unsigned long long* __restrict__ counters) {
   __shared__ float red_o[kAttnWaves * G * kD];
   __shared__ float red_ml[kAttnWaves * G * 2];
@@ -367,7 +367,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
       const int64_t gu = h_units + u;
       const int64_t b = gu / Hkv, len = valid_len(ctx_lens, b, ctx);
       if ((int64_t)c * kChunk < len) {
-        const DenseRows rows{k_hbm + u * ctx * kD, v_hbm + u * ctx * kD};
+        // units [0, stage_units) of the HBM role come from a staged copy of
+        // the host units (DAK_FLAG_STAGED_HOST), passed as k_host / v_host
+        const DenseRows rows{hbm_row(k_host, stage_units, k_hbm, u, ctx * kD),
+                             hbm_row(v_host, stage_units, v_hbm, u, ctx * kD)};
         attn_item<G, UG, COUNT>(q, rows, false, b, (int)(gu % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o,
                                 red_ml, wave, lane, nbytes);
       }
@@ -531,6 +534,7 @@ struct AttnArgs {
   float *o_ws, *ml_ws, *out;
   int host_wgs;
   int64_t host_items, hbm_items;
+  int64_t stage_units;   // HBM-role units read from the staged copy in k_host / v_host
   unsigned long long* counters;
   hipStream_t stream;
 };
@@ -570,7 +574,8 @@ struct DenseLaunch {
     const int64_t grid = a.host_wgs + a.hbm_items;
     hipLaunchKernelGGL((attn_partial_split<G, Un::kH, Un::kG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64),
                        0, a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_units, a.Hkv, a.Hq, a.ctx, a.C,
-                       a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.counters);
+                       a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.stage_units,
+                       a.counters);
   }
 };
 
@@ -715,12 +720,16 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   const int64_t B = kv->batch, Hkv = kv->n_kv_heads, ctx = kv->ctx;
   const int64_t hu = host_units_of(kv), units = B * Hkv;   // host units in (request, KV head) pairs
   const uint64_t per_unit = (uint64_t)ctx * kD * 2;
+  // Copy-based prefetch baseline: the host units were staged in HBM by the
+  // caller, and every work-group reads device memory.
+  const bool stage = (lc.flags & DAK_FLAG_STAGED_HOST) != 0;
+  const Tier host_tier = stage ? Tier::kDevice : Tier::kHost;
   const void *dq = nullptr, *dkh = nullptr, *dvh = nullptr, *dkg = nullptr, *dvg = nullptr, *dout = nullptr,
              *dws = nullptr;
   if ((st = check_tier_ptr(q, (uint64_t)B * n_q_heads * kD * 2, Tier::kDevice, "q", &dq))) return st;
   if (hu > 0) {
-    if ((st = check_tier_ptr(kv->k_host, per_unit * hu, Tier::kHost, "k_host", &dkh))) return st;
-    if ((st = check_tier_ptr(kv->v_host, per_unit * hu, Tier::kHost, "v_host", &dvh))) return st;
+    if ((st = check_tier_ptr(kv->k_host, per_unit * hu, host_tier, "k_host", &dkh))) return st;
+    if ((st = check_tier_ptr(kv->v_host, per_unit * hu, host_tier, "v_host", &dvh))) return st;
   }
   if (hu < units) {
     if ((st = check_tier_ptr(kv->k_hbm, per_unit * (units - hu), Tier::kDevice, "k_hbm", &dkg))) return st;
@@ -744,7 +753,8 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   a.k_hbm = static_cast<const uint16_t*>(dkg);
   a.v_hbm = static_cast<const uint16_t*>(dvg);
   a.batch = B;
-  a.h_units = hu;
+  a.h_units = stage ? 0 : hu;
+  a.stage_units = stage ? hu : 0;
   a.ctx_lens = static_cast<const int32_t*>(dlens);
   a.Hkv = (int)Hkv;
   a.Hq = n_q_heads;
@@ -754,8 +764,8 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   a.o_ws = static_cast<float*>(ws);
   a.ml_ws = a.o_ws + (size_t)B * n_q_heads * a.C * kD;
   a.out = out;
-  a.host_items = hu * a.C;
-  a.hbm_items = (units - hu) * a.C;
+  a.host_items = a.h_units * a.C;
+  a.hbm_items = (units - a.h_units) * a.C;
   a.host_wgs = (int)host_workgroups(a.host_items, lc.host_cus);
   a.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   a.stream = static_cast<hipStream_t>(stream);
@@ -836,6 +846,7 @@ extern "C" dak_status dak_paged_decode_attn(const void* q, const dak_paged_kv* k
   LaunchCfg lc;
   dak_status st = resolve_cfg(cfg, kAttnDefaults, &lc);
   if (st) return st;
+  if (lc.flags & DAK_FLAG_STAGED_HOST) return fail(DAK_EUNSUPPORTED, "paged attention takes no staged host part");
   const size_t need = dak_paged_decode_attn_workspace_bytes(kv, n_q_heads);
   if (ws_bytes < need) return fail(DAK_EINVAL, "workspace of %zu bytes < %zu needed", ws_bytes, need);
 

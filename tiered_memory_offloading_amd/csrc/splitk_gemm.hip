@@ -117,8 +117,9 @@ __device__ __forceinline__ void fma_store(float (&acc)[kRW][N], float* __restric
 template <int N, int UH, int UG, bool COUNT>
 __global__ __launch_bounds__(kThreads) void gemm_fma_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const uint16_t* __restrict__ x, float* __restrict__ y, int host_wgs,
-    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+    int64_t host_rows, const uint16_t* __restrict__ a_stage, int64_t stage_rows, const uint16_t* __restrict__ x,
+    float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fma_split(
     if (it < hbm_items) {
       const int64_t lrow = it * kFmaItemRows + wave * kRW;
       float acc[kRW][N] = {};
-      fma_rows<N, UG, COUNT>(a_hbm + lrow * K, K, x, acc, lane, nbytes);
+      fma_rows<N, UG, COUNT>(hbm_row(a_stage, stage_rows, a_hbm, lrow, K), K, x, acc, lane, nbytes);
       fma_store<N>(acc, y, M, host_rows + lrow, lane);
     }
   }
@@ -315,8 +316,9 @@ constexpr int mfma_lds_bytes() {
 template <int NB, int RBW, int S, int UH, int UG, bool COUNT>
 __global__ __launch_bounds__(64 * S) void gemm_mfma_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
-    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+    int64_t host_rows, const uint16_t* __restrict__ a_stage, int64_t stage_rows, const uint16_t* __restrict__ x,
+    int64_t N, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[mfma_lds_bytes<NB, RBW, S>()];
   f32x4_t* part = reinterpret_cast<f32x4_t*>(lds);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -344,7 +346,8 @@ __global__ __launch_bounds__(64 * S) void gemm_mfma_split(
       for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      mfma_rows_direct<NB, RBW, UG, COUNT>(a_hbm + lrow * K, K, sb, se, x, N, acc, lane, nbytes);
+      mfma_rows_direct<NB, RBW, UG, COUNT>(hbm_row(a_stage, stage_rows, a_hbm, lrow, K), K, sb, se, x, N, acc, lane,
+                                           nbytes);
       mfma_reduce_store<NB, RBW, S>(acc, part, y, M, N, host_rows + lrow, wave, lane);
     }
   }
@@ -363,6 +366,8 @@ struct GemmArgs {
   const uint16_t* a_host;
   const uint16_t* a_hbm;
   int64_t M, K, host_rows;
+  const uint16_t* a_stage;   // staged copy of the host rows (DAK_FLAG_STAGED_HOST), else unused
+  int64_t stage_rows;        // rows of the HBM role taken from a_stage (0 without staging)
   const uint16_t* x;
   int64_t N;
   float* y;
@@ -377,8 +382,8 @@ void launch_fma_n(const GemmArgs& g) {
   constexpr int UG = 4;
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_fma_split<N, UH, UG, COUNT>), dim3((unsigned)grid), dim3(kThreads), 0, g.stream,
-                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.y, g.host_wgs, g.host_items, g.hbm_items,
-                     g.counters);
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.y, g.host_wgs,
+                     g.host_items, g.hbm_items, g.counters);
 }
 
 template <int UH, bool COUNT>
@@ -405,8 +410,8 @@ void launch_mfma_nb(const GemmArgs& g) {
   constexpr int S = kMfmaSlices;
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_mfma_split<NB, RBW, S, UHc, UG, COUNT>), dim3((unsigned)grid), dim3(64 * S), 0,
-                     g.stream, g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items,
-                     g.hbm_items, g.counters);
+                     g.stream, g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.N, g.y,
+                     g.host_wgs, g.host_items, g.hbm_items, g.counters);
 }
 
 template <int UH, bool COUNT>
@@ -474,11 +479,17 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   if (st) return st;
 
   const int64_t host_rows = h * m;
+  // Copy-based prefetch baseline: the host rows were staged in HBM by the
+  // caller, and every work-group reads device memory.
+  const bool stage = (lc.flags & DAK_FLAG_STAGED_HOST) != 0;
+  if (stage && tiled) return fail(DAK_EUNSUPPORTED, "a staged host part is supported for N <= 256 only");
   const void* dh = nullptr;
   const void* dg = nullptr;
   const void* dx = nullptr;
   const void* dy = nullptr;
-  if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K * 2, Tier::kHost, "A.host", &dh))) return st;
+  if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K * 2, stage ? Tier::kDevice : Tier::kHost,
+                                            "A.host", &dh)))
+    return st;
   if (host_rows < M && (st = check_tier_ptr(A->hbm, (uint64_t)(M - host_rows) * K * 2, Tier::kDevice, "A.hbm", &dg)))
     return st;
   if ((st = check_tier_ptr(x, (uint64_t)N * K * 2, Tier::kDevice, "x", &dx))) return st;
@@ -520,8 +531,11 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     t.y = y;
     const int rbw = staged_rbw;
     const int64_t item_rows = 16 * rbw;
-    t.host_items = host_rows / item_rows;
-    t.hbm_items = (M - host_rows) / item_rows;
+    t.a_stage = stage ? t.a_host : nullptr;
+    t.stage_rows = stage ? host_rows : 0;
+    if (stage) t.host_rows = 0;
+    t.host_items = t.host_rows / item_rows;
+    t.hbm_items = (M - t.host_rows) / item_rows;
     t.host_wgs = (int)gemm_host_workgroups(t.host_items, lc, staged_host_inflight(N, rbw));
     if ((st = device_cus(&t.cus))) return st;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
@@ -555,12 +569,14 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
   g.a_hbm = static_cast<const uint16_t*>(dg);
   g.M = M;
   g.K = K;
-  g.host_rows = host_rows;
+  g.host_rows = stage ? 0 : host_rows;
+  g.a_stage = stage ? g.a_host : nullptr;
+  g.stage_rows = stage ? host_rows : 0;
   g.x = static_cast<const uint16_t*>(dx);
   g.N = N;
   g.y = y;
-  g.host_items = host_rows / host_item_rows;
-  g.hbm_items = (M - host_rows) / hbm_item_rows;
+  g.host_items = g.host_rows / host_item_rows;
+  g.hbm_items = (M - g.host_rows) / hbm_item_rows;
   // Least bytes a host work-group keeps in flight: one step of 4 waves x 4 rows
   // x 1 KiB (FMA path, window 1) or one 256-k chunk of 16 rows (MFMA path).
   g.host_wgs = (int)gemm_host_workgroups(g.host_items, lc, fma ? (16u << 10) : (8u << 10));

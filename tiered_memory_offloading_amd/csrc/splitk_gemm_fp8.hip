@@ -158,7 +158,8 @@ struct F8Item {
 template <int NB, int RB, int XR, int STAGES, bool COUNT>
 __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
     const unsigned char* __restrict__ a_host, const unsigned char* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const float* __restrict__ row_scale, const uint16_t* __restrict__ x, int64_t N,
+    int64_t host_rows, const unsigned char* __restrict__ a_stage, int64_t stage_rows,
+    const float* __restrict__ row_scale, const uint16_t* __restrict__ x, int64_t N,
     float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
     unsigned long long* __restrict__ counters) {
   using S = F8Shape<NB, RB, XR>;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
   const int64_t stride = host_role ? host_wgs : items;   // HBM work-groups take one item
   for (; it < items; it += stride) {
     const int64_t lrow = it * S::R;
-    const unsigned char* a = (host_role ? a_host : a_hbm) + lrow * K;
+    const unsigned char* a = host_role ? a_host + lrow * K : hbm_row(a_stage, stage_rows, a_hbm, lrow, K);
     const int64_t yrow = host_role ? lrow : host_rows + lrow;
     f32x4_t acc[NB];
 #pragma unroll
@@ -260,6 +261,8 @@ __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
 struct F8Args {
   const unsigned char *a_host, *a_hbm;
   int64_t M, K, host_rows;
+  const unsigned char* a_stage;   // staged copy of the host rows (DAK_FLAG_STAGED_HOST), else unused
+  int64_t stage_rows;             // rows of the HBM role taken from a_stage (0 without staging)
   const float* row_scale;
   const uint16_t* x;
   int64_t N;
@@ -276,8 +279,8 @@ void launch_f8_nb_rb_st(const F8Args& g) {
   static_assert(ST * F8Shape<NB, RB, XR>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_fp8_split<NB, RB, XR, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
-                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.row_scale, g.x, g.N, g.y, g.host_wgs, g.host_items,
-                     g.hbm_items, g.counters);
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.row_scale, g.x, g.N, g.y,
+                     g.host_wgs, g.host_items, g.hbm_items, g.counters);
 }
 
 // Three slots where two is the default (they need the whole CU), when there
@@ -368,8 +371,11 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
   if (st) return st;
 
   const int64_t host_rows = h * m;
+  const bool stage = (lc.flags & DAK_FLAG_STAGED_HOST) != 0;   // host rows staged in HBM by the caller
   const void *dh = nullptr, *dg = nullptr, *ds = nullptr, *dx = nullptr, *dy = nullptr;
-  if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K, Tier::kHost, "A.host", &dh))) return st;
+  if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K, stage ? Tier::kDevice : Tier::kHost,
+                                            "A.host", &dh)))
+    return st;
   if (host_rows < M && (st = check_tier_ptr(A->hbm, (uint64_t)(M - host_rows) * K, Tier::kDevice, "A.hbm", &dg)))
     return st;
   if ((st = check_tier_ptr(A->row_scale, (uint64_t)M * 4, Tier::kDevice, "A.row_scale", &ds))) return st;
@@ -381,14 +387,16 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
   g.a_hbm = static_cast<const unsigned char*>(dg);
   g.M = M;
   g.K = K;
-  g.host_rows = host_rows;
+  g.host_rows = stage ? 0 : host_rows;
+  g.a_stage = stage ? g.a_host : nullptr;
+  g.stage_rows = stage ? host_rows : 0;
   g.row_scale = static_cast<const float*>(ds);
   g.x = static_cast<const uint16_t*>(dx);
   g.N = N;
   g.y = y;
   const int64_t item_rows = 16 * rb;
-  g.host_items = host_rows / item_rows;
-  g.hbm_items = (M - host_rows) / item_rows;
+  g.host_items = g.host_rows / item_rows;
+  g.hbm_items = (M - g.host_rows) / item_rows;
   g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
   if ((st = device_cus(&g.cus))) return st;
   g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);

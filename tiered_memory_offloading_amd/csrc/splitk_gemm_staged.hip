@@ -117,8 +117,9 @@ struct StagedItem {
 template <int NB, int RB, int STAGES, bool COUNT>
 __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int host_wgs,
-    int64_t host_items, int64_t hbm_items, unsigned long long* __restrict__ counters) {
+    int64_t host_rows, const uint16_t* __restrict__ a_stage, int64_t stage_rows, const uint16_t* __restrict__ x,
+    int64_t N, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
   using S = StagedShape<NB, RB>;
   using I = StagedItem<NB, RB, COUNT>;
   // One array per slot: the slot a wave reads is then a different object from
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
   const int64_t stride = host_role ? host_wgs : items;   // HBM work-groups take one item
   for (; it < items; it += stride) {
     const int64_t lrow = it * S::R;
-    const uint16_t* a = (host_role ? a_host : a_hbm) + lrow * K;
+    const uint16_t* a = host_role ? a_host + lrow * K : hbm_row(a_stage, stage_rows, a_hbm, lrow, K);
     const int64_t yrow = host_role ? lrow : host_rows + lrow;
     f32x4_t acc[NB];
 #pragma unroll
@@ -243,8 +244,8 @@ template <int NB, int RB, int ST, bool COUNT>
 void launch_nb_rb_st(const StagedArgs& g) {
   const int64_t grid = g.host_wgs + g.hbm_items;
   hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
-                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.host_wgs, g.host_items, g.hbm_items,
-                     g.counters);
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.N, g.y, g.host_wgs,
+                     g.host_items, g.hbm_items, g.counters);
 }
 
 template <int NB, int RB, bool COUNT>

@@ -232,6 +232,17 @@ def time_steps(torch, wl, plan, steps, warmup, per_op=True, only=None, graph=Tru
 
     ms = timed(lambda: run_step(wl, plan, only=only))
     graph_ms = timed(g.replay) if g is not None else None
+    # per-step spread, from a separate pass with an event pair around each step
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in sev:
+        e0.record()
+        run_step(wl, plan, only=only)
+        e1.record()
+    torch.cuda.synchronize()
+    st = sorted(e0.elapsed_time(e1) for e0, e1 in sev)
+    pct = lambda p: st[min(len(st) - 1, int(round(p * (len(st) - 1))))]
+    time_steps.spread = {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4), "p90": round(pct(0.9), 4),
+                         "steps": len(st)}
     op_ms = None
     if per_op:
         evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
@@ -260,31 +271,162 @@ def cpu_baseline(wl, reps=5):
     lin = [(L["A_dev"].cpu(), L["x"].cpu()) for L in wl.lin]
     q, K, V = wl.q.cpu(), wl.K_dev.cpu(), wl.V_dev.cpu()
     t_copy = time.perf_counter() - t0
-    runs = []
-    for _ in range(reps):
-        t1 = time.perf_counter()
-        for A, X in lin:
-            og.gemm(og.to_f64(A), og.to_f64(X))
-        t_lin = time.perf_counter() - t1
-        t2 = time.perf_counter()
-        for b in range(BATCH):
-            oa.decode_attention(og.to_f64(q[b:b + 1]), og.to_f64(K[b:b + 1]), og.to_f64(V[b:b + 1]), wl.scale)
-        t_att = time.perf_counter() - t2
-        runs.append((t_lin + t_att, t_lin, t_att))
-    runs.sort()
-    t_step, t_lin, t_att = runs[len(runs) // 2]
+
+    def step_runs(n):
+        runs = []
+        for _ in range(n):
+            t1 = time.perf_counter()
+            for A, X in lin:
+                og.gemm(og.to_f64(A), og.to_f64(X))
+            t_lin = time.perf_counter() - t1
+            t2 = time.perf_counter()
+            for b in range(BATCH):
+                oa.decode_attention(og.to_f64(q[b:b + 1]), og.to_f64(K[b:b + 1]), og.to_f64(V[b:b + 1]), wl.scale)
+            t_att = time.perf_counter() - t2
+            runs.append((t_lin + t_att, t_lin, t_att))
+        runs.sort()
+        return runs[len(runs) // 2]
+
+    t_step, t_lin, t_att = step_runs(reps)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = step_runs(1)
+    except ImportError:
+        pass
     step_bytes = sum(C for _, C, _ in wl.op_bytes())
-    return {
+    res = {
         "value": round(step_bytes / t_step / 1e9, 4),
         "unit": "GB/s",
         "cores": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model_name(),
         "kind": "oracle",
         "sample": (f"the whole step, median of {reps} runs: fp64 numpy oracle of the four split GEMMs at N=16 "
                    f"({t_lin:.2f} s) and of the split-KV attention over 16 requests x 32 query heads x 32768 tokens "
                    f"({t_att:.2f} s), on the same inputs as the GPU step (copied to the host first, {t_copy:.1f} s, "
-                   f"untimed)"),
+                   f"untimed); BLAS on every core the process may use"),
         "seconds_per_step": round(t_step, 3),
     }
+    if one is not None:
+        res["single_thread"] = {"value": round(step_bytes / one[0] / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "seconds_per_step": round(one[0], 3), "gemm_s": round(one[1], 3),
+                                "attention_s": round(one[2], 3), "what": "the same step once, BLAS held to 1 thread"}
+    return res
+
+
+def _cold_timer(torch, dak, reps):
+    """Mean ms per launch over `reps` rotations through every descriptor
+    (each a different HBM copy), after one untimed rotation."""
+    def timed(descs, x, y):
+        for S in descs:
+            dak.splitk_gemm(S, x, y=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for S in descs:
+                dak.splitk_gemm(S, x, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(descs))
+    return timed
+
+
+def headline_extras(torch, dak, b_hbm, b_host, warm_seconds=1.5, reps=3):
+    """Compact numbers from the other configurations, for the headline line:
+    the 1024x1024 GEMV (N = 1) cold at x = 0 and 1/4 against its two-tier
+    roofline; the x = 0 fraction of B_hbm of each Llama-8B decode linear at
+    N in {1, 16, 64}, cold (at least 1 GiB of HBM copies in rotation); and the
+    28672x8192x2048 prefill GEMM's MFMA rate at x = 0 and at the planner's
+    turning point, against the 2.5 PFLOP/s spec and the library's MFMA
+    probe."""
+    timed = _cold_timer(torch, dak, reps)
+    out = {}
+    rows = {}
+    ops = [("gemv_1024x1024", 1024, 1024)] + list(synth.LLAMA8B_LINEARS)
+    for oi, (name, M, K) in enumerate(ops):
+        n = M // M_TILE
+        C = M * K * 2
+        copies = max(2, -(-(1 << 30) // C))
+        A = synth.gemm_inputs(M, K, 1, seed=oi, device="cuda")[0]
+        As = [A] + [A.clone() for _ in range(copies - 1)]
+        if name == "gemv_1024x1024":
+            h = host_units(1, 4, n)
+            A_host = torch.empty((h * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+            A_host.copy_(A[:h * M_TILE])
+            X = synth.gemm_inputs(M, K, 1, seed=oi, device="cuda")[1].contiguous()
+            y = torch.empty((1, M), dtype=torch.float32, device="cuda")
+            t0 = timed([dak.SplitMatrix(None, a, M, K, M_TILE, 0) for a in As], X, y)
+            t1 = timed([dak.SplitMatrix(A_host, a[h * M_TILE:], M, K, M_TILE, h) for a in As], X, y)
+            roof = max((n - h) * (C // n) / (b_hbm * 1e9), h * (C // n) / (b_host * 1e9)) * 1e3
+            out["gemv_1024x1024_cold"] = {"x0_us": round(t0 * 1e3, 2), "x025_us": round(t1 * 1e3, 2),
+                                          "x025_frac_two_tier": round(roof / t1, 4),
+                                          "x0_frac_b_hbm": round(C / (b_hbm * 1e9) * 1e3 / t0, 4)}
+            del A_host
+        else:
+            for N in (1, 16, 64):
+                X = synth.gemm_inputs(M, K, N, seed=oi, device="cuda")[1].contiguous()
+                y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+                t = timed([dak.SplitMatrix(None, a, M, K, M_TILE, 0) for a in As], X, y)
+                rows[f"{name}_N{N}"] = round(C / (b_hbm * 1e9) * 1e3 / t, 4)
+                del X, y
+        del A, As
+        torch.cuda.empty_cache()
+    out["linears_x0_frac_b_hbm_cold"] = rows
+
+    M, K, N = 28672, 8192, 2048
+    n = M // M_TILE
+    flops = 2 * M * K * N
+    A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
+    y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    S0 = dak.SplitMatrix(None, A, M, K, M_TILE, 0)
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            dak.splitk_gemm(S0, X, y=y)
+        torch.cuda.synchronize()
+
+    def med(S, k=7):
+        ts = []
+        for _ in range(k):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dak.splitk_gemm(S, X, y=y)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    t0 = med(S0)
+    _, b, _ = dak.op_turning_points(dak.Op(n, (M * K * 2) // n, t0 * 1e-3), b_hbm * 1e9, b_host * 1e9)
+    b = min(b, host_units(3, 4, n))
+    A_host = torch.empty((b * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+    A_host.copy_(A[:b * M_TILE])
+    t0p = med(S0)
+    tb = med(dak.SplitMatrix(A_host if b else None, A[b * M_TILE:], M, K, M_TILE, b))
+    _, tf_probe = dak.probe_mfma(workgroups=1024, iters=8192, reps=5)
+    tf0, tfb = flops / t0 / 1e9, flops / tb / 1e9
+    out["prefill_28672x8192x2048"] = {
+        "x0_TFLOPs": round(tf0, 1), "x0_frac_spec": round(tf0 / MFMA_BF16_DENSE_TFLOPS, 4),
+        "x0_frac_probe": round(tf0 / tf_probe, 4), "probe_TFLOPs": round(tf_probe, 1),
+        "planner_x": round(b / n, 4), "planner_TFLOPs": round(tfb, 1),
+        "planner_frac_spec": round(tfb / MFMA_BF16_DENSE_TFLOPS, 4),
+        "planner_slowdown_vs_paired_x0": round(tb / t0p, 4)}
+    del A, X, y, A_host
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline_llama70b(torch, model, seed=0):
@@ -994,6 +1136,8 @@ def main(argv=None):
     ap.add_argument("--x-num", type=int, default=5, help="headline ratio numerator over 20 (5 -> 0.25)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="leave out the other configurations' compact numbers from the headline line")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
@@ -1106,6 +1250,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_spread": time_steps.spread,
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
@@ -1146,6 +1291,11 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl)
+    if not args.no_extras:
+        log("other configurations: the 1024x1024 GEMV, the decode linears at x = 0, the prefill GEMM")
+        del wl
+        torch.cuda.empty_cache()
+        result["extras"] = headline_extras(torch, dak, b_hbm, b_host, warm_seconds=args.warm_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

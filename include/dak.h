@@ -138,11 +138,13 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  * of compute units reading the host and the requests each keeps in flight are
  * capped; both come from an offline sweep.
  *   host_cus       cap on work-groups (one per CU) that read host memory;
- *                  0 = per-operator default: split GEMM N <= 4: 8; split
- *                  GEMM 4 < N <= 64: the fewest whose staged chunks in flight
- *                  cover about 256 KiB (8 to 32); 64 < N <= 256: 16; split
- *                  attention: 8 (the fewest that reach the full link rate in
- *                  the library's sweep on MI355X); N > 256: no cap, the
+ *                  0 = per-operator default from the library's host-role
+ *                  sweep on MI355X (the fewest that reach the full link rate;
+ *                  tuning_defaults.hpp, generated from the sweep table): split
+ *                  GEMM N <= 4 and 64 < N <= 256, and split attention, one
+ *                  swept cap each; split GEMM 4 < N <= 64 (bf16 and FP8): the
+ *                  fewest whose staged chunks in flight cover about 256 KiB,
+ *                  within the sweep's bounds; N > 256: no cap, the
  *                  launch picks its group count from a time model of the
  *                  link and of both roles' rounds.  For N > 256 host
  *                  work-groups come in groups of ceil(N/256), one per

@@ -325,3 +325,17 @@ def test_noalloc_attention_rejects_shapes_beyond_its_scratch_before_any_launch()
     # the workspace entry point still refuses a NULL workspace
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 64, C.c_float(0.1), None, None, 1 << 30, None,
                                       None) == L.DAK_EINVAL
+
+
+def test_tuning_defaults_header_matches_the_sweep_table():
+    # The library's host work-group defaults are the generated header's, and
+    # the header is what the committed sweep table gives.
+    import json
+    from tiered_memory_offloading_amd import tune
+    with open(os.path.join(ROOT, "tiered_memory_offloading_amd", "tuning_mi355x.json")) as f:
+        d = tune.defaults_from_table(json.load(f))
+    txt = open(tune.HEADER).read()
+    consts = dict(re.findall(r"constexpr int (kTuned\w+) = (\d+);", txt))
+    assert consts == {"kTunedGemmFmaHostCus": str(d["gemm_fma"]), "kTunedGemmMfmaHostCus": str(d["gemm_mfma"]),
+                      "kTunedAttnHostCus": str(d["attn"]), "kTunedRingHostCusMin": str(d["ring_min"]),
+                      "kTunedRingHostCusMax": str(d["ring_max"])}

@@ -6,6 +6,7 @@
 #include <string>
 
 #include "../../include/dak.h"
+#include "tuning_defaults.hpp"
 
 namespace dak {
 
@@ -19,13 +20,20 @@ void clear_error();
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Host-role work-group caps per operator class, from the offline sweep on
-// MI355X: the fewest host work-groups that reach the link's full rate.
+// MI355X (tuning_defaults.hpp, written by the sweep): the fewest host
+// work-groups that reach the link's full rate.
 struct HostDefaults {
   int host_cus;
 };
-constexpr HostDefaults kGemmFmaDefaults{8};    // split GEMM, N <= 4
-constexpr HostDefaults kGemmMfmaDefaults{16};  // split GEMM, N > 4
-constexpr HostDefaults kAttnDefaults{8};       // split decode attention
+constexpr HostDefaults kGemmFmaDefaults{kTunedGemmFmaHostCus};    // split GEMM, N <= 4
+constexpr HostDefaults kGemmMfmaDefaults{kTunedGemmMfmaHostCus};  // split GEMM, 64 < N <= 256
+constexpr HostDefaults kAttnDefaults{kTunedAttnHostCus};          // split decode attention
+
+// Host work-groups of the LDS-ring GEMMs: enough that their chunks in flight
+// cover the link's bandwidth-delay product (kHostInflightBytes below, given
+// the weight bytes one host work-group keeps in flight), within the sweep's
+// bounds.
+inline int ring_host_cus(uint64_t inflight_per_wg);
 // Split GEMM, N > 256: no cap by default; the launch picks its number of host
 // groups (one work-group per 256-column tile each) from a time model of the
 // link, the groups and the HBM tiles' rounds.
@@ -37,6 +45,12 @@ constexpr int kGemmTiledMaxHostCus = 1 << 30;
 // host parts) get deeper windows; many get shallow ones, which also slows
 // concurrent HBM readers the least.
 constexpr uint64_t kHostInflightBytes = 256u << 10;
+
+inline int ring_host_cus(uint64_t inflight_per_wg) {
+  const uint64_t g = (kHostInflightBytes + inflight_per_wg - 1) / inflight_per_wg;
+  return g < (uint64_t)kTunedRingHostCusMin ? kTunedRingHostCusMin
+         : g > (uint64_t)kTunedRingHostCusMax ? kTunedRingHostCusMax : (int)g;
+}
 
 // Smallest window in {1, 2, 4, ..., max_window} with
 // host_wgs * bytes_per_step_per_wg * window >= kHostInflightBytes.

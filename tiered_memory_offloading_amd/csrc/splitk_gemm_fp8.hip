@@ -342,9 +342,7 @@ int f8_row_blocks(int64_t M, int64_t m) {
 // bandwidth-delay product.
 int f8_host_cus(int64_t N, int rb) {
   const int nb = f8_nb_of(N);
-  const uint64_t inflight = (uint64_t)(f8_stages(nb, rb, nb == 1 ? f8_xr_of(N) : 16) - 1) * 16 * rb * kF8ARow;
-  const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
-  return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
+  return ring_host_cus((uint64_t)(f8_stages(nb, rb, nb == 1 ? f8_xr_of(N) : 16) - 1) * 16 * rb * kF8ARow);
 }
 
 }  // namespace

@@ -297,9 +297,7 @@ uint64_t staged_host_inflight(int64_t N, int row_blocks) {
 int staged_host_cus(int64_t N, int row_blocks) {
   // Enough host work-groups that the chunks they have in flight cover the
   // link's bandwidth-delay product.
-  const uint64_t inflight = staged_host_inflight(N, row_blocks);
-  const uint64_t g = (kHostInflightBytes + inflight - 1) / inflight;
-  return (int)std::min<uint64_t>(32, std::max<uint64_t>(8, g));
+  return ring_host_cus(staged_host_inflight(N, row_blocks));
 }
 
 void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count) {

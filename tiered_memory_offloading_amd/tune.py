@@ -12,17 +12,24 @@ Three measurements, all through the C ABI:
   * the chosen (host_cus, window) per operator class, written as JSON.
 
 Run:  python -m tiered_memory_offloading_amd.tune --out tuning.json
+      python -m tiered_memory_offloading_amd.tune --header-from tuning.json
 
 tuning_mi355x.json beside this file is the table measured on MI355X with the
-current kernels; the library's built-in host work-group defaults (8 for the
-GEMV path and attention, the bandwidth-delay rule for the staged GEMM) sit at
-its plateaus.
+current kernels.  The library's host work-group defaults come from it: the
+second command writes csrc/tuning_defaults.hpp, which the build includes.
+Per operator class the default cap is the sweep's choice, the fewest host
+work-groups within 1 % of the best host rate: the split GEMM at N = 1 (the
+path for N <= 4), at N = 128 (64 < N <= 256) and split attention.  The staged
+bf16 and FP8 GEMMs (4 < N <= 64) size their host role by the link's
+bandwidth-delay product instead; their sweeps' choices (N = 16 and 64) bound
+that rule from below and above.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import math
+import os
 import sys
 import time
 
@@ -141,11 +148,61 @@ def _best(res):
             "best_GBps": top}
 
 
+HEADER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "tuning_defaults.hpp")
+
+
+def defaults_from_table(table):
+    """The library's default host work-group caps from a sweep table."""
+    g = table["gemm"]
+    ring = [g["16"]["best"]["host_cus"], g["64"]["best"]["host_cus"]]
+    ring += [table["gemm_fp8"][n]["best"]["host_cus"] for n in ("1", "16", "64")]
+    return {"gemm_fma": g["1"]["best"]["host_cus"], "gemm_mfma": g["128"]["best"]["host_cus"],
+            "attn": table["attn"]["best"]["host_cus"], "ring_min": min(ring), "ring_max": max(ring)}
+
+
+def write_header(table, path=HEADER, source="tuning_mi355x.json"):
+    d = defaults_from_table(table)
+    text = f"""// Host work-group defaults of the split operators, written by
+// `python -m tiered_memory_offloading_amd.tune --header-from {source}`
+// from the host-role sweep measured on {table.get("device", "the device")}.  Do not edit: re-run
+// the sweep and regenerate.  DAK paper section 4.3.1: the number of compute units
+// reading the host comes from an offline sweep; each value is the fewest host
+// work-groups whose host rate is within 1 % of the best in its sweep.
+#pragma once
+
+namespace dak {{
+
+// Split GEMM, N <= 4 (swept at N = 1, all tile-rows on the host).
+constexpr int kTunedGemmFmaHostCus = {d["gemm_fma"]};
+// Split GEMM, 64 < N <= 256 (swept at N = 128).
+constexpr int kTunedGemmMfmaHostCus = {d["gemm_mfma"]};
+// Split decode attention (swept with all requests on the host).
+constexpr int kTunedAttnHostCus = {d["attn"]};
+// Bounds of the bandwidth-delay rule of the LDS-ring GEMMs (bf16 at
+// 4 < N <= 64, FP8 at N <= 64): the smallest and largest choice of their
+// sweeps (bf16 at N = 16 and 64, FP8 at N = 1, 16 and 64).
+constexpr int kTunedRingHostCusMin = {d["ring_min"]};
+constexpr int kTunedRingHostCusMax = {d["ring_max"]};
+
+}}  // namespace dak
+"""
+    with open(path, "w") as f:
+        f.write(text)
+    return d
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description="host-role parameter sweep")
     ap.add_argument("--out", default=None)
     ap.add_argument("--skip-congestion", action="store_true")
+    ap.add_argument("--header-from", default=None,
+                    help="write csrc/tuning_defaults.hpp from this sweep table and exit (no GPU needed)")
     args = ap.parse_args(argv)
+    if args.header_from:
+        with open(args.header_from) as f:
+            d = write_header(json.load(f), source=os.path.basename(args.header_from))
+        print(json.dumps(d))
+        return 0
     library()
     log = lambda s: print(s, file=sys.stderr, flush=True)
     t0 = time.time()
@@ -153,7 +210,7 @@ def main(argv=None):
     if not args.skip_congestion:
         table["congestion"] = congestion(log=log)
     table["gemm"] = {}
-    for N in (1, 16, 64):
+    for N in (1, 16, 64, 128):
         res = gemm_host_sweep(N, log=log)
         table["gemm"][str(N)] = {"best": _best(res), "sweep": res}
     table["gemm_fp8"] = {}

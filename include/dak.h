@@ -167,7 +167,8 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  *   byte_counters  device pointer to 2 uint64 (host bytes, HBM bytes), used
  *                  only with DAK_FLAG_COUNT_BYTES: the kernels add the bytes
  *                  of A (or of K and V) they load from each tier.  The caller
- *                  zeroes them.
+ *                  zeroes them.  With DAK_FLAG_RECORD_XCC, 2 + 256 uint64 (see
+ *                  there).
  * A NULL dak_launch_cfg* means all defaults. */
 typedef struct {
   int32_t host_cus;
@@ -190,6 +191,15 @@ typedef struct {
  * N > 256 and for paged attention); the byte counters count every byte as
  * HBM. */
 #define DAK_FLAG_STAGED_HOST 2
+/* Split GEMM with N > 256 only (ignored elsewhere): byte_counters then holds
+ * 2 + 256 uint64 (the caller zeroes them), and entry 2 + q receives the
+ * bitwise OR of 1 << (XCD id) over the work-groups of host group q, read from
+ * the hardware's XCC id register.  A mask with one bit shows that the group's
+ * work-groups, which request the same host row block, shared one XCD's L2
+ * (DAK paper §4.3.2: a host tile must cross the link once; on CDNA4 that L2,
+ * not a multicast, serves the repeats).  A debugging aid for the placement
+ * the tiled schedule assumes. */
+#define DAK_FLAG_RECORD_XCC 4
 
 /* ------------------------------------------------------------------------ */
 /* Split GEMM: y = x . A^T with A split by tile-rows across the two tiers      */

@@ -125,16 +125,22 @@ class LaunchConfig:
     window: int = 0                # 0 = library default
     byte_counters: Optional[torch.Tensor] = None   # int64 [2] on the GPU: host, HBM bytes loaded
     staged_host: bool = False      # the host part is a device copy staged by a prefetcher
+    record_xcc: bool = False       # N > 256: byte_counters[2 + q] gets host group q's XCD bit mask
 
     def as_c(self) -> L.LaunchCfg:
         flags = L.DAK_FLAG_STAGED_HOST if self.staged_host else 0
         ptr = None
         if self.byte_counters is not None:
             t = self.byte_counters
-            if t.dtype != torch.int64 or t.numel() < 2 or not t.is_cuda:
-                raise ValueError("byte_counters must be an int64 CUDA tensor of 2 elements")
+            need = 2 + 256 if self.record_xcc else 2
+            if t.dtype != torch.int64 or t.numel() < need or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"byte_counters must be a contiguous int64 CUDA tensor of {need} elements")
             flags |= L.DAK_FLAG_COUNT_BYTES
+            if self.record_xcc:
+                flags |= L.DAK_FLAG_RECORD_XCC
             ptr = t.data_ptr()
+        elif self.record_xcc:
+            raise ValueError("record_xcc needs byte_counters")
         return L.LaunchCfg(int(self.host_cus), int(self.window), flags, 0, ptr)
 
 

@@ -14,6 +14,7 @@ DAK_EHIP = -3
 DAK_EUNSUPPORTED = -4
 DAK_FLAG_COUNT_BYTES = 1
 DAK_FLAG_STAGED_HOST = 2
+DAK_FLAG_RECORD_XCC = 4
 ABI_VERSION = 2
 
 

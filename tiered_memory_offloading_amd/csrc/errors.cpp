@@ -50,11 +50,12 @@ dak_status resolve_cfg(const dak_launch_cfg* cfg, HostDefaults def, LaunchCfg* o
       return fail(DAK_EINVAL, "window %d is not 0, 1, 2, 4 or 8", cfg->window);
     out->window = cfg->window;
   }
-  if (cfg->flags & ~(DAK_FLAG_COUNT_BYTES | DAK_FLAG_STAGED_HOST))
+  if (cfg->flags & ~(DAK_FLAG_COUNT_BYTES | DAK_FLAG_STAGED_HOST | DAK_FLAG_RECORD_XCC))
     return fail(DAK_EINVAL, "unknown flag bits 0x%x", cfg->flags);
   out->flags = cfg->flags;
-  if ((cfg->flags & DAK_FLAG_COUNT_BYTES) && (!cfg->byte_counters || ((uintptr_t)cfg->byte_counters & 7)))
-    return fail(DAK_EINVAL, "DAK_FLAG_COUNT_BYTES needs an 8-byte aligned byte_counters pointer");
+  if ((cfg->flags & (DAK_FLAG_COUNT_BYTES | DAK_FLAG_RECORD_XCC)) &&
+      (!cfg->byte_counters || ((uintptr_t)cfg->byte_counters & 7)))
+    return fail(DAK_EINVAL, "DAK_FLAG_COUNT_BYTES and DAK_FLAG_RECORD_XCC need an 8-byte aligned byte_counters pointer");
   out->byte_counters = cfg->byte_counters;
   return DAK_OK;
 }

@@ -20,6 +20,7 @@ struct TiledArgs {
   int n_groups;   // host groups of ceil(N/256) work-groups (0 when host_rows == 0)
   int cus;        // compute units of the device: the grid, one work-group each
   unsigned long long* counters;
+  unsigned long long* xcc_masks;   // DAK_FLAG_RECORD_XCC: one XCD bit mask per host group, else null
   hipStream_t stream;
 };
 

@@ -307,13 +307,22 @@ template <bool COUNT, bool RAGGED>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int n_groups, int cus,
-    int n_xcd, unsigned long long* __restrict__ counters) {
+    int n_xcd, unsigned long long* __restrict__ counters, unsigned long long* __restrict__ xcc_masks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
   const int tn = (int)((N + kBN - 1) / kBN);
   const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, (host_rows + kBM - 1) / kBM,
                                  (M - host_rows + kBM - 1) / kBM * tn);
   const bool host_role = w.host;
+  // Where the schedule's placement assumption can be checked: each host
+  // work-group ORs the bit of the XCD it runs on (the hardware's XCC id
+  // register) into its group's mask.  One bit per group means the group's
+  // work-groups share one L2, which serves their repeated reads of a host
+  // row block.
+  if (xcc_masks && host_role && threadIdx.x == 0) {
+    const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u;   // hwreg(HW_REG_XCC_ID, 0, 4)
+    atomicOr(&xcc_masks[w.first], 1ull << xcc);
+  }
   if (host_role) {
     for (int64_t rb = w.first; rb < w.end; rb += w.stride) {
       __syncthreads();   // the ring is reused
@@ -343,7 +352,7 @@ void launch_gemm_tiled(const TiledArgs& g, bool count) {
   const bool ragged = (g.K & 31) != 0;
 #define DAK_TILED(C, R)                                                                                          \
   hipLaunchKernelGGL((gemm_tiled_split<C, R>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host, g.a_hbm, \
-                     g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.counters)
+                     g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.counters, g.xcc_masks)
   if (count) {
     if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
   } else {

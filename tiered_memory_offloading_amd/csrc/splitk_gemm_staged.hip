@@ -114,6 +114,20 @@ struct StagedItem {
   }
 };
 
+// Wait until at most `later` chunks' DMA instructions of this wave (PW each)
+// are still in flight; later <= MAXL.
+template <int PW, int MAXL>
+__device__ __forceinline__ void vm_wait_chunks(int64_t later) {
+  static_assert(PW * MAXL <= 63, "vmcnt range");
+  if constexpr (MAXL >= 6) { if (later >= 6) { vm_wait<6 * PW>(); return; } }
+  if constexpr (MAXL >= 5) { if (later == 5) { vm_wait<5 * PW>(); return; } }
+  if constexpr (MAXL >= 4) { if (later == 4) { vm_wait<4 * PW>(); return; } }
+  if constexpr (MAXL >= 3) { if (later == 3) { vm_wait<3 * PW>(); return; } }
+  if constexpr (MAXL >= 2) { if (later == 2) { vm_wait<2 * PW>(); return; } }
+  if constexpr (MAXL >= 1) { if (later == 1) { vm_wait<PW>(); return; } }
+  vm_wait<0>();
+}
+
 template <int NB, int RB, int STAGES, bool COUNT>
 __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
@@ -122,11 +136,9 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
     unsigned long long* __restrict__ counters) {
   using S = StagedShape<NB, RB>;
   using I = StagedItem<NB, RB, COUNT>;
-  // One array per slot: the slot a wave reads is then a different object from
-  // the slots being filled, which keeps the compiler's alias reasoning exact.
-  __shared__ __attribute__((aligned(16))) unsigned char s0[S::SLOT];
-  __shared__ __attribute__((aligned(16))) unsigned char s1[S::SLOT];
-  __shared__ __attribute__((aligned(16))) unsigned char s2[STAGES > 2 ? S::SLOT : 16];
+  // The ring: STAGES slots of one array; chunk c lives in slot c % STAGES.
+  __shared__ __attribute__((aligned(16))) unsigned char ring[STAGES * S::SLOT];
+  unsigned char* const s0 = ring;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rb = wave % RB, phase = wave / RB;
@@ -150,35 +162,28 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    I::issue(s0, 0, a, x, N, K, wave, lane, nbytes, spread);
-    if (STAGES > 2 && nch > 1) I::issue(s1, 1, a, x, N, K, wave, lane, nbytes, spread);
-    // Step for chunk c = c0 + IDX: wait for its DMA (all waves, via the
-    // barrier, which also retires every read of the slot about to be refilled),
-    // refill that slot with chunk c + STAGES - 1, then consume chunk c.
-#define DAK_STAGED_STEP(IDX, RD, WR)                                                             \
-  {                                                                                              \
-    const int64_t c = c0 + IDX;                                                                  \
-    if (c < nch) {                                                                               \
-      const int64_t later = std::min<int64_t>(nch - 1 - c, STAGES - 2);                          \
-      if (later >= 2) vm_wait<2 * S::PER_WAVE>();                                                \
-      else if (later == 1) vm_wait<S::PER_WAVE>();                                               \
-      else vm_wait<0>();                                                                         \
-      __builtin_amdgcn_s_barrier();                                                              \
-      if (c + STAGES - 1 < nch) I::issue(WR, c + STAGES - 1, a, x, N, K, wave, lane, nbytes, spread);    \
-      I::compute(RD, c, K, rb, phase, lane, acc);                                                \
-    }                                                                                            \
-  }
+    // Chunks 0 .. STAGES - 2 in flight before the first is consumed.
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+      if (i < nch) I::issue(ring + i * S::SLOT, i, a, x, N, K, wave, lane, nbytes, spread);
+    // Step for chunk c: wait for its DMA (all waves, via the barrier, which
+    // also retires every read of the slot about to be refilled), refill that
+    // slot with chunk c + STAGES - 1, then consume chunk c.  Unrolled over the
+    // ring so that every slot offset is a constant.
     for (int64_t c0 = 0; c0 < nch; c0 += STAGES) {
-      if constexpr (STAGES == 2) {
-        DAK_STAGED_STEP(0, s0, s1)
-        DAK_STAGED_STEP(1, s1, s0)
-      } else {
-        DAK_STAGED_STEP(0, s0, s2)
-        DAK_STAGED_STEP(1, s1, s0)
-        DAK_STAGED_STEP(2, s2, s1)
+#pragma unroll
+      for (int i = 0; i < STAGES; ++i) {
+        const int64_t c = c0 + i;
+        if (c < nch) {
+          vm_wait_chunks<S::PER_WAVE, STAGES - 2>(std::min<int64_t>(nch - 1 - c, STAGES - 2));
+          __builtin_amdgcn_s_barrier();
+          if (c + STAGES - 1 < nch)
+            I::issue(ring + ((i + STAGES - 1) % STAGES) * S::SLOT, c + STAGES - 1, a, x, N, K, wave, lane, nbytes,
+                     spread);
+          I::compute(ring + i * S::SLOT, c, K, rb, phase, lane, acc);
+        }
       }
     }
-#undef DAK_STAGED_STEP
     const int i16 = lane & 15, g = lane >> 4;
     if constexpr (S::P == 1) {
 #pragma unroll
@@ -225,19 +230,23 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
 // work-groups per CU), else two.
 constexpr int stages_for(int nb, int rb) { return 3 * (16 * rb + 16 * nb) * kRowB <= (80 << 10) ? 3 : 2; }
 
-// Three slots also where they need the whole CU (N > 32, items of 16 or 32
-// rows: 120 or 144 KiB), provided the grid then still runs in one round of one
-// work-group per CU, and the host role's weight bytes in flight (two chunks
-// per host work-group) stay within the link's bandwidth-delay product (the
-// congestion window of DAK §4.3.1).  Every work-group then keeps twice the
-// bytes in flight and no item waits for a second round (measured at N = 64:
-// 4096-row ops 5-9 % faster at x = 0 and 6-9 % at a 1/16 host share; 6144
-// rows, which would need a second round, lose 40 %).  The depth changes no
-// arithmetic.
+// Instances that exist: the ring fits the CU's 160 KiB of LDS and a wave's
+// DMA instructions in flight fit the vmcnt counter.
+template <int NB, int RB, int ST>
+constexpr bool stages_fit() {
+  return ST >= 2 && ST <= 8 && ST * StagedShape<NB, RB>::SLOT <= (160 << 10) &&
+         StagedShape<NB, RB>::PER_WAVE * (ST - 2) <= 63;
+}
+
+// Without a host role: three slots also where they need the whole CU (N > 32,
+// items of 16 or 32 rows: 120 or 144 KiB), provided the grid then still runs
+// in one round of one work-group per CU (measured at N = 64: 4096-row ops 5-9 %
+// faster at x = 0; 6144 rows, which would need a second round, lose 40 %).
+// Deeper rings at x = 0 measured no better (the four Llama-8B linears at
+// N = 16: 110-125 us per step for every depth from 2 to 8).
 bool deep_ring(int nb, int rb, const StagedArgs& g) {
-  const uint64_t host_inflight = (uint64_t)g.host_wgs * 2 * 16 * rb * kRowB;
   return stages_for(nb, rb) == 2 && 3 * (16 * rb + 16 * nb) * kRowB <= (160 << 10) &&
-         g.host_wgs + g.hbm_items <= g.cus && host_inflight <= kHostInflightBytes;
+         g.host_wgs + g.hbm_items <= g.cus;
 }
 
 template <int NB, int RB, int ST, bool COUNT>
@@ -248,10 +257,54 @@ void launch_nb_rb_st(const StagedArgs& g) {
                      g.host_items, g.hbm_items, g.counters);
 }
 
+// Work-groups of one instance resident per CU at once (LDS and registers),
+// as the runtime reports it; 0 if the query fails.
+template <int NB, int RB, int ST, bool COUNT>
+int staged_occupancy() {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_staged_split<NB, RB, ST, COUNT>, kSThreads, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+    return n;
+  }();
+  return occ;
+}
+
+// With a host role: the deepest ring (up to 8 slots) whose grid still runs in
+// one round at that instance's occupancy and whose host work-groups keep at
+// most the link's bandwidth-delay product of weight bytes in flight (DAK
+// §4.3.1's congestion window).  A host share of a few tile-rows has only a
+// few host items, one work-group each; each then keeps ST - 1 chunks in
+// flight instead of one or two (the 70B-shaped down, 8192 x 28672 with one
+// host tile-row at N = 16: four host work-groups, five slots).  The depth
+// changes no arithmetic: a step's k-phase is its index within K.
+template <int NB, int RB, int ST, bool COUNT>
+bool launch_deepest(const StagedArgs& g) {
+  if constexpr (!stages_fit<NB, RB, ST>()) {
+    return false;
+  } else {
+    if constexpr (ST < 8) {
+      if (launch_deepest<NB, RB, ST + 1, COUNT>(g)) return true;
+    }
+    const int occ = staged_occupancy<NB, RB, ST, COUNT>();
+    const uint64_t host_inflight = (uint64_t)g.host_wgs * (ST - 1) * 16 * RB * kRowB;
+    if (occ > 0 && g.host_wgs + g.hbm_items <= (int64_t)g.cus * occ && host_inflight <= kHostInflightBytes) {
+      launch_nb_rb_st<NB, RB, ST, COUNT>(g);
+      return true;
+    }
+    return false;
+  }
+}
+
 template <int NB, int RB, bool COUNT>
 void launch_nb_rb(const StagedArgs& g) {
   constexpr int ST = stages_for(NB, RB);
-  if constexpr (ST == 2 && 3 * (16 * RB + 16 * NB) * kRowB <= (160 << 10)) {
+  if (g.host_wgs > 0) {
+    if (launch_deepest<NB, RB, ST + 1, COUNT>(g)) return;
+  } else if constexpr (ST == 2 && stages_fit<NB, RB, 3>()) {
     if (deep_ring(NB, RB, g)) return launch_nb_rb_st<NB, RB, 3, COUNT>(g);
   }
   launch_nb_rb_st<NB, RB, ST, COUNT>(g);

@@ -90,60 +90,98 @@ struct PagedRows {
   }
 };
 
-// Load one 16-token tile starting at ts (lane: tokens ts + 4 i + lane / 16,
-// dims 8 (lane % 16) .. +7); tokens at or past te, or a tile that does not
-// exist, load zeros and count nothing.
+// Load one 16-token tile starting at ts.  K in the layout of the score
+// MFMA's A operand: lane l holds token ts + (l & 15), dims 32 j + 8 (l >> 4)
+// .. +7 (kt[j], j = 0..3: four 64-byte pieces of each token's 256-byte row).
+// V in the layout of the P.V products: load i covers tokens ts + 4 i + l / 16,
+// dims 8 (l % 16) .. +7 (1 KiB contiguous per load).  Tokens at or past te, or
+// a tile that does not exist, load zeros and count nothing.
 template <bool COUNT, class Rows>
-__device__ __forceinline__ void load_tile(const Rows& rows, int64_t ts, int64_t te, bool exists, int grp, int dq,
-                                          uint4 (&kv)[4], uint4 (&vv)[4], uint64_t& nbytes) {
+__device__ __forceinline__ void load_tile(const Rows& rows, int64_t ts, int64_t te, bool exists, int lane,
+                                          uint4 (&kt)[4], uint4 (&vv)[4], uint64_t& nbytes) {
+  const int n = lane & 15, g = lane >> 4;
+  {
+    const int64_t t = ts + n;
+    const bool ok = exists && (t < te);
+    const int64_t r = rows.off(ts, t) + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kt[j] = ok ? ld16(rows.k + r + 32 * j) : make_uint4(0, 0, 0, 0);
+    if (COUNT && ok) nbytes += 64;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = ts + 4 * i + grp;
+    const int64_t t = ts + 4 * i + g;
     const bool ok = exists && (t < te);
-    const int64_t r = rows.off(ts, t) + dq;
-    kv[i] = ok ? ld16(rows.k + r) : make_uint4(0, 0, 0, 0);
+    const int64_t r = rows.off(ts, t) + 8 * n;
     vv[i] = ok ? ld16(rows.v + r) : make_uint4(0, 0, 0, 0);
-    if (COUNT && ok) nbytes += 32;
+    if (COUNT && ok) nbytes += 16;
   }
 }
 
-// Fold one loaded tile into the lane group's online-softmax state.
+// Fold one loaded tile into the wave's online-softmax state.
+//
+// Scores on the matrix cores: S = K_tile . Q^T with K_tile [16 tokens x 128]
+// as the A operand and Q^T [128 x 16 heads] (heads >= G zero) as the B
+// operand, four v_mfma_f32_16x16x32_bf16 over the 128 dims; lane l then holds
+// the scores of tokens 4 (l >> 4) .. +3 for head l & 15.  The head's running
+// max is reduced over the four lanes that hold its 16 tokens, so every lane
+// that holds a head agrees on it.  The probabilities p = exp2(s - m) of the G
+// real heads go through the wave's LDS buffer (pb: [16 tokens][G] floats,
+// then the rescale factors [G]) to the layout of the P.V products, where lane
+// group l >> 4 takes tokens 4 i + (l >> 4) and lane l & 15 the output dims
+// 8 (l & 15) .. +7, accumulating o[h][e] += p[h] v[e] with one fma per token
+// and l[h] with the same fmas on a value of 1 (so o is exactly c l whenever
+// every V row is a power of two c).  All in fp32; bf16 inputs are exact.
 template <int G>
-__device__ __forceinline__ void attn_tile(const uint4 (&kv)[4], const uint4 (&vv)[4], int64_t ts, int64_t te, int grp,
-                                          const uint32_t (&qb)[G][4], float qscale, float (&m)[G], float (&l)[G],
-                                          float (&o)[G][8]) {
-  // Scores, stage by stage over all 4 G independent values (each value sees
-  // the same operations in the same order as a chain-by-chain walk): the
-  // dot products, then each of the four row-sum steps, so the DPP steps of
-  // different values interleave instead of waiting on each other.
-  float s[4][G];
+__device__ __forceinline__ void attn_tile(const uint4 (&kt)[4], const uint4 (&vv)[4], int64_t ts, int64_t te,
+                                          int lane, const bf16x8_t (&qf)[4], float qscale, float& m_lane,
+                                          float (&l)[G], float (&o)[G][8], float* pb) {
+  const int hl = lane & 15, grp = lane >> 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt[j]), qf[j], acc, 0, 0, 0);
+  float sc[4];
+  if (ts + kTile <= te) {   // uniform: every token of the tile is valid
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = acc[r] * qscale;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (ts + 4 * grp + r < te) ? acc[r] * qscale : kNegInf;
+  }
+  // Tile max of the lane's head over its 16 tokens (4 here, 4 lane groups).
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m_lane, mt);
+  const float ms = (mn == kNegInf) ? 0.f : mn;
+  // Rescale only when some real head's running max grew; elsewhere the
+  // factor is exp2(0) = 1 and the multiply would not change a bit.
+  const bool grew = __any(hl < G && mn > m_lane);
+  if (hl < G) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pb[(4 * grp + r) * G + hl] = exp2_fast(sc[r] - ms);
+    if (grew && grp == 0) pb[16 * G + hl] = exp2_fast(m_lane - ms);
+  }
+  m_lane = mn;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (grew) {
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) al[h] = pb[16 * G + h];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      l[h] = l[h] * al[h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * al[h];
+    }
+  }
+  float p[4][G];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[i][h] = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t kw = q == 0 ? kv[i].x : q == 1 ? kv[i].y : q == 2 ? kv[i].z : kv[i].w;
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = dot2_bf16(kw, qb[h][q], s[i][h]);
-    }
-  }
-  row16_sum_all<4 * G>(&s[0][0]);
-  if (ts + kTile <= te) {   // uniform: every token of the tile is valid
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = s[i][h] * qscale;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = ts + 4 * i + grp;
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = (t < te) ? s[i][h] * qscale : kNegInf;
-    }
-  }
+    for (int h = 0; h < G; ++h) p[i][h] = pb[(4 * i + grp) * G + h];
   float vf[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -156,71 +194,56 @@ __device__ __forceinline__ void attn_tile(const uint4 (&kv)[4], const uint4 (&vv
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mt = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-    const float mn = fmaxf(m[h], mt);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    // Rescale only when some lane group's running max grew; elsewhere the
-    // factor is exp2(0) = 1 and the multiply would not change a bit.
     float ls = l[h];
-    if (__any(mn > m[h])) {
-      const float alpha = exp2_fast(m[h] - ms);
-      ls = ls * alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * alpha;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i][h] - ms);
-    // l and o take the same sequence of operations (o with an fma per token),
-    // so o is exactly c * l whenever every V row equals a power of two c.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ls = ls + p[i];
+    for (int i = 0; i < 4; ++i) ls = __builtin_fmaf(p[i][h], 1.0f, ls);
     l[h] = ls;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float acc = o[h][e];
+      float a = o[h][e];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(p[i], vf[i][e], acc);
-      o[h][e] = acc;
+      for (int i = 0; i < 4; ++i) a = __builtin_fmaf(p[i][h], vf[i][e], a);
+      o[h][e] = a;
     }
-    m[h] = mn;
   }
+  // This tile's reads of pb before the next tile's writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the lane
-// group's online-softmax state.  qb holds the lane's 8 query dims per head as
-// bf16 pairs (unscaled); qscale = scale * log2(e).
+// Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the wave's
+// online-softmax state (qf: the Q^T fragments of the group's G heads).
 //   U > 0: groups of U tiles, each group loaded and then folded in;
 //   U < 0: software-pipelined by one tile: tile j + 1's loads are issued
 //          before tile j is folded in, so a wave always has a tile in flight.
 // The tiles are folded in the same order either way (the same bits).
 template <int G, int U, bool COUNT, class Rows>
-__device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_t te, const uint32_t (&qb)[G][4],
-                                            float qscale, float (&m)[G], float (&l)[G], float (&o)[G][8], int lane,
-                                            uint64_t& nbytes) {
-  const int grp = lane >> 4;
-  const int dq = (lane & 15) * 8;
+__device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_t te, const bf16x8_t (&qf)[4],
+                                            float qscale, float& m_lane, float (&l)[G], float (&o)[G][8], int lane,
+                                            float* pb, uint64_t& nbytes) {
   const int64_t ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
   if constexpr (U < 0) {
     uint4 ka[4], va[4], kb[4], vb[4];
-    load_tile<COUNT>(rows, tb, te, ntiles > 0, grp, dq, ka, va, nbytes);
+    load_tile<COUNT>(rows, tb, te, ntiles > 0, lane, ka, va, nbytes);
     for (int64_t j = 0; j < ntiles; j += 2) {
       const int64_t ts = tb + j * kTile;
-      load_tile<COUNT>(rows, ts + kTile, te, j + 1 < ntiles, grp, dq, kb, vb, nbytes);
-      attn_tile<G>(ka, va, ts, te, grp, qb, qscale, m, l, o);
+      load_tile<COUNT>(rows, ts + kTile, te, j + 1 < ntiles, lane, kb, vb, nbytes);
+      attn_tile<G>(ka, va, ts, te, lane, qf, qscale, m_lane, l, o, pb);
       if (j + 1 >= ntiles) break;   // uniform
-      load_tile<COUNT>(rows, ts + 2 * kTile, te, j + 2 < ntiles, grp, dq, ka, va, nbytes);
-      attn_tile<G>(kb, vb, ts + kTile, te, grp, qb, qscale, m, l, o);
+      load_tile<COUNT>(rows, ts + 2 * kTile, te, j + 2 < ntiles, lane, ka, va, nbytes);
+      attn_tile<G>(kb, vb, ts + kTile, te, lane, qf, qscale, m_lane, l, o, pb);
     }
   } else {
     for (int64_t t0 = 0; t0 < ntiles; t0 += U) {
       uint4 kv[U][4], vv[U][4];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        load_tile<COUNT>(rows, tb + (t0 + u) * kTile, te, t0 + u < ntiles, grp, dq, kv[u], vv[u], nbytes);
+        load_tile<COUNT>(rows, tb + (t0 + u) * kTile, te, t0 + u < ntiles, lane, kv[u], vv[u], nbytes);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (t0 + u < ntiles) attn_tile<G>(kv[u], vv[u], tb + (t0 + u) * kTile, te, grp, qb, qscale, m, l, o);
+        if (t0 + u < ntiles)
+          attn_tile<G>(kv[u], vv[u], tb + (t0 + u) * kTile, te, lane, qf, qscale, m_lane, l, o, pb);
     }
   }
 }
@@ -235,40 +258,50 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
                                           float* __restrict__ o_ws, float* __restrict__ ml_ws, float* red_o,
                                           float* red_ml, int wave, int lane, uint64_t& nbytes) {
   const int dq = (lane & 15) * 8;
-  uint32_t qb[G][4];
+  // Q^T fragments: lane l holds dims 32 j + 8 (l >> 4) .. +7 of the group's
+  // head l & 15 (zeros for l & 15 >= G).
+  bf16x8_t qf[4];
+  {
+    const int hl = lane & 15, kq = (lane >> 4) * 8;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qv = ld16(q + ((b * Hq) + g * G + h) * kD + dq);
-    qb[h][0] = qv.x;
-    qb[h][1] = qv.y;
-    qb[h][2] = qv.z;
-    qb[h][3] = qv.w;
+    for (int j = 0; j < 4; ++j) {
+      const uint4 qv = hl < G ? ld16(q + ((b * Hq) + g * G + hl) * kD + 32 * j + kq) : make_uint4(0, 0, 0, 0);
+      qf[j] = as_bf16x8(qv);
+    }
   }
-  float m[G], l[G], o[G][8];
+  float m_lane = kNegInf, l[G], o[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
+  // The wave's probability buffer: its own region of red_o, which it writes
+  // only after the walk (16 G + G floats <= G kD).
+  float* pb = red_o + wave * G * kD;
   const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
   const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
-  if (!poison) attn_tokens<G, U, COUNT>(rows, tb, te, qb, qscale, m, l, o, lane, nbytes);
+  if (!poison) attn_tokens<G, U, COUNT>(rows, tb, te, qf, qscale, m_lane, l, o, lane, pb, nbytes);
 
-  // Merge the four lane groups (xor 16, then xor 32).
+  // Every head's running max, from the lane that holds it (lane h, h < G).
+  float m[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) m[h] = __shfl(m_lane, h, 64);
+  // Merge the four lane groups (xor 16, then xor 32); they share each head's
+  // max, so the merge's factors are exp2(0) = 1.
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
     float m2[G], l2[G], o2[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      m2[h] = __shfl_xor(m[h], off, 64);
+      m2[h] = m[h];
       l2[h] = __shfl_xor(l[h], off, 64);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o2[h][e] = __shfl_xor(o[h][e], off, 64);
     }
     merge_state<G>(m, l, o, m2, l2, o2);
   }
+  __syncthreads();   // every wave's walk, and so its use of the probability buffer, is done
   // Lanes 0..15 hold the wave's state for dims 8*lane .. +7.
   if (lane < 16) {
 #pragma unroll

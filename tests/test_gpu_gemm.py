@@ -240,6 +240,27 @@ def test_wide_n_edge_shapes(M, K, m, N):
     assert torch.equal(y, run(A, X, m, 0))
 
 
+@pytest.mark.parametrize("M", [1024, 4160, 5184, 6208, 7232])
+def test_wide_n_every_hbm_tile_height_bit_identical(M):
+    # With N = 2000 (8 column tiles) and no host rows these M take HBM tiles
+    # of 128, 160, 192, 224 and 256 rows (the schedule's choice, pinned by the
+    # CPU schedule check); host shares change the HBM rows and so the height.
+    # K = 1000 is ragged against the 32-k step.  Sampled rows against the
+    # oracle; every split bit-identical to the all-HBM output.
+    K, N, m = 1000, 2000, 64
+    A, X = synth.gemm_inputs(M, K, N, seed=120 + M // 64)
+    g = torch.Generator().manual_seed(M)
+    rows = sorted(set(torch.randperm(M, generator=g)[:60].tolist()) | {0, 127, 128, M - 1})
+    ref = og.gemm_rows(og.to_f64(A[rows]), og.to_f64(X))
+    n = M // m
+    outs = [run(A, X, m, h) for h in (0, 1, 5, n // 2, n)]
+    err = og.normwise_error(outs[0][:, rows].numpy(), ref)
+    print(f"M={M} sampled normwise error {err:.3e}")
+    assert err <= TOL
+    for y in outs[1:]:
+        assert torch.equal(y, outs[0])
+
+
 def test_wide_n_bytes_requested_per_column_tile():
     M, K, N, h = 1024, 1024, 512, 7
     A, X = synth.gemm_inputs(M, K, N, seed=110)

@@ -106,6 +106,38 @@ int main() {
   CHECK(tiled_choose_groups(256, 8, 45 * 64, (28672 - 45 * 64 + 255) / 256, 8192, 1 << 20) == 6, "h=45");
   CHECK(tiled_choose_groups(256, 8, 52 * 64, (28672 - 52 * 64 + 255) / 256, 8192, 1 << 20) == 7, "h=52");
   CHECK(tiled_choose_groups(256, 8, 59 * 64, (28672 - 59 * 64 + 255) / 256, 8192, 1 << 20) == 8, "h=59");
+  // HBM tile height: within [4, 8]; never a costlier round plan than the
+  // 256-row tile under the model; on the prefill-style shapes (N = 2048,
+  // 256 CUs, no host rows) the heights the sweep measured fastest: M = 28672
+  // -> 224 rows (4 full rounds instead of 3.5), 10240 -> 160, 14336 -> 224,
+  // 8192 -> 256 (one full round already).
+  for (int cus : {256, 32, 80, 304})
+    for (int tn = 2; tn <= 8; ++tn)
+      for (int g : {0, 1, 3})
+        for (int64_t rows : {0, 1, 64, 255, 4096, 10240, 28672, 100000}) {
+          if (g > tiled_max_groups(cus, tn)) continue;
+          const int rb = tiled_choose_rb(cus, tn, g, rows);
+          CHECK(rb >= kTiledRbMin && rb <= kTiledRbMax, "cus=%d tn=%d g=%d rows=%lld rb=%d", cus, tn, g,
+                (long long)rows, rb);
+          if (rows > 0) {
+            auto cost = [&](int r) {
+              return (double)tiled_hbm_rounds(cus, tn, g, (rows + 32 * r - 1) / (32 * r) * tn) * (r + kTiledRbFixed);
+            };
+            CHECK(cost(rb) <= cost(kTiledRbMax), "rows=%lld rb=%d", (long long)rows, rb);
+          }
+        }
+  CHECK(tiled_choose_rb(256, 8, 0, 0) == 8, "no HBM rows");
+  CHECK(tiled_choose_rb(256, 8, 0, 28672) == 7, "28672");
+  CHECK(tiled_choose_rb(256, 8, 0, 10240) == 5, "10240");
+  CHECK(tiled_choose_rb(256, 8, 0, 14336) == 7, "14336");
+  CHECK(tiled_choose_rb(256, 8, 0, 8192) == 8, "8192");
+  // the all-HBM shapes of the GPU test that runs every tile height
+  CHECK(tiled_choose_rb(256, 8, 0, 1024) == 4 && tiled_choose_rb(256, 8, 0, 4160) == 5 &&
+            tiled_choose_rb(256, 8, 0, 5184) == 6 && tiled_choose_rb(256, 8, 0, 6208) == 7 &&
+            tiled_choose_rb(256, 8, 0, 7232) == 8,
+        "GPU test shapes");
+  CHECK(tiled_hbm_rounds(256, 8, 0, 896) == 4 && tiled_hbm_rounds(256, 8, 0, 1024) == 4 &&
+            tiled_hbm_rounds(256, 8, 0, 1025) == 5, "rounds");
   // The XCD layout of MI355X: 8 x 32 CUs.
   CHECK(tiled_xcds(256) == 8 && tiled_max_groups(256, 8) == 24 && tiled_max_groups(256, 2) == 120, "MI355X layout");
   std::printf("%d configurations, %d failures\n", n, fails);

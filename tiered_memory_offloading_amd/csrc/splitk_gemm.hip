@@ -512,6 +512,7 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
                   (long long)N, tn);
     t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, (M - host_rows + 255) / 256, K,
                                      std::max(1, lc.host_cus / tn));
+    t.hbm_rb = tiled_choose_rb(t.cus, tn, t.n_groups, M - host_rows);
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.xcc_masks = (lc.flags & DAK_FLAG_RECORD_XCC) ? t.counters + 2 : nullptr;
     t.stream = static_cast<hipStream_t>(stream);

@@ -13,14 +13,17 @@
 // Both roles follow exactly this sequence, so results are bit-identical for
 // any host/HBM split.
 //
-// Both roles compute 256 x 256 output tiles with 8 waves of 128 x 64 (8 x 4
-// MFMA blocks each), K in 32-k steps staged through LDS by the DMA form of the
-// load.  HBM tiles: a ring of 4 one-step slots, three steps in flight behind
-// the one consumed.  Host tiles: the link moves long row pieces far better
-// than short ones (256 rows x 64 bytes at a time top out near 37 GB/s, 256
-// bytes per row reach the link's 57 GB/s), so A arrives in super-steps of 4
-// k-steps (256 bytes per row) through two 64 KiB super-slots, x in one-step
-// slots.  Only the staging differs; the MFMA sequence is the same.
+// Both roles compute output tiles of 256 columns with 8 waves in a 2 x 4 grid,
+// K in 32-k steps staged through LDS by the DMA form of the load.  HBM tiles
+// are 32 rb rows high (rb in 4 .. 8, chosen per launch so the last round of
+// tiles is not half empty; each wave 16 rb x 64) and stream through a ring of
+// 4 one-step slots, three steps in flight behind the one consumed.  Host
+// tiles are 256 rows high: the link moves long row pieces far better than
+// short ones (256 rows x 64 bytes at a time top out near 37 GB/s, 256 bytes
+// per row reach the link's 57 GB/s), so A arrives in super-steps of 4 k-steps
+// (256 bytes per row) through two 64 KiB super-slots, x in one-step slots.
+// Only the staging and the tile height differ; the MFMA sequence of an
+// element is the same.
 //
 // Scheduling: one work-group per CU (the LDS rings admit no second), and
 // work-group b runs on XCD b % n_xcd.  A CU belongs to one role for the whole
@@ -78,23 +81,26 @@ __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
 // HBM role
 // ---------------------------------------------------------------------------
 // Slot layout: row r (A rows 0..255, then x rows 0..255) holds the step's 32
-// k values as four 16-byte pieces, piece p at position p ^ ((r >> 2) & 3): the
-// 16 lanes that read one MFMA fragment (16 consecutive rows, one piece) then
-// hit 16 different bank groups.
-__device__ __forceinline__ int slot_pos(int r, int piece) { return r * kSlotRow + ((piece ^ ((r >> 2) & 3)) << 4); }
+// k values as four 16-byte pieces, piece p at position p ^ (2 ((r >> 2) & 1)).
+// A fragment read (16 consecutive rows, one piece per group of 16 lanes) then
+// runs at the LDS's full 256 bytes per clock on gfx950; the swizzle
+// p ^ ((r >> 2) & 3), or none, halves that (measured with ds_read_b128 over
+// these lane patterns).
+__device__ __forceinline__ int slot_swz(int r) { return (r >> 1) & 2; }
+__device__ __forceinline__ int slot_pos(int r, int piece) { return r * kSlotRow + ((piece ^ slot_swz(r)) << 4); }
 
 // Per-lane source of this wave's DMA instructions.  Instruction j of wave w
 // moves slot rows 16 (4 (w & 3) + j) .. +15 of A (waves 0-3) or of x (waves
 // 4-7); lane l writes row + l / 4, position l & 3, i.e. global piece
-// (l & 3) ^ ((row >> 2) & 3).  Rows past the matrix read row 0 of the tile
-// (never stored).
+// (l & 3) ^ slot_swz(row).  A rows at or past the tile height `bm` or the
+// matrix's P rows, and x rows past N, read row 0 of the tile (never stored).
 struct TileDma {
   const uint16_t* src[kDmaPerWave];
   int piece[kDmaPerWave];
   bool counted[kDmaPerWave];
 };
 
-__device__ __forceinline__ TileDma tile_dma(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+__device__ __forceinline__ TileDma tile_dma(const uint16_t* __restrict__ a, int64_t P, int64_t row0, int bm,
                                             const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
                                             int wave, int lane) {
   TileDma d;
@@ -102,9 +108,9 @@ __device__ __forceinline__ TileDma tile_dma(const uint16_t* __restrict__ a, int6
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
     const int r = 16 * (4 * (wave & 3) + j) + (lane >> 2);
-    d.piece[j] = (lane & 3) ^ ((r >> 2) & 3);
+    d.piece[j] = (lane & 3) ^ slot_swz(r);
     const int64_t g = (is_a ? row0 : col0) + r;
-    const bool in = g < (is_a ? P : N);
+    const bool in = is_a ? (r < bm && g < P) : g < N;
     d.src[j] = (is_a ? a : x) + (in ? g : (is_a ? row0 : col0)) * K + d.piece[j] * 8;
     d.counted[j] = is_a && in;
   }
@@ -136,13 +142,13 @@ __device__ __forceinline__ void tile_issue(const TileDma& d, int64_t s, int64_t 
 }
 
 // One k-step from slots `sa` (A rows) and `sx` (x rows) for wave (wm, wn):
-// 8 x 4 MFMA blocks.  MASK zeroes the fragments of k at or past K (a partial
-// last step).
+// RB x 4 MFMA blocks (wave rows 16 RB wm .. +16 RB).  MASK zeroes the
+// fragments of k at or past K (a partial last step).
 // WIDE: `sa` is a host super-slot (rows of 256 bytes, 16-byte position
 // p ^ (row & 15) holding piece p) and `ss` the step within it.
-template <bool MASK, bool WIDE>
+template <bool MASK, bool WIDE, int RB>
 __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigned char* sx, int ss, int wm, int wn,
-                                          int lane, bool kok, f32x4_t (&acc)[8][4]) {
+                                          int lane, bool kok, f32x4_t (&acc)[RB][4]) {
   const int i16 = lane & 15, g = lane >> 4;
   uint4 bf[4];
 #pragma unroll
@@ -151,8 +157,8 @@ __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigne
     if (MASK && !kok) bf[cb] = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int rb = 0; rb < 8; ++rb) {
-    const int ra = wm * 128 + rb * 16 + i16;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int ra = wm * 16 * RB + rb * 16 + i16;
     uint4 af = WIDE ? *reinterpret_cast<const uint4*>(sa + ra * kSuperRow + (((kSuper * ss + g) ^ i16) << 4))
                     : *reinterpret_cast<const uint4*>(sa + slot_pos(ra, g));
     if (MASK && !kok) af = make_uint4(0, 0, 0, 0);
@@ -161,14 +167,16 @@ __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigne
   }
 }
 
-// Write a finished tile: rows below P, columns below N.
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[8][4], int64_t P, int64_t row0, int64_t N,
+// Write a finished tile (wave rows 16 RB wm .. +16 RB): rows below P,
+// columns below N.
+template <int RB>
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[RB][4], int64_t P, int64_t row0, int64_t N,
                                            int64_t col0, int64_t M, int64_t yrow0, float* __restrict__ y, int wm,
                                            int wn, int lane) {
   const int i16 = lane & 15, r4 = 4 * (lane >> 4);
 #pragma unroll
-  for (int rb2 = 0; rb2 < 8; ++rb2) {
-    const int64_t row = row0 + wm * 128 + rb2 * 16 + r4;
+  for (int rb2 = 0; rb2 < RB; ++rb2) {
+    const int64_t row = row0 + wm * 16 * RB + rb2 * 16 + r4;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int64_t n = col0 + wn * 64 + cb * 16 + i16;
@@ -189,11 +197,12 @@ __device__ __forceinline__ void wait_step(int64_t later) {
   }
 }
 
-// HBM tile: output rows [row0, row0 + 256) of the P rows at `a` (written at y
-// rows yrow0 + row), columns [col0, col0 + 256).  A ring of kHbmStages slots,
-// each one step of A rows followed by one step of x rows.  RAGGED: K is not a
-// multiple of 32, so the last step is partial.
-template <bool COUNT, bool RAGGED>
+// HBM tile: output rows [row0, row0 + 32 RB) of the P rows at `a` (written
+// at y rows yrow0 + row), columns [col0, col0 + 256).  A ring of kHbmStages
+// slots, each one step of A rows followed by one step of x rows (A rows past
+// the tile height are fetched but never read).  RAGGED: K is not a multiple
+// of 32, so the last step is partial.
+template <bool COUNT, bool RAGGED, int RB>
 __device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
                                      const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t M,
                                      int64_t yrow0, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
@@ -201,13 +210,13 @@ __device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int half = wave < 4 ? 0 : kSlotA;   // waves 0-3 move A rows, 4-7 x rows
-  f32x4_t acc[8][4];
+  f32x4_t acc[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < 8; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t T = (K + 31) >> 5;
-  const TileDma d = tile_dma(a, P, row0, x, N, col0, K, wave, lane);
+  const TileDma d = tile_dma(a, P, row0, 32 * RB, x, N, col0, K, wave, lane);
 #pragma unroll
   for (int s = 0; s < kHbmStages - 1; ++s)
     if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, lds + s * kSlot + half, wave, nbytes);
@@ -221,10 +230,10 @@ __device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, 
     if (s + kHbmStages - 1 < T)
       tile_issue<COUNT, RAGGED>(d, s + kHbmStages - 1, K,
                                 lds + ((slot + kHbmStages - 1) & (kHbmStages - 1)) * kSlot + half, wave, nbytes);
-    tile_step<RAGGED, false>(lds + slot * kSlot, lds + slot * kSlot + kSlotA, 0, wm, wn, lane,
-                             32 * s + 8 * (lane >> 4) < K, acc);
+    tile_step<RAGGED, false, RB>(lds + slot * kSlot, lds + slot * kSlot + kSlotA, 0, wm, wn, lane,
+                                 32 * s + 8 * (lane >> 4) < K, acc);
   }
-  store_tile(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane);
+  store_tile<RB>(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane);
 }
 
 // Host super-step S (k in [128 S, 128 S + 128)) of A-wave w's 64 rows into a
@@ -264,7 +273,7 @@ __device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t T = (K + 31) >> 5, TS = (T + kSuper - 1) / kSuper;
-  const TileDma d = tile_dma(a, P, row0, x, N, col0, K, wave, lane);   // x waves use it
+  const TileDma d = tile_dma(a, P, row0, kBM, x, N, col0, K, wave, lane);   // x waves use it
   unsigned char* const ring_a = lds;
   unsigned char* const ring_x = lds + 2 * kSuperSlot;
   if (is_a) {
@@ -296,14 +305,14 @@ __device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_
         tile_issue<COUNT, RAGGED>(d, s + kHostSX - 1, K, ring_x + (rx == 0 ? kHostSX - 1 : rx - 1) * kSlotA, wave,
                                   nbytes);
     }
-    tile_step<RAGGED, true>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
+    tile_step<RAGGED, true, 8>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
                             32 * s + 8 * (lane >> 4) < K, acc);
     rx = rx == kHostSX - 1 ? 0 : rx + 1;
   }
-  store_tile(acc, P, row0, N, col0, M, 0, y, wm, wn, lane);
+  store_tile<8>(acc, P, row0, N, col0, M, 0, y, wm, wn, lane);
 }
 
-template <bool COUNT, bool RAGGED>
+template <bool COUNT, bool RAGGED, int RB>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int n_groups, int cus,
@@ -311,8 +320,9 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
   const int tn = (int)((N + kBN - 1) / kBN);
+  constexpr int kHbmRows = 32 * RB;
   const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, (host_rows + kBM - 1) / kBM,
-                                 (M - host_rows + kBM - 1) / kBM * tn);
+                                 (M - host_rows + kHbmRows - 1) / kHbmRows * tn);
   const bool host_role = w.host;
   // Where the schedule's placement assumption can be checked: each host
   // work-group ORs the bit of the XCD it runs on (the hardware's XCC id
@@ -331,7 +341,8 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   } else {
     for (int64_t t = w.first; t < w.end; t += w.stride) {
       __syncthreads();   // the ring is reused
-      tile<COUNT, RAGGED>(a_hbm, M - host_rows, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, lds, nbytes);
+      tile<COUNT, RAGGED, RB>(a_hbm, M - host_rows, t / tn * kHbmRows, x, N, t % tn * kBN, K, M, host_rows, y, lds,
+                              nbytes);
     }
   }
   if (COUNT) {
@@ -347,11 +358,11 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
 
 int tiled_max_host_groups(int64_t N, int cus) { return tiled_max_groups(cus, (int)((N + kBN - 1) / kBN)); }
 
-void launch_gemm_tiled(const TiledArgs& g, bool count) {
-  const int n_xcd = tiled_xcds(g.cus);
+template <int RB>
+static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
   const bool ragged = (g.K & 31) != 0;
-#define DAK_TILED(C, R)                                                                                          \
-  hipLaunchKernelGGL((gemm_tiled_split<C, R>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host, g.a_hbm, \
+#define DAK_TILED(C, R)                                                                                              \
+  hipLaunchKernelGGL((gemm_tiled_split<C, R, RB>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host, g.a_hbm, \
                      g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.counters, g.xcc_masks)
   if (count) {
     if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
@@ -359,6 +370,18 @@ void launch_gemm_tiled(const TiledArgs& g, bool count) {
     if (ragged) DAK_TILED(false, true); else DAK_TILED(false, false);
   }
 #undef DAK_TILED
+}
+
+void launch_gemm_tiled(const TiledArgs& g, bool count) {
+  const int n_xcd = tiled_xcds(g.cus);
+  static_assert(kTiledRbMin == 4 && kTiledRbMax == 8, "one instance per HBM tile height");
+  switch (g.hbm_rb) {
+    case 4: return launch_rb<4>(g, count, n_xcd);
+    case 5: return launch_rb<5>(g, count, n_xcd);
+    case 6: return launch_rb<6>(g, count, n_xcd);
+    case 7: return launch_rb<7>(g, count, n_xcd);
+    default: return launch_rb<8>(g, count, n_xcd);
+  }
 }
 
 }  // namespace dak

@@ -77,14 +77,31 @@ inline constexpr TiledCost kTiledCostMi355x{0.92, 10.0, 55.0};
 
 constexpr double tiled_max_d(double a, double b) { return a > b ? a : b; }
 
+// Rounds of HBM tiles: each XCD's HBM work-groups run their share of `tiles`
+// (split in proportion to their number, as tiled_work does) in whole rounds
+// of one tile each; the launch lasts as long as its slowest XCD.
+constexpr int64_t tiled_hbm_rounds(int cus, int tn, int n_groups, int64_t tiles) {
+  const int n_xcd = tiled_xcds(cus);
+  int64_t total = 0;
+  for (int v = 0; v < n_xcd; ++v) total += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+  int64_t rounds = 0, before = 0;
+  for (int v = 0; v < n_xcd; ++v) {
+    const int64_t w = tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+    const int64_t share = tiles * (before + w) / total - tiles * before / total;
+    before += w;
+    const int64_t r = (share + w - 1) / w;
+    rounds = r > rounds ? r : rounds;
+  }
+  return rounds;
+}
+
 // Predicted microseconds of a launch with `n_groups` host groups: host row
 // blocks go round by round to the groups (a round lasts as long as a tile, as
 // one group's stream of a block, or as the link needs for all active groups'
 // blocks, whichever is longest); each XCD's HBM work-groups run their share
-// of the HBM tiles in whole rounds of one tile.
+// of the HBM tiles (here of 256 rows) in whole rounds of one tile.
 constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_row_tiles, int64_t K,
                                   TiledCost c) {
-  const int n_xcd = tiled_xcds(cus);
   const double t_tile = (double)((K + 31) / 32) * c.step_us;
   const double block_bytes = 256.0 * (double)K * 2.0;
   double t_host = 0.0;
@@ -95,18 +112,34 @@ constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_ro
                                               (double)active * block_bytes / (c.link_gbps * 1e3)));
     left -= active;
   }
-  const int64_t tiles = hbm_row_tiles * tn;
-  int64_t total = 0;
-  for (int v = 0; v < n_xcd; ++v) total += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
-  double t_hbm = 0.0;
-  int64_t before = 0;
-  for (int v = 0; v < n_xcd; ++v) {
-    const int64_t w = tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
-    const int64_t share = tiles * (before + w) / total - tiles * before / total;
-    before += w;
-    t_hbm = tiled_max_d(t_hbm, (double)((share + w - 1) / w) * t_tile);
-  }
+  const double t_hbm = (double)tiled_hbm_rounds(cus, tn, n_groups, hbm_row_tiles * tn) * t_tile;
   return tiled_max_d(t_host, t_hbm);
+}
+
+// Height of the HBM role's tiles: 32 rb rows, rb in [kTiledRbMin, 8].  On
+// MI355X a round of such tiles takes time in proportion to rb + 4 (measured
+// with N = 2048, K = 8192 and M = 10240, 14336 and 28672: the x rows, the
+// barrier and the DMA issue do not shrink with the tile), so a shorter tile
+// pays only where it evens out the last round: the rb with the least
+// rounds * (rb + 4), the tallest on ties.  256-row blocks of host rows keep
+// their height; the choice only places work (every output element is the
+// same sum of the same MFMAs for any tile height).
+constexpr int kTiledRbMin = 4, kTiledRbMax = 8;
+constexpr double kTiledRbFixed = 4.0;
+constexpr int tiled_choose_rb(int cus, int tn, int n_groups, int64_t hbm_rows) {
+  if (hbm_rows <= 0) return kTiledRbMax;
+  int best = kTiledRbMax;
+  double best_c = 0.0;
+  for (int rb = kTiledRbMax; rb >= kTiledRbMin; --rb) {
+    const int64_t rows = 32 * (int64_t)rb;
+    const double c = (double)tiled_hbm_rounds(cus, tn, n_groups, (hbm_rows + rows - 1) / rows * tn) *
+                     ((double)rb + kTiledRbFixed);
+    if (rb == kTiledRbMax || c < best_c * (1.0 - 1e-9)) {
+      best = rb;
+      best_c = c;
+    }
+  }
+  return best;
 }
 
 // Host groups for a launch: the count in [1, cap] (and at most one per host

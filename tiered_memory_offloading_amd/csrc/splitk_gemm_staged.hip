@@ -9,9 +9,10 @@
 // (global_load_lds_dwordx4), which moves 16 bytes per lane straight into LDS
 // without passing through registers.
 //
-// Work item: R = 16 * RB rows x all K x all N.  K is read in chunks of 256
-// (512 contiguous bytes per row: the host link needs long row pieces, and HBM
-// streams them at full rate).  Each chunk of A rows and of the N activation
+// Work item: R = 16 * RB rows x all K x all N.  K is read in chunks of KC =
+// 256 (512 contiguous bytes per row: the host link needs long row pieces, and
+// HBM streams them at full rate), or of 128 for launches without a host role
+// whose 256-k slots would leave one work-group per CU (see launch_nb_rb).  Each chunk of A rows and of the N activation
 // rows is DMA-ed into one slot of an LDS ring of STAGES slots; STAGES - 1
 // chunks are in flight while one is consumed.  The ring depth depends on the
 // shape only (the window of the launch configuration does not apply here); the
@@ -43,25 +44,29 @@ namespace {
 
 constexpr int kSWaves = 4;
 constexpr int kSThreads = 64 * kSWaves;
-constexpr int kKC = 256;                 // k per chunk
-constexpr int kRowB = kKC * 2;           // bytes per staged row
-constexpr int kStepsPerChunk = kKC / 32;
+constexpr int kKC = 256;                 // k per chunk (default)
+constexpr int kRowB = kKC * 2;           // bytes per staged row (default)
 
-template <int NB, int RB>
+template <int NB, int RB, int KC = kKC>
 struct StagedShape {
+  static_assert(KC == 128 || KC == 256, "a chunk is 4 or 8 k-steps");
+  static constexpr int ROWB = KC * 2;               // bytes per staged row
+  static constexpr int LPR = ROWB / 16;             // DMA lanes per staged row
+  static constexpr int STEPS = KC / 32;             // k-steps per chunk
   static constexpr int R = 16 * RB;                 // A rows per item
   static constexpr int ROWS = R + 16 * NB;          // staged rows per chunk (A, then x)
-  static constexpr int SLOT = ROWS * kRowB;         // bytes per LDS slot
+  static constexpr int SLOT = ROWS * ROWB;          // bytes per LDS slot
   static constexpr int INSTR = SLOT / 1024;         // 1 KiB DMA instructions per slot
   static constexpr int PER_WAVE = INSTR / kSWaves;  // per wave per chunk
   static constexpr int P = kSWaves / RB;            // k-phases
   static_assert(INSTR % kSWaves == 0, "every wave issues the same number of DMA instructions");
   static_assert(PER_WAVE * 2 <= 63, "vmcnt range");
+  static_assert(STEPS % (kSWaves / RB) == 0, "every wave's k-phase recurs in each chunk");
 };
 
-template <int NB, int RB, bool COUNT>
+template <int NB, int RB, bool COUNT, int KC = kKC>
 struct StagedItem {
-  using S = StagedShape<NB, RB>;
+  using S = StagedShape<NB, RB, KC>;
 
   // DMA chunk c of the item whose first A row is `a` into `slot`.  Pieces past
   // K and activation rows past N are fetched from an in-bounds address and
@@ -75,9 +80,9 @@ struct StagedItem {
 #pragma unroll
     for (int j = 0; j < S::PER_WAVE; ++j) {
       const int ins = spread ? wave + kSWaves * j : wave * S::PER_WAVE + j;
-      const int r = 2 * ins + (lane >> 5);
-      const int piece = (lane & 31) ^ (r & 15);
-      const int64_t k = c * kKC + piece * 8;
+      const int r = (64 / S::LPR) * ins + lane / S::LPR;
+      const int piece = (lane % S::LPR) ^ (r & 15);
+      const int64_t k = c * KC + piece * 8;
       const int64_t kk = k < K ? k : 0;
       const uint16_t* src;
       if (r < S::R) {
@@ -97,16 +102,16 @@ struct StagedItem {
     const int i16 = lane & 15, g = lane >> 4;
     const int ra = 16 * rb + i16;
 #pragma unroll
-    for (int t = 0; t < kStepsPerChunk; ++t) {
+    for (int t = 0; t < S::STEPS; ++t) {
       if (t % S::P != phase) continue;   // uniform
-      const bool kok = c * kKC + 32 * t + 8 * g < K;
+      const bool kok = c * KC + 32 * t + 8 * g < K;
       const int pc = 4 * t + g;
-      uint4 af = *reinterpret_cast<const uint4*>(slot + ra * kRowB + ((pc ^ (ra & 15)) << 4));
+      uint4 af = *reinterpret_cast<const uint4*>(slot + ra * S::ROWB + ((pc ^ (ra & 15)) << 4));
       if (!kok) af = make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         const int rx = S::R + 16 * cb + i16;
-        uint4 xf = *reinterpret_cast<const uint4*>(slot + rx * kRowB + ((pc ^ (rx & 15)) << 4));
+        uint4 xf = *reinterpret_cast<const uint4*>(slot + rx * S::ROWB + ((pc ^ (rx & 15)) << 4));
         if (!kok) xf = make_uint4(0, 0, 0, 0);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc[cb], 0, 0, 0);
       }
@@ -128,21 +133,21 @@ __device__ __forceinline__ void vm_wait_chunks(int64_t later) {
   vm_wait<0>();
 }
 
-template <int NB, int RB, int STAGES, bool COUNT>
+template <int NB, int RB, int STAGES, bool COUNT, int KC = kKC>
 __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ a_stage, int64_t stage_rows, const uint16_t* __restrict__ x,
     int64_t N, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
     unsigned long long* __restrict__ counters) {
-  using S = StagedShape<NB, RB>;
-  using I = StagedItem<NB, RB, COUNT>;
+  using S = StagedShape<NB, RB, KC>;
+  using I = StagedItem<NB, RB, COUNT, KC>;
   // The ring: STAGES slots of one array; chunk c lives in slot c % STAGES.
   __shared__ __attribute__((aligned(16))) unsigned char ring[STAGES * S::SLOT];
   unsigned char* const s0 = ring;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rb = wave % RB, phase = wave / RB;
-  const int64_t nch = (K + kKC - 1) / kKC;
+  const int64_t nch = (K + KC - 1) / KC;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
   // Spread DMA instructions over the waves, except in host work-groups of
@@ -249,10 +254,10 @@ bool deep_ring(int nb, int rb, const StagedArgs& g) {
          g.host_wgs + g.hbm_items <= g.cus;
 }
 
-template <int NB, int RB, int ST, bool COUNT>
+template <int NB, int RB, int ST, bool COUNT, int KC = kKC>
 void launch_nb_rb_st(const StagedArgs& g) {
   const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
+  hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT, KC>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.N, g.y, g.host_wgs,
                      g.host_items, g.hbm_items, g.counters);
 }
@@ -302,6 +307,15 @@ bool launch_deepest(const StagedArgs& g) {
 template <int NB, int RB, bool COUNT>
 void launch_nb_rb(const StagedArgs& g) {
   constexpr int ST = stages_for(NB, RB);
+  // Without a host role, 64 activation rows and 64-row items: two slots of
+  // 256-k chunks take 128 KiB, one work-group per CU with one chunk in flight.
+  // Chunks of 128 k halve the slots, so two work-groups share each CU (and the
+  // items of the 28672-row gate+up, 1.75 per CU, all start at once): measured
+  // 57 us against 73-80 us at x = 0.  At N <= 32 and for shorter items 128-k
+  // chunks measured slower (more barriers per byte), so they keep 256.
+  if constexpr (NB == 4 && RB == 4) {
+    if (g.host_wgs == 0) return launch_nb_rb_st<NB, RB, 2, COUNT, 128>(g);
+  }
   if (g.host_wgs > 0) {
     if (launch_deepest<NB, RB, ST + 1, COUNT>(g)) return;
   } else if constexpr (ST == 2 && stages_fit<NB, RB, 3>()) {

@@ -16,8 +16,9 @@
 // Both roles compute output tiles of 256 columns with 8 waves in a 2 x 4 grid,
 // K in 32-k steps staged through LDS by the DMA form of the load.  HBM tiles
 // are 32 rb rows high (rb in 4 .. 8, chosen per launch so the last round of
-// tiles is not half empty; each wave 16 rb x 64) and stream through a ring of
-// 4 one-step slots, three steps in flight behind the one consumed.  Host
+// tiles is not half empty; each wave 16 rb x 64) and stream through two slots
+// of 64-k steps (128 bytes per row), one step in flight behind the one
+// consumed; each step is two 32-k MFMA substeps.  Host
 // tiles are 256 rows high: the link moves long row pieces far better than
 // short ones (256 rows x 64 bytes at a time top out near 37 GB/s, 256 bytes
 // per row reach the link's 57 GB/s), so A arrives in super-steps of 4 k-steps
@@ -58,10 +59,14 @@ constexpr int kSlotA = kBM * kSlotRow;       // one step of A rows (or of x rows
 static_assert(kBN == kBM, "A and x slots have one size");
 constexpr int kDmaPerWave = 2 * kSlotA / 1024 / kTW;   // 1 KiB DMA instructions per wave per step
 static_assert(kDmaPerWave * kTW * 1024 == 2 * kSlotA, "the waves split a step's DMA evenly");
-// HBM tiles: a ring of 4 one-step slots (A rows, then x rows), three steps in
-// flight behind the one consumed.
-constexpr int kHbmStages = 4;
-static_assert((kHbmStages & (kHbmStages - 1)) == 0, "ring depth is a power of two");
+// HBM tiles: two slots of one 64-k step each (A rows, then x rows, 128
+// bytes per row: every DMA request a whole 128-byte line), one step in flight
+// behind the one consumed.
+constexpr int kHbmRow = 128;                          // bytes per staged row: one 64-k step
+constexpr int kHbmSlotA = kBM * kHbmRow;              // 32 KiB: one step of 256 rows
+constexpr int kHbmStages = 2;
+constexpr int kHbmDmaPerWave = 2 * kHbmSlotA / 1024 / kTW;   // 8
+static_assert(kHbmDmaPerWave * kTW * 1024 == 2 * kHbmSlotA, "the waves split a step's DMA evenly");
 // Host tiles: the link needs long pieces of each row (with 64- or 128-byte
 // pieces from 256 rows at once it tops out near 37 GB/s; from 256 bytes on it
 // reaches its 57 GB/s), so A moves in super-steps of 4 k-steps, 256 bytes per
@@ -71,7 +76,7 @@ constexpr int kSuperRow = kSuper * kSlotRow;   // 256 bytes
 constexpr int kSuperSlot = kBM * kSuperRow;    // 64 KiB
 constexpr int kHostSX = 2;
 constexpr int kLds = 2 * kSuperSlot + kHostSX * kSlotA;   // 160 KiB
-static_assert(kHbmStages * 2 * kSlotA <= kLds, "the HBM ring fits");
+static_assert(kHbmStages * 2 * kHbmSlotA <= kLds, "the HBM ring fits");
 
 __device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -197,41 +202,107 @@ __device__ __forceinline__ void wait_step(int64_t later) {
   }
 }
 
+// HBM ring layout: row r (A rows 0..255, then x rows 0..255) holds the
+// step's 64 k values as eight 16-byte pieces, piece p at position p ^ (r & 7);
+// a fragment read (16 consecutive rows, one piece per group of 16 lanes) runs
+// at the LDS's full rate (measured over this lane pattern).
+__device__ __forceinline__ int hbm_pos(int r, int piece) { return r * kHbmRow + ((piece ^ (r & 7)) << 4); }
+
+// Per-lane source of this wave's HBM DMA instructions.  Instruction j of wave
+// w moves slot rows 64 (w & 3) + 8 j .. +7 of A (waves 0-3) or of x (waves
+// 4-7); lane l writes row + l / 8, position l & 7, i.e. global piece
+// (l & 7) ^ (row & 7) = (l & 7) ^ (l >> 3).  A rows at or past the tile height
+// or the matrix's P rows, and x rows past N, read the tile's first row (never
+// stored).
+struct HbmDma {
+  const uint16_t* src[kHbmDmaPerWave];
+  bool counted[kHbmDmaPerWave];
+  int piece;
+};
+
+__device__ __forceinline__ HbmDma hbm_dma(const uint16_t* __restrict__ a, int64_t P, int64_t row0, int bm,
+                                          const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
+                                          int wave, int lane) {
+  HbmDma d;
+  const bool is_a = wave < 4;
+  d.piece = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+  for (int j = 0; j < kHbmDmaPerWave; ++j) {
+    const int r = 64 * (wave & 3) + 8 * j + (lane >> 3);
+    const int64_t g = (is_a ? row0 : col0) + r;
+    const bool in = is_a ? (r < bm && g < P) : g < N;
+    d.src[j] = (is_a ? a : x) + (in ? g : (is_a ? row0 : col0)) * K + d.piece * 8;
+    d.counted[j] = is_a && in;
+  }
+  return d;
+}
+
+// DMA 64-k step s of this wave's rows into `slot` (the half of a ring slot
+// that holds them).  Pieces at or past K (only in a partial last step) are
+// fetched from column 0 (in bounds) and zeroed where they are read.
+template <bool COUNT, bool RAGGED>
+__device__ __forceinline__ void hbm_issue(const HbmDma& d, int64_t s, int64_t K, unsigned char* slot, int wave,
+                                          uint64_t& nbytes) {
+  unsigned char* base = slot + 64 * (wave & 3) * kHbmRow;
+  const int64_t k = 64 * s + 8 * d.piece;
+  const bool kin = !RAGGED || k < K;
+#pragma unroll
+  for (int j = 0; j < kHbmDmaPerWave; ++j) {
+    dma16(d.src[j] + (kin ? 64 * s : -8 * d.piece), base + 8 * j * kHbmRow);
+    if (COUNT && kin && d.counted[j]) nbytes += 16;
+  }
+}
+
 // HBM tile: output rows [row0, row0 + 32 RB) of the P rows at `a` (written
-// at y rows yrow0 + row), columns [col0, col0 + 256).  A ring of kHbmStages
-// slots, each one step of A rows followed by one step of x rows (A rows past
-// the tile height are fetched but never read).  RAGGED: K is not a multiple
-// of 32, so the last step is partial.
+// at y rows yrow0 + row), columns [col0, col0 + 256).  Step s (k in
+// [64 s, 64 s + 64)): wait for its DMA (every wave's part, via the barrier,
+// which also retires every read of the other slot), issue step s + 1 into
+// the other slot, then the step's 32-k substeps in order.  A substep at or
+// past K (a last step of at most 32 k) is skipped, so each element sums the
+// same ceil(K / 32) MFMAs as in the host role.  RAGGED: K is not a multiple
+// of 64.
 template <bool COUNT, bool RAGGED, int RB>
 __device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
                                      const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t M,
                                      int64_t yrow0, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
-  constexpr int kSlot = 2 * kSlotA;
+  constexpr int kSlot = 2 * kHbmSlotA;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int half = wave < 4 ? 0 : kSlotA;   // waves 0-3 move A rows, 4-7 x rows
+  const int wm = wave >> 2, wn = wave & 3, i16 = lane & 15, g = lane >> 4;
+  const int half = wave < 4 ? 0 : kHbmSlotA;   // waves 0-3 move A rows, 4-7 x rows
   f32x4_t acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t T = (K + 31) >> 5;
-  const TileDma d = tile_dma(a, P, row0, 32 * RB, x, N, col0, K, wave, lane);
-#pragma unroll
-  for (int s = 0; s < kHbmStages - 1; ++s)
-    if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, lds + s * kSlot + half, wave, nbytes);
-  // Step s: wait for its DMA (every wave's part, via the barrier, which also
-  // retires every read of the slot refilled next), refill that slot with step
-  // s + kHbmStages - 1, then consume step s.
+  const int64_t T = (K + 63) >> 6;
+  const HbmDma d = hbm_dma(a, P, row0, 32 * RB, x, N, col0, K, wave, lane);
+  hbm_issue<COUNT, RAGGED>(d, 0, K, lds + half, wave, nbytes);
   for (int64_t s = 0; s < T; ++s) {
-    wait_step<kHbmStages - 2>(T - 1 - s);
+    vm_wait<0>();
     __builtin_amdgcn_s_barrier();
-    const int slot = (int)(s & (kHbmStages - 1));
-    if (s + kHbmStages - 1 < T)
-      tile_issue<COUNT, RAGGED>(d, s + kHbmStages - 1, K,
-                                lds + ((slot + kHbmStages - 1) & (kHbmStages - 1)) * kSlot + half, wave, nbytes);
-    tile_step<RAGGED, false, RB>(lds + slot * kSlot, lds + slot * kSlot + kSlotA, 0, wm, wn, lane,
-                                 32 * s + 8 * (lane >> 4) < K, acc);
+    const int slot = (int)(s & 1);
+    if (s + 1 < T) hbm_issue<COUNT, RAGGED>(d, s + 1, K, lds + (slot ^ 1) * kSlot + half, wave, nbytes);
+    const unsigned char* sa = lds + slot * kSlot;
+    const unsigned char* sx = sa + kHbmSlotA;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t k = 64 * s + 32 * h;
+      if (RAGGED && k >= K) break;   // uniform
+      const bool kok = k + 8 * g < K;
+      uint4 bf[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        bf[cb] = *reinterpret_cast<const uint4*>(sx + hbm_pos(wn * 64 + cb * 16 + i16, 4 * h + g));
+        if (RAGGED && !kok) bf[cb] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        uint4 af = *reinterpret_cast<const uint4*>(sa + hbm_pos(wm * 16 * RB + rb * 16 + i16, 4 * h + g));
+        if (RAGGED && !kok) af = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
+      }
+    }
   }
   store_tile<RB>(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane);
 }

@@ -754,6 +754,39 @@ def run_linears(torch, dak, args, b_hbm, b_host):
     return 0
 
 
+def run_linears_x0(torch, dak, args, b_hbm, b_host):
+    """The Llama-8B decode linears at x = 0 and N in {16, 64}: each (op, N)
+    launched once on each of three copies of its weights (cold in L2), in a
+    fixed order that the JSON line lists, for counter runs that attribute
+    each dispatch (L2 requests per weight line)."""
+    order, rows = [], {}
+    for oi, (name, M, K) in enumerate(synth.LLAMA8B_LINEARS):
+        A = synth.gemm_inputs(M, K, 1, seed=oi, device="cuda")[0]
+        copies = [A.clone() for _ in range(3)]
+        for N in (16, 64):
+            X = synth.gemm_inputs(M, K, N, seed=oi, device="cuda")[1].contiguous()
+            y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+            ts = []
+            for c in copies:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                dak.splitk_gemm(dak.SplitMatrix(None, c, M, K, M_TILE, 0), X, y=y)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+                order.append(f"{name}_N{N}")
+            rows[f"{name}_N{N}"] = {"us": [round(t * 1e3, 1) for t in ts],
+                                    "GBps_median": round(M * K * 2 / (statistics.median(ts) * 1e6), 1)}
+            del X, y
+        del A, copies
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "x = 0 GB/s of the decode linears, one launch per cold weight copy", "unit": "GB/s",
+                      "n_gpus": 1, "higher_is_better": True, "data": "synthetic (seeded)",
+                      "config": {"workload": "Llama-8B decode linears at x = 0, N in {16, 64}, three cold copies"},
+                      "b_hbm_GBps": round(b_hbm, 1), "dispatch_order": order, "ops": rows}), flush=True)
+    return 0
+
+
 def run_fp8_linears(torch, dak, args, b_hbm, b_host):
     """The Llama-8B decode linears (QKV 6144x4096, O 4096x4096, gate+up
     28672x4096, down 4096x14336) with FP8 weights (e4m3 codes, one fp32 scale
@@ -1141,12 +1174,13 @@ def main(argv=None):
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.5,
                     help="prefill: seconds of sustained x = 0 launches before timing (the clock climbs under load)")
-    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "plan-compare",
-                                           "paged", "fp8-linears", "prefetch"),
+    ap.add_argument("--workload", choices=("llama8b-layer", "llama70b", "prefill", "linears", "linears-x0",
+                                           "plan-compare", "paged", "fp8-linears", "prefetch"),
                     default="llama8b-layer",
                     help="llama70b: the 80-layer 70B-shaped decode step with planner-chosen ratios; prefill: "
                          "the compute-bound 28672x8192x2048 split GEMM; linears: the decode linears one by one "
-                         "at N in {1,16,64} over x = 0..0.5, cold; plan-compare: greedy per-op ratios against a "
+                         "at N in {1,16,64} over x = 0..0.5, cold; linears-x0: each decode linear at x = 0, "
+                         "N in {16, 64}, once per cold weight copy (for counter runs); plan-compare: greedy per-op ratios against a "
                          "uniform ratio for one decoder layer at large batch; paged: paged against dense "
                          "split attention; fp8-linears: the decode linears with FP8 weights; prefetch: direct "
                          "access against copy-based prefetch of the host units, and the copy-interference probe "
@@ -1189,6 +1223,8 @@ def main(argv=None):
         return run_prefill(torch, dak, args, b_hbm, b_host)
     if args.workload == "linears":
         return run_linears(torch, dak, args, b_hbm, b_host)
+    if args.workload == "linears-x0":
+        return run_linears_x0(torch, dak, args, b_hbm, b_host)
     if args.workload == "plan-compare":
         return run_plan_compare(torch, dak, args, b_hbm, b_host)
     if args.workload == "paged":

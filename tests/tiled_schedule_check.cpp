@@ -27,14 +27,14 @@ static int fails = 0;
     }                                    \
   } while (0)
 
-static void check(int cus, int tn, int n_groups, int64_t host_blocks, int64_t hbm_row_tiles) {
+static void check(int cus, int tn, int n_groups, int64_t host_blocks, int64_t hbm_row_tiles, bool reverse) {
   const int n_xcd = tiled_xcds(cus);
   const int64_t hbm_tiles = hbm_row_tiles * tn;
   std::vector<int> host_cover(host_blocks * tn, 0), hbm_cover(hbm_tiles, 0);
   std::map<int, std::set<int>> group_xcd, group_cols;
   std::vector<int64_t> hbm_wgs(n_xcd, 0), hbm_share(n_xcd, 0);
   for (int b = 0; b < cus; ++b) {
-    const TiledWork w = tiled_work(b, cus, n_xcd, n_groups, tn, host_blocks, hbm_tiles);
+    const TiledWork w = tiled_work(b, cus, n_xcd, n_groups, tn, host_blocks, hbm_tiles, reverse);
     const int xcd = b % n_xcd;
     if (w.host) {
       const int q = (int)w.first;
@@ -88,7 +88,8 @@ int main() {
             if (g == 0 && hb > 0) continue;   // host rows always get a group
             if (g > 0 && hb == 0) continue;
             if (g > hb && hb > 0) continue;   // never more groups than row blocks
-            check(cus, tn, g, hb, hr);
+            check(cus, tn, g, hb, hr, false);
+            check(cus, tn, g, hb, hr, true);
             ++n;
           }
     }
@@ -96,48 +97,69 @@ int main() {
   // and, for the 28672 x 8192 x 2048 prefill GEMM on 256 CUs, the counts that
   // measured fastest in the warm paired sweep on MI355X (h tile-rows of 64:
   // h = 45 -> 6 groups, 52 -> 7, 59 -> 8).
-  CHECK(tiled_choose_groups(256, 8, 0, 112, 8192, 64) == 0, "no host rows");
+  CHECK(tiled_choose_groups(256, 8, 0, 28672, 8192, 64) == 0, "no host rows");
   for (int64_t hr : {64, 1000, 2880, 3328, 7168, 28672})
     for (int cap : {1, 2, 5, 100}) {
-      const int g = tiled_choose_groups(256, 8, hr, (28672 - hr + 255) / 256, 8192, cap);
+      const int g = tiled_choose_groups(256, 8, hr, 28672 - hr, 8192, cap);
       CHECK(g >= 1 && g <= cap && g <= (hr + 255) / 256 && g <= tiled_max_groups(256, 8), "hr=%lld cap=%d g=%d",
             (long long)hr, cap, g);
     }
-  CHECK(tiled_choose_groups(256, 8, 45 * 64, (28672 - 45 * 64 + 255) / 256, 8192, 1 << 20) == 6, "h=45");
-  CHECK(tiled_choose_groups(256, 8, 52 * 64, (28672 - 52 * 64 + 255) / 256, 8192, 1 << 20) == 7, "h=52");
-  CHECK(tiled_choose_groups(256, 8, 59 * 64, (28672 - 59 * 64 + 255) / 256, 8192, 1 << 20) == 8, "h=59");
-  // HBM tile height: within [4, 8]; never a costlier round plan than the
-  // 256-row tile under the model; on the prefill-style shapes (N = 2048,
-  // 256 CUs, no host rows) the heights the sweep measured fastest: M = 28672
-  // -> 224 rows (4 full rounds instead of 3.5), 10240 -> 160, 14336 -> 224,
-  // 8192 -> 256 (one full round already).
+  CHECK(tiled_choose_groups(256, 8, 45 * 64, 28672 - 45 * 64, 8192, 1 << 20) == 6, "h=45");
+  CHECK(tiled_choose_groups(256, 8, 52 * 64, 28672 - 52 * 64, 8192, 1 << 20) == 7, "h=52");
+  CHECK(tiled_choose_groups(256, 8, 59 * 64, 28672 - 59 * 64, 8192, 1 << 20) == 8, "h=59");
+  // HBM plan: first-phase tiles all full (256 n1 < rows), the two phases
+  // cover the rows, heights within [4, 8]; never costlier under the model than
+  // one walk of 256-row tiles; the model's cost equals the slowest work-group
+  // of an explicit walk of both phases through tiled_work.
   for (int cus : {256, 32, 80, 304})
     for (int tn = 2; tn <= 8; ++tn)
-      for (int g : {0, 1, 3})
-        for (int64_t rows : {0, 1, 64, 255, 4096, 10240, 28672, 100000}) {
+      for (int g : {0, 1, 3, 6})
+        for (int64_t rows : {0, 1, 64, 255, 4096, 10240, 25792, 28672, 100000}) {
           if (g > tiled_max_groups(cus, tn)) continue;
-          const int rb = tiled_choose_rb(cus, tn, g, rows);
-          CHECK(rb >= kTiledRbMin && rb <= kTiledRbMax, "cus=%d tn=%d g=%d rows=%lld rb=%d", cus, tn, g,
-                (long long)rows, rb);
-          if (rows > 0) {
-            auto cost = [&](int r) {
-              return (double)tiled_hbm_rounds(cus, tn, g, (rows + 32 * r - 1) / (32 * r) * tn) * (r + kTiledRbFixed);
-            };
-            CHECK(cost(rb) <= cost(kTiledRbMax), "rows=%lld rb=%d", (long long)rows, rb);
+          const TiledHbmPlan p = tiled_choose_plan(cus, tn, g, rows);
+          CHECK(p.rb2 >= kTiledRbMin && p.rb2 <= kTiledRbMax && p.n1 >= 0, "cus=%d tn=%d g=%d rows=%lld", cus, tn,
+                g, (long long)rows);
+          if (rows <= 0) continue;
+          const int64_t t2 = tiled_plan_tiles2(rows, p);
+          CHECK(256 * p.n1 < rows && 256 * p.n1 + 32 * p.rb2 * t2 >= rows && 256 * p.n1 + 32 * p.rb2 * (t2 - 1) < rows,
+                "rows=%lld n1=%lld rb2=%d", (long long)rows, (long long)p.n1, p.rb2);
+          CHECK(tiled_plan_cost(cus, tn, g, rows, p) <= tiled_plan_cost(cus, tn, g, rows, TiledHbmPlan{0, 8}),
+                "rows=%lld", (long long)rows);
+          // explicit walk
+          const int n_xcd = tiled_xcds(cus);
+          double worst = 0.0;
+          for (int b = 0; b < cus; ++b) {
+            const TiledWork w1 = tiled_work(b, cus, n_xcd, g, tn, 1, p.n1 * tn);
+            if (w1.host) continue;
+            const TiledWork w2 = tiled_work(b, cus, n_xcd, g, tn, 1, t2 * tn, true);
+            double c = 0.0;
+            for (int64_t t = w1.first; t < w1.end; t += w1.stride) c += kTiledRbMax + kTiledRbFixed;
+            for (int64_t t = w2.first; t < w2.end; t += w2.stride) c += p.rb2 + kTiledRbFixed;
+            worst = c > worst ? c : worst;
           }
+          CHECK(worst == tiled_plan_cost(cus, tn, g, rows, p), "cus=%d tn=%d g=%d rows=%lld walk %.1f model %.1f", cus,
+                tn, g, (long long)rows, worst, tiled_plan_cost(cus, tn, g, rows, p));
         }
-  CHECK(tiled_choose_rb(256, 8, 0, 0) == 8, "no HBM rows");
-  CHECK(tiled_choose_rb(256, 8, 0, 28672) == 7, "28672");
-  CHECK(tiled_choose_rb(256, 8, 0, 10240) == 5, "10240");
-  CHECK(tiled_choose_rb(256, 8, 0, 14336) == 7, "14336");
-  CHECK(tiled_choose_rb(256, 8, 0, 8192) == 8, "8192");
+  // Measured on MI355X (N = 2048, K = 8192, 256 CUs, no host rows): one walk
+  // of 224-row tiles for M = 28672 and 14336, of 160 rows for 10240, of 256
+  // rows for 8192 (one full round already).
+  auto single = [](int64_t rows, int rb) {
+    const TiledHbmPlan p = tiled_choose_plan(256, 8, 0, rows);
+    return p.n1 == 0 && p.rb2 == rb;
+  };
+  CHECK(tiled_choose_plan(256, 8, 0, 0).n1 == 0 && tiled_choose_plan(256, 8, 0, 0).rb2 == 8, "no HBM rows");
+  CHECK(single(28672, 7) && single(10240, 5) && single(14336, 7) && single(8192, 8), "prefill-style shapes");
   // the all-HBM shapes of the GPU test that runs every tile height
-  CHECK(tiled_choose_rb(256, 8, 0, 1024) == 4 && tiled_choose_rb(256, 8, 0, 4160) == 5 &&
-            tiled_choose_rb(256, 8, 0, 5184) == 6 && tiled_choose_rb(256, 8, 0, 6208) == 7 &&
-            tiled_choose_rb(256, 8, 0, 7232) == 8,
+  CHECK(single(1024, 4) && single(4160, 5) && single(5184, 6) && single(6208, 7) && single(7232, 8),
         "GPU test shapes");
-  CHECK(tiled_hbm_rounds(256, 8, 0, 896) == 4 && tiled_hbm_rounds(256, 8, 0, 1024) == 4 &&
-            tiled_hbm_rounds(256, 8, 0, 1025) == 5, "rounds");
+  // 28672 rows with 45 host tile-rows of 64 and 6 host groups (208 HBM
+  // work-groups): three rounds of 256-row tiles, then one of 224 rows (47
+  // units against 48 for four rounds of 256 rows).
+  {
+    const TiledHbmPlan p = tiled_choose_plan(256, 8, 6, 28672 - 45 * 64);
+    CHECK(p.n1 == 78 && p.rb2 == 7 && tiled_plan_cost(256, 8, 6, 28672 - 45 * 64, p) == 47.0, "h=45: n1=%lld rb2=%d",
+          (long long)p.n1, p.rb2);
+  }
   // The XCD layout of MI355X: 8 x 32 CUs.
   CHECK(tiled_xcds(256) == 8 && tiled_max_groups(256, 8) == 24 && tiled_max_groups(256, 2) == 120, "MI355X layout");
   std::printf("%d configurations, %d failures\n", n, fails);

@@ -18,7 +18,8 @@ struct TiledArgs {
   int64_t N;
   float* y;
   int n_groups;   // host groups of ceil(N/256) work-groups (0 when host_rows == 0)
-  int hbm_rb;     // HBM tiles are 32 hbm_rb rows high, hbm_rb in [4, 8] (tiled_choose_rb)
+  int64_t hbm_n1;   // HBM rows: first hbm_n1 row tiles of 256 rows, then tiles of
+  int hbm_rb2;      // 32 hbm_rb2 rows, hbm_rb2 in [4, 8] (tiled_choose_plan)
   int cus;        // compute units of the device: the grid, one work-group each
   unsigned long long* counters;
   unsigned long long* xcc_masks;   // DAK_FLAG_RECORD_XCC: one XCD bit mask per host group, else null

@@ -510,9 +510,10 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     if (max_groups < 1)
       return fail(DAK_EUNSUPPORTED, "N=%lld: a host group of %d work-groups does not fit one XCD of this device",
                   (long long)N, tn);
-    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, (M - host_rows + 255) / 256, K,
-                                     std::max(1, lc.host_cus / tn));
-    t.hbm_rb = tiled_choose_rb(t.cus, tn, t.n_groups, M - host_rows);
+    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn));
+    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows);
+    t.hbm_n1 = plan.n1;
+    t.hbm_rb2 = plan.rb2;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.xcc_masks = (lc.flags & DAK_FLAG_RECORD_XCC) ? t.counters + 2 : nullptr;
     t.stream = static_cast<hipStream_t>(stream);

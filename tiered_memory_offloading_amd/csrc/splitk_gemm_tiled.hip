@@ -15,10 +15,11 @@
 //
 // Both roles compute output tiles of 256 columns with 8 waves in a 2 x 4 grid,
 // K in 32-k steps staged through LDS by the DMA form of the load.  HBM tiles
-// are 32 rb rows high (rb in 4 .. 8, chosen per launch so the last round of
-// tiles is not half empty; each wave 16 rb x 64) and stream through two slots
-// of 64-k steps (128 bytes per row), one step in flight behind the one
-// consumed; each step is two 32-k MFMA substeps.  Host
+// are 32 rb rows high (each wave 16 rb x 64): whole rounds of 256-row tiles,
+// then tiles of a height chosen per launch (rb in 4 .. 8) so that the last
+// round is not half empty; they stream through two slots of 64-k steps (128
+// bytes per row), one step in flight behind the one consumed; each step is
+// two 32-k MFMA substeps.  Host
 // tiles are 256 rows high: the link moves long row pieces far better than
 // short ones (256 rows x 64 bytes at a time top out near 37 GB/s, 256 bytes
 // per row reach the link's 57 GB/s), so A arrives in super-steps of 4 k-steps
@@ -383,17 +384,22 @@ __device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_
   store_tile<8>(acc, P, row0, N, col0, M, 0, y, wm, wn, lane);
 }
 
-template <bool COUNT, bool RAGGED, int RB>
+// HBM rows: hbm_n1 row tiles of 256 rows, then the rest in tiles of 32 RB2
+// rows (tiled_choose_plan).
+template <bool COUNT, bool RAGGED, int RB2>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int n_groups, int cus,
-    int n_xcd, unsigned long long* __restrict__ counters, unsigned long long* __restrict__ xcc_masks) {
+    int n_xcd, int64_t hbm_n1, unsigned long long* __restrict__ counters,
+    unsigned long long* __restrict__ xcc_masks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
   const int tn = (int)((N + kBN - 1) / kBN);
-  constexpr int kHbmRows = 32 * RB;
-  const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, (host_rows + kBM - 1) / kBM,
-                                 (M - host_rows + kHbmRows - 1) / kHbmRows * tn);
+  const int64_t host_blocks = (host_rows + kBM - 1) / kBM;
+  const int64_t P = M - host_rows;
+  constexpr int kRows2 = 32 * RB2;
+  const int64_t rows2 = P - (int64_t)kBM * hbm_n1;
+  const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks, hbm_n1 * tn);
   const bool host_role = w.host;
   // Where the schedule's placement assumption can be checked: each host
   // work-group ORs the bit of the XCD it runs on (the hardware's XCC id
@@ -412,8 +418,16 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   } else {
     for (int64_t t = w.first; t < w.end; t += w.stride) {
       __syncthreads();   // the ring is reused
-      tile<COUNT, RAGGED, RB>(a_hbm, M - host_rows, t / tn * kHbmRows, x, N, t % tn * kBN, K, M, host_rows, y, lds,
-                              nbytes);
+      tile<COUNT, RAGGED, kBM / 32>(a_hbm, P, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, lds, nbytes);
+    }
+    if (rows2 > 0) {
+      const TiledWork w2 = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks,
+                                      (rows2 + kRows2 - 1) / kRows2 * tn, true);
+      for (int64_t t = w2.first; t < w2.end; t += w2.stride) {
+        __syncthreads();   // the ring is reused
+        tile<COUNT, RAGGED, RB2>(a_hbm, P, kBM * hbm_n1 + t / tn * kRows2, x, N, t % tn * kBN, K, M, host_rows, y,
+                                 lds, nbytes);
+      }
     }
   }
   if (COUNT) {
@@ -429,12 +443,13 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
 
 int tiled_max_host_groups(int64_t N, int cus) { return tiled_max_groups(cus, (int)((N + kBN - 1) / kBN)); }
 
-template <int RB>
+template <int RB2>
 static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
   const bool ragged = (g.K & 31) != 0;
-#define DAK_TILED(C, R)                                                                                              \
-  hipLaunchKernelGGL((gemm_tiled_split<C, R, RB>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host, g.a_hbm, \
-                     g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.counters, g.xcc_masks)
+#define DAK_TILED(C, R)                                                                                               \
+  hipLaunchKernelGGL((gemm_tiled_split<C, R, RB2>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host,          \
+                     g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.hbm_n1, g.counters, \
+                     g.xcc_masks)
   if (count) {
     if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
   } else {
@@ -445,8 +460,9 @@ static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
 
 void launch_gemm_tiled(const TiledArgs& g, bool count) {
   const int n_xcd = tiled_xcds(g.cus);
-  static_assert(kTiledRbMin == 4 && kTiledRbMax == 8, "one instance per HBM tile height");
-  switch (g.hbm_rb) {
+  static_assert(kTiledRbMin == 4 && kTiledRbMax == 8 && kBM == 32 * kTiledRbMax,
+                "one instance per second-phase tile height; first-phase tiles are kBM rows");
+  switch (g.hbm_rb2) {
     case 4: return launch_rb<4>(g, count, n_xcd);
     case 5: return launch_rb<5>(g, count, n_xcd);
     case 6: return launch_rb<6>(g, count, n_xcd);

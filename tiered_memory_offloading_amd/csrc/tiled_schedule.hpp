@@ -31,8 +31,11 @@ constexpr int tiled_groups_on(int v, int n_groups, int n_xcd) {
 // b in [0, cus); tn column tiles; host_blocks 256-row blocks of host rows;
 // hbm_tiles = HBM row tiles * tn.  Requires every XCD to keep at least one
 // HBM work-group: tiled_groups_on(v) * tn < tiled_cus_on(v) for all v.
+// `reverse` numbers an XCD's HBM work-groups from its last one, so that the
+// work-groups that took fewer tiles of an earlier walk take the first tiles
+// of this one.
 constexpr TiledWork tiled_work(int b, int cus, int n_xcd, int n_groups, int tn, int64_t host_blocks,
-                               int64_t hbm_tiles) {
+                               int64_t hbm_tiles, bool reverse = false) {
   const int xcd = b % n_xcd, j = b / n_xcd;
   const int hw = tiled_groups_on(xcd, n_groups, n_xcd) * tn;
   if (j < hw) {
@@ -46,7 +49,8 @@ constexpr TiledWork tiled_work(int b, int cus, int n_xcd, int n_groups, int tn, 
     total += c;
   }
   const int64_t mine = tiled_cus_on(xcd, cus, n_xcd) - hw;
-  return TiledWork{false, 0, hbm_tiles * before / total + (j - hw), hbm_tiles * (before + mine) / total, mine};
+  const int64_t i = reverse ? mine - 1 - (j - hw) : j - hw;
+  return TiledWork{false, 0, hbm_tiles * before / total + i, hbm_tiles * (before + mine) / total, mine};
 }
 
 // XCDs of a device with `cus` compute units (MI355X: 32 CUs per XCD).
@@ -77,30 +81,97 @@ inline constexpr TiledCost kTiledCostMi355x{0.92, 10.0, 55.0};
 
 constexpr double tiled_max_d(double a, double b) { return a > b ? a : b; }
 
-// Rounds of HBM tiles: each XCD's HBM work-groups run their share of `tiles`
-// (split in proportion to their number, as tiled_work does) in whole rounds
-// of one tile each; the launch lasts as long as its slowest XCD.
-constexpr int64_t tiled_hbm_rounds(int cus, int tn, int n_groups, int64_t tiles) {
+// The HBM role's tiles.  A tile is 32 rb rows by 256 columns, rb in
+// [kTiledRbMin, 8].  On MI355X a tile's time grows as rb + kTiledRbFixed
+// (measured with N = 2048, K = 8192 and M = 10240, 14336 and 28672: the x
+// rows, the barriers and the DMA issue do not shrink with the tile), so the
+// tallest tile is cheapest per row, and shorter tiles pay only where they even
+// out the work-groups' last round.  A plan walks the HBM rows in two phases:
+// first n1 row tiles of 256 rows (rb 8), then the rest in tiles of 32 rb2
+// rows, the second walk numbered from each XCD's last HBM work-group
+// (tiled_work's `reverse`), so the work-groups with one tile fewer in the
+// first phase start the second.  n1 = 0 is a single walk of one height.  The
+// plan only places work: every output element is the same sum of the same
+// MFMAs for any tile height.
+constexpr int kTiledRbMin = 4, kTiledRbMax = 8;
+constexpr double kTiledRbFixed = 4.0;
+struct TiledHbmPlan {
+  int64_t n1;   // first-phase row tiles (256 rows each)
+  int rb2;      // second phase: tiles of 32 rb2 rows
+};
+
+constexpr int64_t tiled_plan_tiles2(int64_t hbm_rows, const TiledHbmPlan& p) {
+  const int64_t rest = hbm_rows - 32 * kTiledRbMax * p.n1;
+  return rest > 0 ? (rest + 32 * p.rb2 - 1) / (32 * p.rb2) : 0;
+}
+
+// Modelled duration of a plan, in units of kTiledRbFixed-offset tile rows:
+// the slowest HBM work-group over all XCDs.  Within an XCD of w HBM
+// work-groups the first s1 % w of them take one first-phase tile more, and
+// the last s2 % w one second-phase tile more.
+constexpr double tiled_plan_cost(int cus, int tn, int n_groups, int64_t hbm_rows, const TiledHbmPlan& p) {
   const int n_xcd = tiled_xcds(cus);
+  const int64_t t1 = p.n1 * tn, t2 = tiled_plan_tiles2(hbm_rows, p) * tn;
+  const double c1 = kTiledRbMax + kTiledRbFixed, c2 = p.rb2 + kTiledRbFixed;
   int64_t total = 0;
   for (int v = 0; v < n_xcd; ++v) total += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
-  int64_t rounds = 0, before = 0;
+  double worst = 0.0;
+  int64_t before = 0;
   for (int v = 0; v < n_xcd; ++v) {
     const int64_t w = tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
-    const int64_t share = tiles * (before + w) / total - tiles * before / total;
+    const int64_t s1 = t1 * (before + w) / total - t1 * before / total;
+    const int64_t s2 = t2 * (before + w) / total - t2 * before / total;
     before += w;
-    const int64_t r = (share + w - 1) / w;
-    rounds = r > rounds ? r : rounds;
+    const int64_t r1 = s1 % w, r2 = s2 % w;
+    const double extra = (r1 > 0 && r2 > 0 && r1 + r2 > w) ? c1 + c2
+                         : tiled_max_d(r1 > 0 ? c1 : 0.0, r2 > 0 ? c2 : 0.0);
+    const double c = (double)(s1 / w) * c1 + (double)(s2 / w) * c2 + extra;
+    worst = c > worst ? c : worst;
   }
-  return rounds;
+  return worst;
+}
+
+// The plan with the least modelled duration.  Candidates: a single walk of
+// each height (the tallest first), then first phases of whole rounds of
+// 256-row tiles followed by each second-phase height; a candidate replaces
+// the best only when strictly cheaper.
+constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t hbm_rows) {
+  TiledHbmPlan best{0, kTiledRbMax};
+  if (hbm_rows <= 0) return best;
+  double best_c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, best);
+  for (int rb = kTiledRbMax - 1; rb >= kTiledRbMin; --rb) {
+    const TiledHbmPlan p{0, rb};
+    const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p);
+    if (c < best_c * (1.0 - 1e-9)) {
+      best = p;
+      best_c = c;
+    }
+  }
+  const int n_xcd = tiled_xcds(cus);
+  int64_t wgs = 0;
+  for (int v = 0; v < n_xcd; ++v) wgs += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
+  const int64_t all = (hbm_rows + 32 * kTiledRbMax - 1) / (32 * kTiledRbMax);
+  for (int64_t r1 = 1; r1 * wgs / tn < all; ++r1) {
+    const int64_t n1 = r1 * wgs / tn;
+    if (n1 < 1) continue;
+    for (int rb = kTiledRbMax; rb >= kTiledRbMin; --rb) {
+      const TiledHbmPlan p{n1, rb};
+      const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p);
+      if (c < best_c * (1.0 - 1e-9)) {
+        best = p;
+        best_c = c;
+      }
+    }
+  }
+  return best;
 }
 
 // Predicted microseconds of a launch with `n_groups` host groups: host row
 // blocks go round by round to the groups (a round lasts as long as a tile, as
 // one group's stream of a block, or as the link needs for all active groups'
-// blocks, whichever is longest); each XCD's HBM work-groups run their share
-// of the HBM tiles (here of 256 rows) in whole rounds of one tile.
-constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_row_tiles, int64_t K,
+// blocks, whichever is longest); the HBM role takes its chosen plan's
+// modelled duration, a 256-row tile lasting `t_tile`.
+constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_rows, int64_t K,
                                   TiledCost c) {
   const double t_tile = (double)((K + 31) / 32) * c.step_us;
   const double block_bytes = 256.0 * (double)K * 2.0;
@@ -112,40 +183,15 @@ constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_ro
                                               (double)active * block_bytes / (c.link_gbps * 1e3)));
     left -= active;
   }
-  const double t_hbm = (double)tiled_hbm_rounds(cus, tn, n_groups, hbm_row_tiles * tn) * t_tile;
+  const TiledHbmPlan p = tiled_choose_plan(cus, tn, n_groups, hbm_rows);
+  const double t_hbm = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p) / (kTiledRbMax + kTiledRbFixed) * t_tile;
   return tiled_max_d(t_host, t_hbm);
-}
-
-// Height of the HBM role's tiles: 32 rb rows, rb in [kTiledRbMin, 8].  On
-// MI355X a round of such tiles takes time in proportion to rb + 4 (measured
-// with N = 2048, K = 8192 and M = 10240, 14336 and 28672: the x rows, the
-// barrier and the DMA issue do not shrink with the tile), so a shorter tile
-// pays only where it evens out the last round: the rb with the least
-// rounds * (rb + 4), the tallest on ties.  256-row blocks of host rows keep
-// their height; the choice only places work (every output element is the
-// same sum of the same MFMAs for any tile height).
-constexpr int kTiledRbMin = 4, kTiledRbMax = 8;
-constexpr double kTiledRbFixed = 4.0;
-constexpr int tiled_choose_rb(int cus, int tn, int n_groups, int64_t hbm_rows) {
-  if (hbm_rows <= 0) return kTiledRbMax;
-  int best = kTiledRbMax;
-  double best_c = 0.0;
-  for (int rb = kTiledRbMax; rb >= kTiledRbMin; --rb) {
-    const int64_t rows = 32 * (int64_t)rb;
-    const double c = (double)tiled_hbm_rounds(cus, tn, n_groups, (hbm_rows + rows - 1) / rows * tn) *
-                     ((double)rb + kTiledRbFixed);
-    if (rb == kTiledRbMax || c < best_c * (1.0 - 1e-9)) {
-      best = rb;
-      best_c = c;
-    }
-  }
-  return best;
 }
 
 // Host groups for a launch: the count in [1, cap] (and at most one per host
 // row block) with the least predicted time, the fewest on ties; 0 without
 // host rows.
-constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_row_tiles, int64_t K, int cap,
+constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_rows, int64_t K, int cap,
                                   TiledCost c = kTiledCostMi355x) {
   if (host_rows <= 0) return 0;
   const int64_t blocks = (host_rows + 255) / 256;
@@ -154,9 +200,9 @@ constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hb
   if (blocks < hi) hi = (int)blocks;
   if (hi < 1) hi = 1;
   int best = 1;
-  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_row_tiles, K, c);
+  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c);
   for (int g = 2; g <= hi; ++g) {
-    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_row_tiles, K, c);
+    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c);
     if (t < best_t * (1.0 - 1e-9)) {
       best = g;
       best_t = t;

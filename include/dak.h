@@ -278,12 +278,18 @@ typedef struct {
  * and every host byte crosses the link once.
  *   A     the FP8 split matrix
  *   x     bf16 [N, K] in device memory
- *   N     1 .. 64 (decode batches; larger N is DAK_EUNSUPPORTED)
+ *   N     1 .. 2048: decode batches (N <= 64) take the memory-bound kernel;
+ *         wider activations (DAK §4.2.1's compute-bound regime, where halving
+ *         the bytes of a tile-row doubles the turning point's host share)
+ *         take the tiled kernel of dak_splitk_gemm with FP8 A tiles, the
+ *         codes widened to bf16 (exact) before the same bf16 MFMA
  *   y     fp32 [N, M] in device memory; fully written
  *   cfg   nullable launch configuration (the window does not apply: the
- *         kernel stages fixed-depth rings)
+ *         kernels stage fixed-depth rings; for N > 64 host_cus caps the host
+ *         groups as in dak_splitk_gemm)
  * Errors: DAK_EINVAL for shapes/pointers outside the above, DAK_EUNSUPPORTED
- * for N > 64.  A NaN code gives NaN in its row. */
+ * for N > 2048 and for a staged host part (DAK_FLAG_STAGED_HOST) with
+ * N > 64.  A NaN code gives NaN in its row. */
 dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
                                const dak_launch_cfg* cfg, void* stream);
 

@@ -110,11 +110,14 @@ def test_nan_code_poisons_its_row_only():
 
 
 def test_fp8_arguments_checked():
-    codes, scale, x = synth.fp8_gemm_inputs(64, 256, 65, seed=6)
+    codes, scale, x = synth.fp8_gemm_inputs(64, 256, 2049, seed=6)
     S = dak.place_matrix_fp8(codes, scale, 64, 0)
     with pytest.raises(dak.DakError) as e:
-        dak.splitk_gemm_fp8(S, x.cuda())              # N = 65
+        dak.splitk_gemm_fp8(S, x.cuda())              # N = 2049
     assert e.value.status == -4   # DAK_EUNSUPPORTED
+    with pytest.raises(dak.DakError) as e:            # a staged host part with N > 64
+        dak.splitk_gemm_fp8(S, x[:65].cuda().contiguous(), cfg=dak.LaunchConfig(staged_host=True))
+    assert e.value.status == -4
     S.row_scale = S.row_scale.cpu()                   # scales must be device memory
     with pytest.raises(dak.DakError):
         dak.splitk_gemm_fp8(S, x[:8].cuda().contiguous())
@@ -136,3 +139,77 @@ def test_small_and_ragged_shapes(M, K, m, N):
     assert normwise_error(base.numpy(), ref) <= TOL
     for h in range(1, M // m + 1):
         assert torch.equal(run(codes, scale, x, m, h), base), h
+
+
+# ---------------------------------------------------------------------------
+# Wide activations (N > 64): the compute-bound tiled kernel with FP8 A tiles
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N", [65, 257, 600])
+@pytest.mark.parametrize("K", [528, 1056, 1024])
+def test_wide_n_every_code_and_split(N, K):
+    # Every finite code; M = 320 leaves a partial HBM tile and a partial host
+    # block for every split; K = 528 ends in a half 32-k step, K = 1056 in a
+    # half 64-k HBM step, K = 1024 in neither.
+    M, m = 320, 64
+    codes = synth.fp8_all_codes(M, K, seed=N + K)
+    scale = torch.rand(M, generator=torch.Generator().manual_seed(N + K)) * 0.01 + 1e-3
+    x = synth.gemm_inputs(16, K, N, seed=N + K)[1]
+    ref = of.gemm_fp8(codes, scale, x)
+    base = run(codes, scale, x, m, 0)
+    err = normwise_error(base.numpy(), ref)
+    print(f"N={N} K={K} normwise error {err:.3e}")
+    assert err <= TOL
+    for h in range(1, M // m + 1):
+        assert torch.equal(run(codes, scale, x, m, h), base), h
+
+
+def test_wide_n_power_of_two_scales_exact():
+    ints = torch.tensor([0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0x00], dtype=torch.uint8)
+    gen = torch.Generator().manual_seed(8)
+    M, K, N = 512, 1024, 512
+    codes = ints[torch.randint(0, len(ints), (M, K), generator=gen)]
+    scale = 2.0 ** torch.randint(-3, 3, (M,), generator=gen).float()
+    x = torch.randint(-3, 4, (N, K), generator=gen).to(torch.bfloat16)
+    ref = of.gemm_fp8(codes, scale, x)
+    for h in (0, 3, 8):
+        assert np.array_equal(run(codes, scale, x, 64, h).double().numpy(), ref)
+
+
+def test_wide_n_prefill_sampled():
+    # The prefill-shaped GEMM (A 28672 x 8192, B 8192 x 2048) with FP8
+    # weights: 256 sampled rows (all 2048 columns) against the oracle; the
+    # all-HBM, a planner-sized and the all-host split bit-identical.
+    M, K, N = 28672, 8192, 2048
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, N, seed=9, device="cuda")
+    n = M // 64
+    outs = [run(codes, scale, x, 64, h) for h in (0, 90, n)]
+    assert torch.equal(outs[1], outs[0]) and torch.equal(outs[2], outs[0])
+    rows = torch.randperm(M, generator=torch.Generator().manual_seed(9))[:256].sort().values
+    ref = of.gemm_fp8(codes.cpu()[rows], scale.cpu()[rows], x.cpu())
+    err = normwise_error(outs[0][:, rows].numpy(), ref)
+    print(f"prefill FP8 sampled normwise error {err:.3e}")
+    assert err <= TOL
+
+
+def test_wide_n_bytes_requested_per_column_tile():
+    # Each A panel is requested once per 256-column tile of the output; host
+    # panels by the work-groups of one host group, which share an XCD's L2.
+    M, K, N, h = 1024, 1024, 512, 7
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, N, seed=10, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    run(codes, scale, x, 64, h, cfg=dak.LaunchConfig(byte_counters=cnt))
+    assert cnt.tolist() == [2 * h * 64 * K, 2 * (M - h * 64) * K]
+
+
+def test_wide_n_nan_code_poisons_its_row_only():
+    M, K, N = 320, 512, 300
+    codes, scale, x = synth.fp8_gemm_inputs(M, K, N, seed=11)
+    base = run(codes, scale, x, 64, 0)
+    bad = codes.clone()
+    bad[17, 100] = 0x7F
+    bad[300, 511] = 0xFF
+    for h in (0, 1, 5):
+        y = run(bad, scale, x, 64, h)
+        assert torch.isnan(y[:, 17]).all() and torch.isnan(y[:, 300]).all()
+        keep = [r for r in range(M) if r not in (17, 300)]
+        assert torch.equal(y[:, keep], base[:, keep])

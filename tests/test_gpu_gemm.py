@@ -231,8 +231,10 @@ def test_wide_n_small_shapes_ragged_all_splits_bit_identical(N):
         assert torch.equal(y, outs[0]), f"h={h} differs from h=0"
 
 
-@pytest.mark.parametrize("M,K,m,N", [(32, 8, 32, 257), (96, 40, 32, 600), (512, 4104, 128, 1536), (48, 264, 16, 300)])
+@pytest.mark.parametrize("M,K,m,N", [(32, 8, 32, 257), (96, 40, 32, 600), (512, 4104, 128, 1536), (48, 264, 16, 300),
+                                     (320, 1056, 64, 300), (64, 96, 32, 257)])
 def test_wide_n_edge_shapes(M, K, m, N):
+    # K = 1056 and 96 end in half a 64-k HBM step (a multiple of 32, not 64).
     A, X = synth.gemm_inputs(M, K, N, seed=M + K + N)
     ref = ref_of(A, X)
     y = run(A, X, m, M // m)             # everything on the host

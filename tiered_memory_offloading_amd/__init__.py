@@ -384,7 +384,8 @@ def place_matrix_fp8(codes: torch.Tensor, row_scale: torch.Tensor, m: int, h: in
 def splitk_gemm_fp8(A: SplitMatrixFP8, x: torch.Tensor, y: Optional[torch.Tensor] = None,
                     cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
     """y[n, r] = row_scale[r] * sum_k e4m3(A[r, k]) x[n, k]; x bf16 [N, K] on
-    the GPU (N <= 64), y fp32 [N, M]."""
+    the GPU (N <= 2048; N > 64 takes the compute-bound tiled kernel), y fp32
+    [N, M]."""
     lib = library()
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")

@@ -57,6 +57,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Eight e4m3 codes (k ascending from the low byte) widened to eight bf16 with
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value, subnormals
+// included, is a bf16 normal; the NaN code gives NaN).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
 // Sum over all 64 lanes by a fixed xor butterfly; all lanes end with equal bits.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

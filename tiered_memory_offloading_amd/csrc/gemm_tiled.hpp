@@ -11,8 +11,10 @@ namespace dak {
 constexpr int64_t kTiledMaxN = 2048;
 
 struct TiledArgs {
-  const uint16_t* a_host;
-  const uint16_t* a_hbm;
+  bool f8;                  // A holds e4m3 codes (K bytes per row) scaled by row_scale; else bf16
+  const void* a_host;
+  const void* a_hbm;
+  const float* row_scale;   // f8: fp32 [M] in device memory
   int64_t M, K, host_rows;
   const uint16_t* x;
   int64_t N;

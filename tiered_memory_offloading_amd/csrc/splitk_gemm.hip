@@ -497,8 +497,10 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
 
   if (tiled) {
     TiledArgs t;
-    t.a_host = static_cast<const uint16_t*>(dh);
-    t.a_hbm = static_cast<const uint16_t*>(dg);
+    t.f8 = false;
+    t.a_host = dh;
+    t.a_hbm = dg;
+    t.row_scale = nullptr;
     t.M = M;
     t.K = K;
     t.host_rows = host_rows;

@@ -1,6 +1,10 @@
 // Split GEMM over FP8 weights: y = s . (x . e4m3(A)^T) with A's first h
 // tile-rows of e4m3 codes in pinned host memory, the rest in HBM, one fp32
-// scale per row and bf16 activations (1 <= N <= 64).
+// scale per row and bf16 activations.  This file holds the memory-bound
+// kernel for decode batches (1 <= N <= 64) and the entry point; wider
+// activations (the compute-bound regime, DAK paper §4.2.1) go to the tiled
+// kernel with FP8 A tiles (splitk_gemm_tiled.hip), where halving the bytes of
+// a tile-row moves the turning point B_h / B_i to twice the host share.
 //
 // DAK paper §4.1 "DAK Design": disjoint work-groups compute disjoint output
 // rows and each reads one tier (Fig. 5b); §4.3.2: a host tile is fetched by one
@@ -40,6 +44,8 @@
 #include <algorithm>
 
 #include "device_common.hpp"
+#include "gemm_tiled.hpp"
+#include "tiled_schedule.hpp"
 
 namespace dak {
 namespace {
@@ -86,16 +92,6 @@ __device__ __forceinline__ void f8_wait_later(int64_t later) {
   if (later >= 2) vm_wait<2 * PW>();
   else if (later == 1) vm_wait<PW>();
   else vm_wait<0>();
-}
-
-// Eight e4m3 codes (k ascending from the low byte) widened to eight bf16.
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
-  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
 }
 
 template <int NB, int RB, int XR, bool COUNT>
@@ -361,15 +357,19 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
   const int64_t n_units = M / m;
   if (h < 0 || h > n_units) return fail(DAK_EINVAL, "h=%lld outside [0, %lld]", (long long)h, (long long)n_units);
   if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
-  if (N > kF8MaxN) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld for FP8 weights", (long long)N, (long long)kF8MaxN);
+  if (N > kTiledMaxN) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld for FP8 weights", (long long)N, (long long)kTiledMaxN);
   if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
-  const int rb = f8_row_blocks(M, m);
+  // Decode batches (N <= 64) take the memory-bound ring kernel below; wider
+  // activations the compute-bound tiled kernel with FP8 A tiles.
+  const bool tiled = N > kF8MaxN;
+  const int rb = tiled ? 1 : f8_row_blocks(M, m);
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, HostDefaults{f8_host_cus(N, rb)}, &lc);
+  dak_status st = resolve_cfg(cfg, tiled ? HostDefaults{kGemmTiledMaxHostCus} : HostDefaults{f8_host_cus(N, rb)}, &lc);
   if (st) return st;
 
   const int64_t host_rows = h * m;
   const bool stage = (lc.flags & DAK_FLAG_STAGED_HOST) != 0;   // host rows staged in HBM by the caller
+  if (stage && tiled) return fail(DAK_EUNSUPPORTED, "a staged host part is supported for N <= %lld only", (long long)kF8MaxN);
   const void *dh = nullptr, *dg = nullptr, *ds = nullptr, *dx = nullptr, *dy = nullptr;
   if (host_rows > 0 && (st = check_tier_ptr(A->host, (uint64_t)host_rows * K, stage ? Tier::kDevice : Tier::kHost,
                                             "A.host", &dh)))
@@ -379,6 +379,36 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
   if ((st = check_tier_ptr(A->row_scale, (uint64_t)M * 4, Tier::kDevice, "A.row_scale", &ds))) return st;
   if ((st = check_tier_ptr(x, (uint64_t)N * K * 2, Tier::kDevice, "x", &dx))) return st;
   if ((st = check_tier_ptr(y, (uint64_t)N * M * 4, Tier::kDevice, "y", &dy))) return st;
+
+  if (tiled) {
+    TiledArgs t;
+    t.f8 = true;
+    t.a_host = dh;
+    t.a_hbm = dg;
+    t.row_scale = static_cast<const float*>(ds);
+    t.M = M;
+    t.K = K;
+    t.host_rows = host_rows;
+    t.x = static_cast<const uint16_t*>(dx);
+    t.N = N;
+    t.y = y;
+    if ((st = device_cus(&t.cus))) return st;
+    const int tn = (int)((N + 255) / 256);
+    if (tiled_max_host_groups(N, t.cus) < 1)
+      return fail(DAK_EUNSUPPORTED, "N=%lld: a host group of %d work-groups does not fit one XCD of this device",
+                  (long long)N, tn);
+    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn), 1);
+    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows);
+    t.hbm_n1 = plan.n1;
+    t.hbm_rb2 = plan.rb2;
+    t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
+    t.xcc_masks = (lc.flags & DAK_FLAG_RECORD_XCC) ? t.counters + 2 : nullptr;
+    t.stream = static_cast<hipStream_t>(stream);
+    launch_gemm_tiled(t, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip((int)e, "fp8 tiled gemm kernel launch");
+    return DAK_OK;
+  }
 
   F8Args g;
   g.a_host = static_cast<const unsigned char*>(dh);

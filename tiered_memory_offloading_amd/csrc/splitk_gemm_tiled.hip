@@ -27,6 +27,12 @@
 // Only the staging and the tile height differ; the MFMA sequence of an
 // element is the same.
 //
+// FP8 weights (e4m3 codes, one fp32 scale per row): A rows hold one byte per
+// k, so HBM steps stage 64 bytes of A per row and host super-steps cover 8
+// k-steps; each lane's 8 codes are widened to bf16 (exact) and feed the same
+// MFMA against the same bf16 activations, and the row's scale multiplies the
+// finished sum once.
+//
 // Scheduling: one work-group per CU (the LDS rings admit no second), and
 // work-group b runs on XCD b % n_xcd.  A CU belongs to one role for the whole
 // launch (§4.1's disjoint CU groups):
@@ -152,9 +158,12 @@ __device__ __forceinline__ void tile_issue(const TileDma& d, int64_t s, int64_t 
 // fragments of k at or past K (a partial last step).
 // WIDE: `sa` is a host super-slot (rows of 256 bytes, 16-byte position
 // p ^ (row & 15) holding piece p) and `ss` the step within it.
-template <bool MASK, bool WIDE, int RB>
+// F8 (with WIDE): `sa` holds e4m3 codes, 256 per row; the lane's 8 codes of
+// step ss start at byte 32 ss + 8 g, in piece 2 ss + g / 2.
+template <bool MASK, bool WIDE, int RB, bool F8 = false>
 __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigned char* sx, int ss, int wm, int wn,
                                           int lane, bool kok, f32x4_t (&acc)[RB][4]) {
+  static_assert(!F8 || WIDE, "FP8 steps come from host super-slots");
   const int i16 = lane & 15, g = lane >> 4;
   uint4 bf[4];
 #pragma unroll
@@ -165,8 +174,13 @@ __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigne
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int ra = wm * 16 * RB + rb * 16 + i16;
-    uint4 af = WIDE ? *reinterpret_cast<const uint4*>(sa + ra * kSuperRow + (((kSuper * ss + g) ^ i16) << 4))
-                    : *reinterpret_cast<const uint4*>(sa + slot_pos(ra, g));
+    uint4 af;
+    if constexpr (F8)
+      af = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(sa + ra * kSuperRow +
+                                                          (((2 * ss + (g >> 1)) ^ i16) << 4) + 8 * (g & 1)));
+    else
+      af = WIDE ? *reinterpret_cast<const uint4*>(sa + ra * kSuperRow + (((kSuper * ss + g) ^ i16) << 4))
+                : *reinterpret_cast<const uint4*>(sa + slot_pos(ra, g));
     if (MASK && !kok) af = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
@@ -174,19 +188,31 @@ __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigne
 }
 
 // Write a finished tile (wave rows 16 RB wm .. +16 RB): rows below P,
-// columns below N.
-template <int RB>
+// columns below N.  F8: each sum times its row's scale (y row yrow0 + row).
+template <int RB, bool F8 = false>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[RB][4], int64_t P, int64_t row0, int64_t N,
                                            int64_t col0, int64_t M, int64_t yrow0, float* __restrict__ y, int wm,
-                                           int wn, int lane) {
+                                           int wn, int lane, const float* __restrict__ scale = nullptr) {
   const int i16 = lane & 15, r4 = 4 * (lane >> 4);
 #pragma unroll
   for (int rb2 = 0; rb2 < RB; ++rb2) {
     const int64_t row = row0 + wm * 16 * RB + rb2 * 16 + r4;
+    f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (F8)
+      if (row < P) sc = *reinterpret_cast<const f32x4_t*>(scale + yrow0 + row);   // P is a multiple of 16
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int64_t n = col0 + wn * 64 + cb * 16 + i16;
-      if (n < N && row < P) *reinterpret_cast<f32x4_t*>(y + n * M + yrow0 + row) = acc[rb2][cb];
+      if (n < N && row < P) {
+        f32x4_t v = acc[rb2][cb];
+        if constexpr (F8) {
+          v[0] *= sc[0];
+          v[1] *= sc[1];
+          v[2] *= sc[2];
+          v[3] *= sc[3];
+        }
+        *reinterpret_cast<f32x4_t*>(y + n * M + yrow0 + row) = v;
+      }
     }
   }
 }
@@ -254,6 +280,51 @@ __device__ __forceinline__ void hbm_issue(const HbmDma& d, int64_t s, int64_t K,
   }
 }
 
+// FP8 A rows in the HBM ring: 64 bytes (64 codes) per row per 64-k step,
+// 16-byte piece p at position p ^ ((r >> 2) & 3).  A fragment read (8 codes
+// per lane: 16 rows, 32 bytes of each per pair of lane groups) then runs at
+// the LDS's full ds_read_b64 rate, ~138 bytes per clock per CU (measured over
+// this lane pattern; with p ^ (r & 3) or no swizzle, 80).
+constexpr int kHbmRowA8 = 64;
+constexpr int kHbmSlotA8 = kBM * kHbmRowA8;        // 16 KiB
+constexpr int kHbmDmaA8 = kHbmSlotA8 / 1024 / 4;   // 4 instructions per A wave
+__device__ __forceinline__ int hbm_pos8(int r, int piece) { return r * kHbmRowA8 + ((piece ^ ((r >> 2) & 3)) << 4); }
+
+// Instruction j of A-wave w moves FP8 rows 64 (w & 3) + 16 j .. +15; lane l
+// writes row + l / 4, position l & 3, i.e. global piece (l & 3) ^ (l >> 4).
+// Rows at or past the tile height or P read the tile's first row.
+struct HbmDma8 {
+  const unsigned char* src[kHbmDmaA8];
+  bool counted[kHbmDmaA8];
+  int piece;
+};
+
+__device__ __forceinline__ HbmDma8 hbm_dma8(const unsigned char* __restrict__ a, int64_t P, int64_t row0, int bm,
+                                            int64_t K, int wave, int lane) {
+  HbmDma8 d;
+  d.piece = (lane & 3) ^ (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < kHbmDmaA8; ++j) {
+    const int r = 64 * (wave & 3) + 16 * j + (lane >> 2);
+    const bool in = r < bm && row0 + r < P;
+    d.src[j] = a + (in ? row0 + r : row0) * K + 16 * d.piece;
+    d.counted[j] = in;
+  }
+  return d;
+}
+
+template <bool COUNT, bool RAGGED>
+__device__ __forceinline__ void hbm_issue8(const HbmDma8& d, int64_t s, int64_t K, unsigned char* slot, int wave,
+                                           uint64_t& nbytes) {
+  unsigned char* base = slot + 64 * (wave & 3) * kHbmRowA8;
+  const bool kin = !RAGGED || 64 * s + 16 * d.piece < K;
+#pragma unroll
+  for (int j = 0; j < kHbmDmaA8; ++j) {
+    dma16(d.src[j] + (kin ? 64 * s : -16 * d.piece), base + 16 * j * kHbmRowA8);
+    if (COUNT && kin && d.counted[j]) nbytes += 16;
+  }
+}
+
 // HBM tile: output rows [row0, row0 + 32 RB) of the P rows at `a` (written
 // at y rows yrow0 + row), columns [col0, col0 + 256).  Step s (k in
 // [64 s, 64 s + 64)): wait for its DMA (every wave's part, via the barrier,
@@ -262,29 +333,42 @@ __device__ __forceinline__ void hbm_issue(const HbmDma& d, int64_t s, int64_t K,
 // past K (a last step of at most 32 k) is skipped, so each element sums the
 // same ceil(K / 32) MFMAs as in the host role.  RAGGED: K is not a multiple
 // of 64.
-template <bool COUNT, bool RAGGED, int RB>
-__device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+// F8: `a` holds e4m3 codes (K bytes per row), the slot's A part 64 bytes per
+// row, and the tile is stored times the rows' scales.
+template <bool F8, bool COUNT, bool RAGGED, int RB>
+__device__ __forceinline__ void tile(const void* __restrict__ a, int64_t P, int64_t row0,
                                      const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t M,
-                                     int64_t yrow0, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
-  constexpr int kSlot = 2 * kHbmSlotA;
+                                     int64_t yrow0, float* __restrict__ y, const float* __restrict__ scale,
+                                     unsigned char* lds, uint64_t& nbytes) {
+  constexpr int kSlotA = F8 ? kHbmSlotA8 : kHbmSlotA;   // A part of a slot; then x rows
+  constexpr int kSlot = kSlotA + kHbmSlotA;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3, i16 = lane & 15, g = lane >> 4;
-  const int half = wave < 4 ? 0 : kHbmSlotA;   // waves 0-3 move A rows, 4-7 x rows
+  const bool a_wave = wave < 4;                 // waves 0-3 move A rows, 4-7 x rows
+  const int half = a_wave ? 0 : kSlotA;
   f32x4_t acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int64_t T = (K + 63) >> 6;
-  const HbmDma d = hbm_dma(a, P, row0, 32 * RB, x, N, col0, K, wave, lane);
-  hbm_issue<COUNT, RAGGED>(d, 0, K, lds + half, wave, nbytes);
+  const HbmDma d = hbm_dma(static_cast<const uint16_t*>(a), P, row0, 32 * RB, x, N, col0, K, wave, lane);
+  HbmDma8 d8;
+  if constexpr (F8) d8 = hbm_dma8(static_cast<const unsigned char*>(a), P, row0, 32 * RB, K, wave, lane);
+  auto issue = [&](int64_t s, unsigned char* slot) {
+    if (F8 && a_wave)
+      hbm_issue8<COUNT, RAGGED>(d8, s, K, slot, wave, nbytes);
+    else
+      hbm_issue<COUNT, RAGGED>(d, s, K, slot, wave, nbytes);
+  };
+  issue(0, lds + half);
   for (int64_t s = 0; s < T; ++s) {
     vm_wait<0>();
     __builtin_amdgcn_s_barrier();
     const int slot = (int)(s & 1);
-    if (s + 1 < T) hbm_issue<COUNT, RAGGED>(d, s + 1, K, lds + (slot ^ 1) * kSlot + half, wave, nbytes);
+    if (s + 1 < T) issue(s + 1, lds + (slot ^ 1) * kSlot + half);
     const unsigned char* sa = lds + slot * kSlot;
-    const unsigned char* sx = sa + kHbmSlotA;
+    const unsigned char* sx = sa + kSlotA;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t k = 64 * s + 32 * h;
@@ -298,14 +382,19 @@ __device__ __forceinline__ void tile(const uint16_t* __restrict__ a, int64_t P, 
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        uint4 af = *reinterpret_cast<const uint4*>(sa + hbm_pos(wm * 16 * RB + rb * 16 + i16, 4 * h + g));
+        const int ra = wm * 16 * RB + rb * 16 + i16;
+        uint4 af;
+        if constexpr (F8)
+          af = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(sa + hbm_pos8(ra, 2 * h + (g >> 1)) + 8 * (g & 1)));
+        else
+          af = *reinterpret_cast<const uint4*>(sa + hbm_pos(ra, 4 * h + g));
         if (RAGGED && !kok) af = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = mfma(af, bf[cb], acc[rb][cb]);
       }
     }
   }
-  store_tile<RB>(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane);
+  store_tile<RB, F8>(acc, P, row0, N, col0, M, yrow0, y, wm, wn, lane, scale);
 }
 
 // Host super-step S (k in [128 S, 128 S + 128)) of A-wave w's 64 rows into a
@@ -329,12 +418,42 @@ __device__ __forceinline__ void host_a_issue(const uint16_t* __restrict__ a, int
   }
 }
 
+// The same for FP8 rows (K bytes each): super-step S holds codes
+// [256 S, 256 S + 256), 8 k-steps.
+template <bool COUNT>
+__device__ __forceinline__ void host_a_issue8(const unsigned char* __restrict__ a, int64_t P, int64_t row0,
+                                              int64_t K, int64_t S, unsigned char* slot, int wave, int lane,
+                                              uint64_t& nbytes) {
+  const int pos = lane & 15, rl = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 64 * wave + 4 * j + rl;
+    const int gp = pos ^ ((4 * j + rl) & 15);
+    const bool in = row0 + r < P;
+    const int64_t k = 256 * S + 16 * gp;
+    const bool kin = k < K;
+    dma16(a + (in ? row0 + r : row0) * K + (kin ? k : 0), slot + (64 * wave + 4 * j) * kSuperRow);
+    if (COUNT && in && kin) nbytes += 16;
+  }
+}
+
 // The tile of `tile` for host rows: A through two super-slots (one super-step
 // in flight while the other is consumed), x through kHostSX one-step slots.
-template <bool COUNT, bool RAGGED>
-__device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_t P, int64_t row0,
+// F8: A holds e4m3 codes, super-steps of 8 k-steps, stored times the scales.
+template <bool F8, bool COUNT, bool RAGGED>
+__device__ __forceinline__ void tile_host(const void* __restrict__ a, int64_t P, int64_t row0,
                                           const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
-                                          int64_t M, float* __restrict__ y, unsigned char* lds, uint64_t& nbytes) {
+                                          int64_t M, float* __restrict__ y, const float* __restrict__ scale,
+                                          unsigned char* lds, uint64_t& nbytes) {
+  constexpr int kSteps = F8 ? 2 * kSuper : kSuper;   // k-steps per super-step
+  const uint16_t* const a16 = static_cast<const uint16_t*>(a);
+  const unsigned char* const a8 = static_cast<const unsigned char*>(a);
+  auto a_issue = [&](int64_t S, unsigned char* slot, int wave, int lane) {
+    if constexpr (F8)
+      host_a_issue8<COUNT>(a8, P, row0, K, S, slot, wave, lane, nbytes);
+    else
+      host_a_issue<COUNT>(a16, P, row0, K, S, slot, wave, lane, nbytes);
+  };
   static_assert(kHostSX >= 2 && (kHostSX - 2) * kDmaPerWave <= 63, "x ring");
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
@@ -344,25 +463,25 @@ __device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_
   for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t T = (K + 31) >> 5, TS = (T + kSuper - 1) / kSuper;
-  const TileDma d = tile_dma(a, P, row0, kBM, x, N, col0, K, wave, lane);   // x waves use it
+  const int64_t T = (K + 31) >> 5, TS = (T + kSteps - 1) / kSteps;
+  const TileDma d = tile_dma(a16, P, row0, kBM, x, N, col0, K, wave, lane);   // x waves use it
   unsigned char* const ring_a = lds;
   unsigned char* const ring_x = lds + 2 * kSuperSlot;
   if (is_a) {
-    host_a_issue<COUNT>(a, P, row0, K, 0, ring_a, wave, lane, nbytes);
+    a_issue(0, ring_a, wave, lane);
   } else {
 #pragma unroll
     for (int s = 0; s < kHostSX - 1; ++s)
       if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, ring_x + s * kSlotA, wave, nbytes);
   }
-  // Step s: A waves wait for super-step s / 4 at its first step; x waves for
+  // Step s: A waves wait for super-step s / kSteps at its first step; x waves for
   // step s.  After the barrier (every read of step s - 1 retired), the first
   // step of a super-step refills the other super-slot with the next super-step
   // and every step refills x's slot of step s - 1.
   int rx = 0;
   for (int64_t s = 0; s < T; ++s) {
-    const int ss = (int)(s & (kSuper - 1));
-    const int64_t S = s / kSuper;
+    const int ss = (int)(s & (kSteps - 1));
+    const int64_t S = s / kSteps;
     if (is_a) {
       if (ss == 0) vm_wait<0>();
     } else {
@@ -371,26 +490,28 @@ __device__ __forceinline__ void tile_host(const uint16_t* __restrict__ a, int64_
     __builtin_amdgcn_s_barrier();
     if (is_a) {
       if (ss == 0 && S + 1 < TS)
-        host_a_issue<COUNT>(a, P, row0, K, S + 1, ring_a + ((S + 1) & 1) * kSuperSlot, wave, lane, nbytes);
+        a_issue(S + 1, ring_a + ((S + 1) & 1) * kSuperSlot, wave, lane);
     } else {
       if (s + kHostSX - 1 < T)
         tile_issue<COUNT, RAGGED>(d, s + kHostSX - 1, K, ring_x + (rx == 0 ? kHostSX - 1 : rx - 1) * kSlotA, wave,
                                   nbytes);
     }
-    tile_step<RAGGED, true, 8>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
+    tile_step<RAGGED, true, 8, F8>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
                             32 * s + 8 * (lane >> 4) < K, acc);
     rx = rx == kHostSX - 1 ? 0 : rx + 1;
   }
-  store_tile<8>(acc, P, row0, N, col0, M, 0, y, wm, wn, lane);
+  store_tile<8, F8>(acc, P, row0, N, col0, M, 0, y, wm, wn, lane, scale);
 }
 
 // HBM rows: hbm_n1 row tiles of 256 rows, then the rest in tiles of 32 RB2
-// rows (tiled_choose_plan).
-template <bool COUNT, bool RAGGED, int RB2>
+// rows (tiled_choose_plan).  F8: A holds e4m3 codes and row_scale the rows'
+// scales; else A holds bf16 and row_scale is unused.  RAGGED: K is not a
+// multiple of 64 (the HBM step).
+template <bool F8, bool COUNT, bool RAGGED, int RB2>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
-    const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
-    int64_t host_rows, const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, int n_groups, int cus,
-    int n_xcd, int64_t hbm_n1, unsigned long long* __restrict__ counters,
+    const void* __restrict__ a_host, const void* __restrict__ a_hbm, int64_t M, int64_t K, int64_t host_rows,
+    const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, const float* __restrict__ row_scale,
+    int n_groups, int cus, int n_xcd, int64_t hbm_n1, unsigned long long* __restrict__ counters,
     unsigned long long* __restrict__ xcc_masks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
@@ -413,20 +534,22 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   if (host_role) {
     for (int64_t rb = w.first; rb < w.end; rb += w.stride) {
       __syncthreads();   // the ring is reused
-      tile_host<COUNT, RAGGED>(a_host, host_rows, rb * kBM, x, N, (int64_t)w.col_tile * kBN, K, M, y, lds, nbytes);
+      tile_host<F8, COUNT, RAGGED>(a_host, host_rows, rb * kBM, x, N, (int64_t)w.col_tile * kBN, K, M, y, row_scale,
+                                   lds, nbytes);
     }
   } else {
     for (int64_t t = w.first; t < w.end; t += w.stride) {
       __syncthreads();   // the ring is reused
-      tile<COUNT, RAGGED, kBM / 32>(a_hbm, P, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, lds, nbytes);
+      tile<F8, COUNT, RAGGED, kBM / 32>(a_hbm, P, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, row_scale,
+                                        lds, nbytes);
     }
     if (rows2 > 0) {
       const TiledWork w2 = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks,
                                       (rows2 + kRows2 - 1) / kRows2 * tn, true);
       for (int64_t t = w2.first; t < w2.end; t += w2.stride) {
         __syncthreads();   // the ring is reused
-        tile<COUNT, RAGGED, RB2>(a_hbm, P, kBM * hbm_n1 + t / tn * kRows2, x, N, t % tn * kBN, K, M, host_rows, y,
-                                 lds, nbytes);
+        tile<F8, COUNT, RAGGED, RB2>(a_hbm, P, kBM * hbm_n1 + t / tn * kRows2, x, N, t % tn * kBN, K, M, host_rows,
+                                     y, row_scale, lds, nbytes);
       }
     }
   }
@@ -443,13 +566,13 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
 
 int tiled_max_host_groups(int64_t N, int cus) { return tiled_max_groups(cus, (int)((N + kBN - 1) / kBN)); }
 
-template <int RB2>
+template <bool F8, int RB2>
 static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
-  const bool ragged = (g.K & 31) != 0;
-#define DAK_TILED(C, R)                                                                                               \
-  hipLaunchKernelGGL((gemm_tiled_split<C, R, RB2>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream, g.a_host,          \
-                     g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.n_groups, g.cus, n_xcd, g.hbm_n1, g.counters, \
-                     g.xcc_masks)
+  const bool ragged = (g.K & 63) != 0;   // the HBM role's 64-k steps (the host role's 32-k steps divide them)
+#define DAK_TILED(C, R)                                                                                          \
+  hipLaunchKernelGGL((gemm_tiled_split<F8, C, R, RB2>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream,           \
+                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.row_scale, g.n_groups, g.cus, \
+                     n_xcd, g.hbm_n1, g.counters, g.xcc_masks)
   if (count) {
     if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
   } else {
@@ -458,17 +581,25 @@ static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
 #undef DAK_TILED
 }
 
+template <bool F8>
+static void launch_height(const TiledArgs& g, bool count, int n_xcd) {
+  switch (g.hbm_rb2) {
+    case 4: return launch_rb<F8, 4>(g, count, n_xcd);
+    case 5: return launch_rb<F8, 5>(g, count, n_xcd);
+    case 6: return launch_rb<F8, 6>(g, count, n_xcd);
+    case 7: return launch_rb<F8, 7>(g, count, n_xcd);
+    default: return launch_rb<F8, 8>(g, count, n_xcd);
+  }
+}
+
 void launch_gemm_tiled(const TiledArgs& g, bool count) {
   const int n_xcd = tiled_xcds(g.cus);
   static_assert(kTiledRbMin == 4 && kTiledRbMax == 8 && kBM == 32 * kTiledRbMax,
                 "one instance per second-phase tile height; first-phase tiles are kBM rows");
-  switch (g.hbm_rb2) {
-    case 4: return launch_rb<4>(g, count, n_xcd);
-    case 5: return launch_rb<5>(g, count, n_xcd);
-    case 6: return launch_rb<6>(g, count, n_xcd);
-    case 7: return launch_rb<7>(g, count, n_xcd);
-    default: return launch_rb<8>(g, count, n_xcd);
-  }
+  if (g.f8)
+    launch_height<true>(g, count, n_xcd);
+  else
+    launch_height<false>(g, count, n_xcd);
 }
 
 }  // namespace dak

@@ -170,11 +170,12 @@ constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t 
 // blocks go round by round to the groups (a round lasts as long as a tile, as
 // one group's stream of a block, or as the link needs for all active groups'
 // blocks, whichever is longest); the HBM role takes its chosen plan's
-// modelled duration, a 256-row tile lasting `t_tile`.
+// modelled duration, a 256-row tile lasting `t_tile`.  elem_bytes: bytes per
+// weight (2 for bf16, 1 for FP8 codes, which feed the same bf16 MFMAs).
 constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_rows, int64_t K,
-                                  TiledCost c) {
+                                  TiledCost c, int elem_bytes = 2) {
   const double t_tile = (double)((K + 31) / 32) * c.step_us;
-  const double block_bytes = 256.0 * (double)K * 2.0;
+  const double block_bytes = 256.0 * (double)K * elem_bytes;
   double t_host = 0.0;
   int64_t left = (host_rows + 255) / 256;
   while (left > 0) {
@@ -192,7 +193,7 @@ constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_ro
 // row block) with the least predicted time, the fewest on ties; 0 without
 // host rows.
 constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_rows, int64_t K, int cap,
-                                  TiledCost c = kTiledCostMi355x) {
+                                  int elem_bytes = 2, TiledCost c = kTiledCostMi355x) {
   if (host_rows <= 0) return 0;
   const int64_t blocks = (host_rows + 255) / 256;
   int hi = tiled_max_groups(cus, tn);
@@ -200,9 +201,9 @@ constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hb
   if (blocks < hi) hi = (int)blocks;
   if (hi < 1) hi = 1;
   int best = 1;
-  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c);
+  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c, elem_bytes);
   for (int g = 2; g <= hi; ++g) {
-    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c);
+    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes);
     if (t < best_t * (1.0 - 1e-9)) {
       best = g;
       best_t = t;

@@ -101,8 +101,6 @@ class DecodeModel:
             raise ValueError("weights must be 'bf16' or 'fp8'")
         if kv_unit not in (KV_UNIT_REQUEST, KV_UNIT_HEAD):
             raise ValueError("kv_unit must be KV_UNIT_REQUEST or KV_UNIT_HEAD")
-        if weights == "fp8" and batch > 64:
-            raise ValueError("the FP8 split GEMM takes N <= 64 activations")
         self.shape, self.batch, self.ctx, self.m = shape, batch, ctx, m
         self.b_hbm, self.b_host = b_hbm, b_host
         self.weights, self.kv_unit = weights, kv_unit

@@ -576,29 +576,39 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     (x holds B^T, N = 2048), 64-row tile-rows.  The op's compute time at x = 0
     gives the planner's turning point b (DAK paper §4.2.1: host reads hide
     behind compute while x C / B_host <= T_comp); the kernel is timed at x = 0,
-    at b / n and on a sweep of x up to 0.75, and its MFMA utilisation reported."""
+    at b / n and on a sweep of x up to 0.75, and its MFMA utilisation reported.
+    `--prefill-weights fp8`: the same shape with FP8 weights (e4m3 codes, one
+    fp32 scale per row, widened to bf16 for the same MFMAs): half the bytes per
+    tile-row, so about twice the host share before the turning point."""
     M, K, N = 28672, 8192, 2048
     n = M // M_TILE
-    C = M * K * 2
+    fp8 = args.prefill_weights == "fp8"
+    C = M * K * (1 if fp8 else 2)
     flops = 2 * M * K * N
-    A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
+    if fp8:
+        A, scale, X = synth.fp8_gemm_inputs(M, K, N, seed=0, device="cuda")
+    else:
+        A, X = synth.gemm_inputs(M, K, N, seed=0, device="cuda")
     hmax = host_units(3, 4, n)
-    A_host = torch.empty((hmax * M_TILE, K), dtype=torch.bfloat16, pin_memory=True)
+    A_host = torch.empty((hmax * M_TILE, K), dtype=A.dtype, pin_memory=True)
     A_host.copy_(A[:hmax * M_TILE])
     y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    gemm = dak.splitk_gemm_fp8 if fp8 else dak.splitk_gemm
 
     def desc(h):
-        return dak.SplitMatrix(A_host[:h * M_TILE] if h else None, A[h * M_TILE:] if h < n else None,
-                               M, K, M_TILE, h)
+        hp, gp = A_host[:h * M_TILE] if h else None, A[h * M_TILE:] if h < n else None
+        if fp8:
+            return dak.SplitMatrixFP8(hp, gp, scale, M, K, M_TILE, h)
+        return dak.SplitMatrix(hp, gp, M, K, M_TILE, h)
 
     def time_h(h, reps):
         S = desc(h)
         for _ in range(args.warmup):
-            dak.splitk_gemm(S, X, y=y)
+            gemm(S, X, y=y)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for e0, e1 in ev:
             e0.record()
-            dak.splitk_gemm(S, X, y=y)
+            gemm(S, X, y=y)
             e1.record()
         torch.cuda.synchronize()
         return statistics.mean(e0.elapsed_time(e1) for e0, e1 in ev)
@@ -611,7 +621,7 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     t_end = time.perf_counter() + args.warm_seconds
     while time.perf_counter() < t_end:
         for _ in range(20):
-            dak.splitk_gemm(S0, X, y=y)
+            gemm(S0, X, y=y)
         torch.cuda.synchronize()
     t0s = [time_h(0, reps)]
     a, b, mb = dak.op_turning_points(dak.Op(n, C // n, t0s[0] * 1e-3), b_hbm * 1e9, b_host * 1e9)
@@ -633,7 +643,11 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
     sweep.insert(0, {"x": 0.0, "h": 0, "ms": round(t0, 4), "TFLOPs": round(flops / t0 / 1e9, 1),
                      "x0_ms_paired": round(t0, 4), "slowdown_vs_x0": 1.0, "model_ms": round(t0, 4),
                      "frac_of_model": 1.0})
-    # a library GEMM of the same shape, all in HBM, as context for the MFMA rate
+    # a library GEMM of the same shape (bf16 weights), all in HBM, as context
+    # for the MFMA rate
+    if fp8:
+        del A_host
+        A = synth.gemm_inputs(M, K, 1, seed=0, device="cuda")[0]   # timing only
     Bt = X.t()
     for _ in range(args.warmup):
         torch.matmul(A, Bt)
@@ -651,8 +665,11 @@ def run_prefill(torch, dak, args, b_hbm, b_host):
         "metric": "TFLOP/s of the compute-bound split GEMM and its slowdown at the planner's host share",
         "value": round(flops / at_b["ms"] / 1e9, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": reps,
         "warmup": args.warmup, "ms_per_step": at_b["ms"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
-        "config": {"workload": "prefill split GEMM A 28672x8192 . B 8192x2048, 64-row tile-rows",
+        "vs_baseline": None,
+        "dtype": ("e4m3 weights widened to bf16, " if fp8 else "") + "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "prefill split GEMM A 28672x8192 . B 8192x2048, 64-row tile-rows"
+                               + (", FP8 weights" if fp8 else ""),
                    "x": at_b["x"], "h": b, "n": n},
         "turning_points": {"a": a, "b": b, "memory_bound": mb, "t_comp_ms": round(t0s[0], 4)},
         "slowdown_at_b": at_b["slowdown_vs_x0"], "x0_ms_all": [round(t, 4) for t in t0s],
@@ -1191,6 +1208,7 @@ def main(argv=None):
                     help="plan-compare: global host shares to compare at")
     ap.add_argument("--b70-batch", type=int, default=16, help="llama70b: requests (activation rows N)")
     ap.add_argument("--b70-weights", choices=("bf16", "fp8"), default="bf16", help="llama70b: weight format")
+    ap.add_argument("--prefill-weights", choices=("bf16", "fp8"), default="bf16", help="prefill: weight format")
     ap.add_argument("--b70-kv-unit", choices=("request", "head"), default="request",
                     help="llama70b: KV host unit (whole requests or single (request, KV head) pairs)")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,

@@ -107,6 +107,18 @@ int main() {
   CHECK(tiled_choose_groups(256, 8, 45 * 64, 28672 - 45 * 64, 8192, 1 << 20) == 6, "h=45");
   CHECK(tiled_choose_groups(256, 8, 52 * 64, 28672 - 52 * 64, 8192, 1 << 20) == 7, "h=52");
   CHECK(tiled_choose_groups(256, 8, 59 * 64, 28672 - 59 * 64, 8192, 1 << 20) == 8, "h=59");
+  // All 14336 rows of 8192 on the host: bf16 rows need 7 groups to fill the
+  // link (measured: 7 and 8 groups 4.24-4.28 ms, 14 groups 4.41 ms), FP8 rows
+  // (one byte per weight, the same compute per block) 14 (measured: 7 groups
+  // 2.57 ms, 8 2.36, 12 2.19, 14 2.17).
+  CHECK(tiled_choose_groups(256, 8, 14336, 0, 8192, 1 << 20, 2) == 7, "all-host bf16");
+  CHECK(tiled_choose_groups(256, 8, 14336, 0, 8192, 1 << 20, 1) == 14, "all-host fp8");
+  // the smooth maximum
+  CHECK(tiled_smax(3.0, 0.0, 0.0) == 3.0 && tiled_smax(0.0, 0.0, 0.0) == 0.0, "smax");
+  {
+    const double v = tiled_smax(1.0, 1.0, 0.0);   // 2^(1/6)
+    CHECK(v > 1.122462 && v < 1.122463, "smax(1, 1, 0) = %.9f", v);
+  }
   // HBM plan: first-phase tiles all full (256 n1 < rows), the two phases
   // cover the rows, heights within [4, 8]; never costlier under the model than
   // one walk of 256-row tiles; the model's cost equals the slowest work-group

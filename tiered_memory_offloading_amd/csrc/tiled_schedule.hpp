@@ -69,15 +69,35 @@ namespace dak {
 
 // Time model used to pick the number of host groups (the choice only places
 // work; results do not depend on it).  Constants measured on MI355X with the
-// 28672 x 8192 x 2048 prefill GEMM (warm clocks): one 32-k step of a 256 x 256
-// tile takes ~0.92 us; a group streams ~10 GB/s of host rows when the link is
-// not the limit (one 64 KiB super-step in flight); the link carries ~55 GB/s.
+// 28672 x 8192 x 2048 prefill GEMM and all-host GEMMs of 8192-long rows (warm
+// clocks): one 32-k step of a 256 x 256 HBM tile takes ~0.92 us and of a host
+// tile ~1.125 us (x staged per step, a barrier each); a group streams ~11.5
+// GB/s of host rows when neither its compute nor the link is the limit (one
+// 64 KiB super-step in flight); the link carries ~55 GB/s.
 struct TiledCost {
   double step_us;
+  double host_step_us;
   double group_gbps;
   double link_gbps;
 };
-inline constexpr TiledCost kTiledCostMi355x{0.92, 10.0, 55.0};
+inline constexpr TiledCost kTiledCostMi355x{0.92, 1.125, 11.5, 55.0};
+
+// A smooth maximum, (a^6 + b^6 + c^6)^(1/6): a host round's compute, its
+// group's stream and the link's share overlap, but not perfectly when two of
+// them are close (fitted to all-host rounds of 4 to 24 groups with bf16 and
+// FP8 rows: within 4 % of the measured round times).
+constexpr double tiled_smax(double a, double b, double c) {
+  const double m = a > b ? (a > c ? a : c) : (b > c ? b : c);
+  if (m <= 0.0) return 0.0;
+  const double ra = a / m, rb = b / m, rc = c / m;
+  const double t = ra * ra * ra * ra * ra * ra + rb * rb * rb * rb * rb * rb + rc * rc * rc * rc * rc * rc;
+  double r = 1.0 + (t - 1.0) / 6.0;   // t in [1, 3]: Newton steps on r^6 = t
+  for (int i = 0; i < 8; ++i) {
+    const double r5 = r * r * r * r * r;
+    r -= (r5 * r - t) / (6.0 * r5);
+  }
+  return m * r;
+}
 
 constexpr double tiled_max_d(double a, double b) { return a > b ? a : b; }
 
@@ -167,21 +187,22 @@ constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t 
 }
 
 // Predicted microseconds of a launch with `n_groups` host groups: host row
-// blocks go round by round to the groups (a round lasts as long as a tile, as
-// one group's stream of a block, or as the link needs for all active groups'
-// blocks, whichever is longest); the HBM role takes its chosen plan's
+// blocks go round by round to the groups (a round lasts the smooth maximum of
+// a host tile's compute, one group's stream of a block and the link's time
+// for all active groups' blocks); the HBM role takes its chosen plan's
 // modelled duration, a 256-row tile lasting `t_tile`.  elem_bytes: bytes per
 // weight (2 for bf16, 1 for FP8 codes, which feed the same bf16 MFMAs).
 constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_rows, int64_t K,
                                   TiledCost c, int elem_bytes = 2) {
   const double t_tile = (double)((K + 31) / 32) * c.step_us;
+  const double t_host_tile = (double)((K + 31) / 32) * c.host_step_us;
   const double block_bytes = 256.0 * (double)K * elem_bytes;
   double t_host = 0.0;
   int64_t left = (host_rows + 255) / 256;
   while (left > 0) {
     const int64_t active = left < n_groups ? left : n_groups;
-    t_host += tiled_max_d(t_tile, tiled_max_d(block_bytes / (c.group_gbps * 1e3),
-                                              (double)active * block_bytes / (c.link_gbps * 1e3)));
+    t_host += tiled_smax(t_host_tile, block_bytes / (c.group_gbps * 1e3),
+                         (double)active * block_bytes / (c.link_gbps * 1e3));
     left -= active;
   }
   const TiledHbmPlan p = tiled_choose_plan(cus, tn, n_groups, hbm_rows);
@@ -189,9 +210,11 @@ constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_ro
   return tiled_max_d(t_host, t_hbm);
 }
 
-// Host groups for a launch: the count in [1, cap] (and at most one per host
-// row block) with the least predicted time, the fewest on ties; 0 without
-// host rows.
+// Host groups for a launch: the fewest in [1, cap] (and at most one per host
+// row block) predicted within 2 % of the fastest count.  More groups than the
+// link needs put more host requests in flight, which the model does not price
+// and which measured slower (all-host bf16 rows: 8 groups 4.22 ms, 16-24
+// groups 4.45-4.50 ms); 0 without host rows.
 constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_rows, int64_t K, int cap,
                                   int elem_bytes = 2, TiledCost c = kTiledCostMi355x) {
   if (host_rows <= 0) return 0;
@@ -200,16 +223,14 @@ constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hb
   if (cap < hi) hi = cap;
   if (blocks < hi) hi = (int)blocks;
   if (hi < 1) hi = 1;
-  int best = 1;
-  double best_t = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c, elem_bytes);
+  double fastest = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c, elem_bytes);
   for (int g = 2; g <= hi; ++g) {
     const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes);
-    if (t < best_t * (1.0 - 1e-9)) {
-      best = g;
-      best_t = t;
-    }
+    fastest = t < fastest ? t : fastest;
   }
-  return best;
+  for (int g = 1; g < hi; ++g)
+    if (tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes) <= fastest * 1.02) return g;
+  return hi;
 }
 
 }  // namespace dak

@@ -1025,7 +1025,9 @@ def run_plan_compare(torch, dak, args, b_hbm, b_host):
         return ms, [a.elapsed_time(b) for a, b in evs]
 
     log(f"all-HBM layer at batch {batch}, ctx {ctx}: per-op times for T_comp")
-    base = DecodeModel(LLAMA8B_ONE_LAYER, batch, ctx, b_hbm * 1e9, b_host * 1e9, free, x_global=0.0, log=log)
+    wts = args.plan_weights
+    base = DecodeModel(LLAMA8B_ONE_LAYER, batch, ctx, b_hbm * 1e9, b_host * 1e9, free, x_global=0.0, log=log,
+                       weights=wts)
     _, op0 = time_model(base)
     t_comp = {}
     for o, t in zip(base.slots, op0):
@@ -1040,7 +1042,7 @@ def run_plan_compare(torch, dak, args, b_hbm, b_host):
         row = {"x_global": xg}
         for policy in ("uniform", "greedy"):
             mdl = DecodeModel(LLAMA8B_ONE_LAYER, batch, ctx, b_hbm * 1e9, b_host * 1e9, free, x_global=xg,
-                              policy=policy, t_comp=lambda o: t_comp[o.kind], log=lambda *_: None)
+                              policy=policy, t_comp=lambda o: t_comp[o.kind], log=lambda *_: None, weights=wts)
             ms, op_ms = time_model(mdl)
             row[policy] = {"ms": round(ms, 4), "modeled_ms": round(mdl.modeled_s * 1e3, 4),
                            "host_bytes": mdl.host_bytes,
@@ -1058,9 +1060,11 @@ def run_plan_compare(torch, dak, args, b_hbm, b_host):
         "value": round(statistics.mean(r["speedup_greedy_over_uniform"] for r in rows), 4),
         "unit": "mean speedup (uniform ms / greedy ms)", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic (seeded, generated on the GPU)",
+        "dtype": ("e4m3 weights, " if wts == "fp8" else "") + "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded, generated on the GPU)",
         "config": {"workload": f"one Llama-8B decoder layer (QKV, split-KV attention 32q/8kv hd128, O, gate+up, "
-                               f"down) at batch {batch}, {ctx} ctx/request", "footprint_bytes": footprint},
+                               f"down) at batch {batch}, {ctx} ctx/request"
+                               + (", FP8 weights" if wts == "fp8" else ""), "footprint_bytes": footprint},
         "t_comp_ms": {k: round(v * 1e3, 4) for k, v in t_comp.items()},
         "all_hbm_op_ms": {"qkv": round(op0[0], 4), "attn": round(op0[1], 4), "o": round(op0[2], 4),
                           "gate_up": round(op0[3], 4), "down": round(op0[4], 4)},
@@ -1209,6 +1213,7 @@ def main(argv=None):
     ap.add_argument("--b70-batch", type=int, default=16, help="llama70b: requests (activation rows N)")
     ap.add_argument("--b70-weights", choices=("bf16", "fp8"), default="bf16", help="llama70b: weight format")
     ap.add_argument("--prefill-weights", choices=("bf16", "fp8"), default="bf16", help="prefill: weight format")
+    ap.add_argument("--plan-weights", choices=("bf16", "fp8"), default="bf16", help="plan-compare: weight format")
     ap.add_argument("--b70-kv-unit", choices=("request", "head"), default="request",
                     help="llama70b: KV host unit (whole requests or single (request, KV head) pairs)")
     ap.add_argument("--hbm-reserve-gib", type=float, default=3.0,

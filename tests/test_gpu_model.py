@@ -22,9 +22,11 @@ def _cat(a, b):
     return torch.cat(parts, dim=0)
 
 
-@pytest.mark.parametrize("weights, kv_unit", [("bf16", dak.KV_UNIT_REQUEST), ("fp8", dak.KV_UNIT_HEAD)])
-def test_planned_step_matches_the_oracle(weights, kv_unit):
-    B, ctx = 4, 600
+@pytest.mark.parametrize("weights, kv_unit, B", [("bf16", dak.KV_UNIT_REQUEST, 4), ("fp8", dak.KV_UNIT_HEAD, 4),
+                                                  ("fp8", dak.KV_UNIT_REQUEST, 96)])
+def test_planned_step_matches_the_oracle(weights, kv_unit, B):
+    # B = 96: the linears run at N = 96, FP8 weights through the tiled kernel.
+    ctx = 600
     probe = DecodeModel(SMALL, B, ctx, 6.4e12, 57.5e9, 1 << 40, weights=weights, kv_unit=kv_unit,
                         log=lambda *_: None)
     H = int(probe.footprint * 0.8)                        # x_global = 0.2

@@ -51,7 +51,7 @@ const char* dak_last_error(void);
 int32_t dak_last_hip_error(void);
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t dak_abi_version(void);
-#define DAK_ABI_VERSION 2
+#define DAK_ABI_VERSION 3
 
 /* ------------------------------------------------------------------------ */
 /* Capacity and planning (pure CPU, deterministic)                            */
@@ -246,6 +246,27 @@ typedef struct {
 dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, float* y,
                            const dak_launch_cfg* cfg, void* stream);
 
+/* Bytes of workspace that dak_splitk_gemm_ws uses for an M x K weight and N
+ * activation rows; 0 when the shape is not split.  Shapes of the tiled kernel
+ * (N > 256) whose 256 x 256 output tiles would leave most CUs of a round idle
+ * (small M: QKV, O or down at a prefill-sized N) split K into 2, 4 or 8
+ * segments, chosen from (M, K, N) alone; the workspace holds one fp32 [N, M]
+ * partial output per segment. */
+uint64_t dak_splitk_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* dak_splitk_gemm with a workspace.  ws: device memory, 16-byte aligned, of
+ * at least dak_splitk_gemm_workspace_bytes(M, K, N) bytes, owned by the
+ * caller and not read after the call's work completes on `stream`; NULL runs
+ * the shape unsplit (as dak_splitk_gemm does).  Split, each output is the
+ * sum, in segment order, of one fp32 MFMA chain per K segment, added by a
+ * second kernel on the same stream: a different rounding order from the
+ * unsplit launch, still bit-identical for every h, host_cus and window.
+ * Errors: those of dak_splitk_gemm, and DAK_EINVAL for a non-NULL workspace
+ * that is too small, misaligned or not device memory.  Calls that share one
+ * workspace must not overlap. */
+dak_status dak_splitk_gemm_ws(const dak_split_matrix* A, const void* x, int64_t N, float* y, void* ws,
+                              uint64_t ws_bytes, const dak_launch_cfg* cfg, void* stream);
+
 /* A weight matrix of FP8 codes, cut along M like dak_split_matrix.  Each
  * weight is an OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
  * mantissa bits; no infinities; 0x7F and 0xFF are NaN) and each row r carries
@@ -292,6 +313,13 @@ typedef struct {
  * N > 64.  A NaN code gives NaN in its row. */
 dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
                                const dak_launch_cfg* cfg, void* stream);
+
+/* The FP8 counterparts of dak_splitk_gemm_workspace_bytes and
+ * dak_splitk_gemm_ws (the tiled kernel, and so a split, starts at N > 64);
+ * split, the row scale multiplies the sum of the segments' partial sums. */
+uint64_t dak_splitk_gemm_fp8_workspace_bytes(int64_t M, int64_t K, int64_t N);
+dak_status dak_splitk_gemm_fp8_ws(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y, void* ws,
+                                  uint64_t ws_bytes, const dak_launch_cfg* cfg, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Split decode attention: KV cache split along the batch                      */

@@ -213,3 +213,21 @@ def test_wide_n_nan_code_poisons_its_row_only():
         assert torch.isnan(y[:, 17]).all() and torch.isnan(y[:, 300]).all()
         keep = [r for r in range(M) if r not in (17, 300)]
         assert torch.equal(y[:, keep], base[:, keep])
+
+
+@pytest.mark.parametrize("M, K, N", [(512, 2048, 300), (64, 1024, 65), (512, 2080, 100)])
+def test_wide_n_k_segments(M, K, N):
+    # Shapes that split K (the FP8 tiled kernel starts at N > 64): every
+    # code, all splits bit-identical, against the oracle; the row scale
+    # multiplies the sum of the segments.
+    assert dak.library().dak_splitk_gemm_fp8_workspace_bytes(M, K, N) > 0
+    codes = synth.fp8_all_codes(M, K, seed=M + N)
+    scale = torch.rand(M, generator=torch.Generator().manual_seed(M + N)) * 0.01 + 1e-3
+    x = synth.gemm_inputs(16, K, N, seed=M + N)[1]
+    ref = of.gemm_fp8(codes, scale, x)
+    base = run(codes, scale, x, 64, 0)
+    err = normwise_error(base.numpy(), ref)
+    print(f"M={M} K={K} N={N} split normwise error {err:.3e}")
+    assert err <= TOL
+    for h in range(1, M // 64 + 1):
+        assert torch.equal(run(codes, scale, x, 64, h), base), h

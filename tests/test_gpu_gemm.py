@@ -263,6 +263,54 @@ def test_wide_n_every_hbm_tile_height_bit_identical(M):
         assert torch.equal(y, outs[0])
 
 
+@pytest.mark.parametrize("M,K,N", [(512, 2048, 300), (512, 2080, 300), (1024, 1024, 512), (320, 4096, 600)])
+def test_wide_n_k_segments_all_splits_bit_identical(M, K, N):
+    # Few 256 x 256 output tiles: K is cut into 2-8 segments (K = 2080 ends in
+    # a partial 64-k step inside the last segment), each output the sum of the
+    # segments' MFMA chains in segment order.  Against the oracle; every host
+    # share bit-identical; the unsplit launch within the same bar.
+    assert dak.library().dak_splitk_gemm_workspace_bytes(M, K, N) > 0
+    m = 64
+    A, X = synth.gemm_inputs(M, K, N, seed=200 + M + K + N)
+    ref = ref_of(A, X)
+    outs = [run(A, X, m, h) for h in range(M // m + 1)]
+    err = og.normwise_error(outs[0].numpy(), ref)
+    print(f"M={M} K={K} N={N} split normwise error {err:.3e}")
+    assert err <= TOL
+    for h, y in enumerate(outs[1:], 1):
+        assert torch.equal(y, outs[0]), f"h={h} differs from h=0"
+    S = dak.place_matrix(A, m, 2)
+    y1 = dak.splitk_gemm(S, X.cuda(), split=False)
+    torch.cuda.synchronize()
+    assert og.normwise_error(y1.cpu().numpy(), ref) <= TOL
+
+
+def test_wide_n_k_segments_integer_exact_and_workspace_checked():
+    M, K, N = 512, 2048, 300
+    A = synth.int_valued_bf16((M, K), -4, 4, seed=11)
+    X = synth.int_valued_bf16((N, K), -4, 4, seed=12)
+    ref = og.gemm_rows(og.to_f64(A), og.to_f64(X))
+    for h in (0, 3, 8):
+        assert np.array_equal(run(A, X, 64, h).double().numpy(), ref)
+    S = dak.place_matrix(A, 64, 3)
+    need = int(dak.library().dak_splitk_gemm_workspace_bytes(M, K, N))
+    Xd = X.cuda()
+    with pytest.raises(ValueError):                    # the binding's own size check
+        dak.splitk_gemm(S, Xd, ws=torch.empty((need - 16,), dtype=torch.uint8, device="cuda"))
+    y = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    big = torch.empty((need + 16,), dtype=torch.uint8, device="cuda")
+    lib = dak.library()
+    from tiered_memory_offloading_amd import _lib as L
+    d = S.desc()
+    small = lib.dak_splitk_gemm_ws(L.C.byref(d), Xd.data_ptr(), N, y.data_ptr(), big.data_ptr(), need - 16, None, None)
+    assert small == -1                                 # DAK_EINVAL: too small
+    odd = lib.dak_splitk_gemm_ws(L.C.byref(d), Xd.data_ptr(), N, y.data_ptr(), big.data_ptr() + 4, need, None, None)
+    assert odd == -1                                   # DAK_EINVAL: not 16-byte aligned
+    assert lib.dak_splitk_gemm_ws(L.C.byref(d), Xd.data_ptr(), N, y.data_ptr(), big.data_ptr(), need, None, None) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(y.double().cpu().numpy(), ref)
+
+
 def test_wide_n_bytes_requested_per_column_tile():
     M, K, N, h = 1024, 1024, 512, 7
     A, X = synth.gemm_inputs(M, K, N, seed=110)

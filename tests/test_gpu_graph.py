@@ -20,7 +20,7 @@ def test_graph_replays_match_eager_launches():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     mats = []
     for M, K, N, h in [(320, 1000, 1, 2), (320, 1000, 16, 2), (512, 1024, 64, 3), (320, 1000, 100, 2),
-                       (320, 1000, 300, 2)]:
+                       (320, 1000, 300, 2), (512, 2048, 300, 3)]:   # the last splits K (a second kernel)
         A, X = synth.gemm_inputs(M, K, N, seed=M + N)
         mats.append((dak.place_matrix(A, 64, h), X.cuda(), torch.empty((N, M), dtype=torch.float32, device="cuda")))
     q, Kc, Vc = synth.attn_inputs(4, 8, 2, 128, 1000, seed=3)

@@ -172,6 +172,30 @@ int main() {
     CHECK(p.n1 == 78 && p.rb2 == 7 && tiled_plan_cost(256, 8, 6, 28672 - 45 * 64, p) == 47.0, "h=45: n1=%lld rb2=%d",
           (long long)p.n1, p.rb2);
   }
+  // K segments: unsplit (length K) or 2-8 segments of whole multiples of 256
+  // k, at least 512 each, covering K; on the shapes measured on MI355X:
+  // split at N = 512 for the Llama-8B QKV / O / down (4 / 4 / 8 segments,
+  // 1.3-4.3x faster), never for gate+up or the 28672 x 8192 x 2048 prefill
+  // GEMM, and not for O or the 70B-shaped QKV at N = 2048 (where two segments
+  // measured 10-14 % slower).
+  for (int64_t M : {64, 320, 1024, 4096, 6144, 28672})
+    for (int64_t K : {16, 520, 1000, 2080, 4096, 14336})
+      for (int64_t N : {257, 300, 512, 2048}) {
+        const int64_t len = tiled_k_seg_len(M, N, K);
+        const int segs = tiled_k_segs(K, len);
+        CHECK(segs >= 1 && segs <= kTiledMaxSegs, "M=%lld K=%lld N=%lld segs=%d", (long long)M, (long long)K,
+              (long long)N, segs);
+        if (segs > 1)
+          CHECK(len % 256 == 0 && len >= 512 && len * (segs - 1) < K && len * segs >= K, "M=%lld K=%lld N=%lld len=%lld",
+                (long long)M, (long long)K, (long long)N, (long long)len);
+        else
+          CHECK(len == K, "unsplit length");
+      }
+  auto segs_of = [](int64_t M, int64_t K, int64_t N) { return tiled_k_segs(K, tiled_k_seg_len(M, N, K)); };
+  CHECK(segs_of(6144, 4096, 512) == 4 && segs_of(4096, 4096, 512) == 4 && segs_of(4096, 14336, 512) == 8,
+        "Llama-8B QKV / O / down at N = 512");
+  CHECK(segs_of(28672, 4096, 512) == 1 && segs_of(28672, 8192, 2048) == 1, "gate+up, prefill");
+  CHECK(segs_of(4096, 4096, 2048) == 1 && segs_of(10240, 8192, 2048) == 1, "O, 70B QKV at N = 2048");
   // The XCD layout of MI355X: 8 x 32 CUs.
   CHECK(tiled_xcds(256) == 8 && tiled_max_groups(256, 8) == 24 && tiled_max_groups(256, 2) == 120, "MI355X layout");
   std::printf("%d configurations, %d failures\n", n, fails);

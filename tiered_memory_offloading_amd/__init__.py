@@ -306,9 +306,29 @@ def place_kv(K: torch.Tensor, V: torch.Tensor, h: int, device=None, unit: int = 
 # ----------------------------------------------------------------------------
 # Compute entry points
 # ----------------------------------------------------------------------------
+def _gemm_workspace(need: int, ws: Optional[torch.Tensor], device, stream) -> Optional[torch.Tensor]:
+    # The K-split workspace of a tiled launch: the caller's, or one from
+    # torch's allocator, kept alive for the stream the launch runs on.
+    if need == 0:
+        return None
+    if ws is None:
+        ws = torch.empty((need,), dtype=torch.uint8, device=device)
+        if isinstance(stream, torch.cuda.Stream):
+            ws.record_stream(stream)
+        return ws
+    if not ws.is_cuda or not ws.is_contiguous() or ws.numel() * ws.element_size() < need:
+        raise ValueError(f"ws must be a contiguous CUDA tensor of at least {need} bytes")
+    return ws
+
+
 def splitk_gemm(A: SplitMatrix, x: torch.Tensor, y: Optional[torch.Tensor] = None,
-                cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
-    """y[n, r] = sum_k A[r, k] x[n, k]; x bf16 [N, K] on the GPU, y fp32 [N, M]."""
+                cfg: Optional[LaunchConfig] = None, stream=None, ws: Optional[torch.Tensor] = None,
+                split: bool = True) -> torch.Tensor:
+    """y[n, r] = sum_k A[r, k] x[n, k]; x bf16 [N, K] on the GPU, y fp32 [N, M].
+
+    Shapes that the library splits along K (dak_splitk_gemm_workspace_bytes >
+    0) get a workspace: `ws`, or one allocated here; split=False runs them
+    unsplit (dak_splitk_gemm)."""
     lib = library()
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
@@ -322,7 +342,10 @@ def splitk_gemm(A: SplitMatrix, x: torch.Tensor, y: Optional[torch.Tensor] = Non
         raise ValueError("y must be a contiguous fp32 [N, M] tensor")
     d = A.desc()
     c, cp = _cfg_ptr(cfg)
-    _check(lib.dak_splitk_gemm(C.byref(d), x.data_ptr(), N, y.data_ptr(), cp, _stream_handle(stream)))
+    need = int(lib.dak_splitk_gemm_workspace_bytes(A.M, A.K, N)) if split else 0
+    w = _gemm_workspace(need, ws, x.device, stream)
+    _check(lib.dak_splitk_gemm_ws(C.byref(d), x.data_ptr(), N, y.data_ptr(), None if w is None else w.data_ptr(),
+                                  need, cp, _stream_handle(stream)))
     return y
 
 
@@ -382,7 +405,8 @@ def place_matrix_fp8(codes: torch.Tensor, row_scale: torch.Tensor, m: int, h: in
 
 
 def splitk_gemm_fp8(A: SplitMatrixFP8, x: torch.Tensor, y: Optional[torch.Tensor] = None,
-                    cfg: Optional[LaunchConfig] = None, stream=None) -> torch.Tensor:
+                    cfg: Optional[LaunchConfig] = None, stream=None, ws: Optional[torch.Tensor] = None,
+                    split: bool = True) -> torch.Tensor:
     """y[n, r] = row_scale[r] * sum_k e4m3(A[r, k]) x[n, k]; x bf16 [N, K] on
     the GPU (N <= 2048; N > 64 takes the compute-bound tiled kernel), y fp32
     [N, M]."""
@@ -399,7 +423,10 @@ def splitk_gemm_fp8(A: SplitMatrixFP8, x: torch.Tensor, y: Optional[torch.Tensor
         raise ValueError("y must be a contiguous fp32 [N, M] tensor")
     d = A.desc()
     c, cp = _cfg_ptr(cfg)
-    _check(lib.dak_splitk_gemm_fp8(C.byref(d), x.data_ptr(), N, y.data_ptr(), cp, _stream_handle(stream)))
+    need = int(lib.dak_splitk_gemm_fp8_workspace_bytes(A.M, A.K, N)) if split else 0
+    w = _gemm_workspace(need, ws, x.device, stream)
+    _check(lib.dak_splitk_gemm_fp8_ws(C.byref(d), x.data_ptr(), N, y.data_ptr(),
+                                      None if w is None else w.data_ptr(), need, cp, _stream_handle(stream)))
     return y
 
 

@@ -15,7 +15,7 @@ DAK_EUNSUPPORTED = -4
 DAK_FLAG_COUNT_BYTES = 1
 DAK_FLAG_STAGED_HOST = 2
 DAK_FLAG_RECORD_XCC = 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class OpDesc(C.Structure):
@@ -69,6 +69,12 @@ SIGNATURES = [
                                     C.POINTER(LaunchCfg), C.c_void_p]),
     ("dak_splitk_gemm_fp8", C.c_int32, [C.POINTER(SplitMatrixFP8Desc), C.c_void_p, C.c_int64, C.c_void_p,
                                         C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_splitk_gemm_workspace_bytes", C.c_uint64, [C.c_int64, C.c_int64, C.c_int64]),
+    ("dak_splitk_gemm_ws", C.c_int32, [C.POINTER(SplitMatrixDesc), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                       C.c_uint64, C.POINTER(LaunchCfg), C.c_void_p]),
+    ("dak_splitk_gemm_fp8_workspace_bytes", C.c_uint64, [C.c_int64, C.c_int64, C.c_int64]),
+    ("dak_splitk_gemm_fp8_ws", C.c_int32, [C.POINTER(SplitMatrixFP8Desc), C.c_void_p, C.c_int64, C.c_void_p,
+                                           C.c_void_p, C.c_uint64, C.POINTER(LaunchCfg), C.c_void_p]),
     ("dak_decode_attn_workspace_bytes", C.c_size_t, [C.POINTER(SplitKVDesc), C.c_int32]),
     ("dak_splitk_decode_attn", C.c_int32, [C.c_void_p, C.POINTER(SplitKVDesc), C.c_int32, C.c_float, C.c_void_p,
                                            C.c_void_p, C.c_size_t, C.POINTER(LaunchCfg), C.c_void_p]),

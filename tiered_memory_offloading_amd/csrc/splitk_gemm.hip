@@ -450,8 +450,20 @@ void launch_any(const GemmArgs& g, int window, bool fma, int nb, int rbw) {
 }  // namespace
 }  // namespace dak
 
+extern "C" uint64_t dak_splitk_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  using namespace dak;
+  if (M < 1 || K < 1 || N <= 256 || N > kTiledMaxN) return 0;   // only the tiled kernel splits K
+  const int segs = tiled_k_segs(K, tiled_k_seg_len(M, N, K));
+  return segs > 1 ? (uint64_t)segs * N * M * 4 : 0;
+}
+
 extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, int64_t N, float* y,
                                       const dak_launch_cfg* cfg, void* stream) {
+  return dak_splitk_gemm_ws(A, x, N, y, nullptr, 0, cfg, stream);
+}
+
+extern "C" dak_status dak_splitk_gemm_ws(const dak_split_matrix* A, const void* x, int64_t N, float* y, void* ws,
+                                         uint64_t ws_bytes, const dak_launch_cfg* cfg, void* stream) {
   using namespace dak;
   clear_error();
   if (!A) return fail(DAK_EINVAL, "A is NULL");
@@ -512,8 +524,10 @@ extern "C" dak_status dak_splitk_gemm(const dak_split_matrix* A, const void* x, 
     if (max_groups < 1)
       return fail(DAK_EUNSUPPORTED, "N=%lld: a host group of %d work-groups does not fit one XCD of this device",
                   (long long)N, tn);
-    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn));
-    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows);
+    if ((st = tiled_segments(M, K, N, ws, ws_bytes, &t))) return st;
+    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn), 2,
+                                     t.k_segs);
+    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows, t.k_segs);
     t.hbm_n1 = plan.n1;
     t.hbm_rb2 = plan.rb2;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);

@@ -344,8 +344,20 @@ int f8_host_cus(int64_t N, int rb) {
 }  // namespace
 }  // namespace dak
 
+extern "C" uint64_t dak_splitk_gemm_fp8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  using namespace dak;
+  if (M < 1 || K < 1 || N <= kF8MaxN || N > kTiledMaxN) return 0;   // only the tiled kernel splits K
+  const int segs = tiled_k_segs(K, tiled_k_seg_len(M, N, K));
+  return segs > 1 ? (uint64_t)segs * N * M * 4 : 0;
+}
+
 extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
                                           const dak_launch_cfg* cfg, void* stream) {
+  return dak_splitk_gemm_fp8_ws(A, x, N, y, nullptr, 0, cfg, stream);
+}
+
+extern "C" dak_status dak_splitk_gemm_fp8_ws(const dak_split_matrix_fp8* A, const void* x, int64_t N, float* y,
+                                             void* ws, uint64_t ws_bytes, const dak_launch_cfg* cfg, void* stream) {
   using namespace dak;
   clear_error();
   if (!A) return fail(DAK_EINVAL, "A is NULL");
@@ -397,8 +409,10 @@ extern "C" dak_status dak_splitk_gemm_fp8(const dak_split_matrix_fp8* A, const v
     if (tiled_max_host_groups(N, t.cus) < 1)
       return fail(DAK_EUNSUPPORTED, "N=%lld: a host group of %d work-groups does not fit one XCD of this device",
                   (long long)N, tn);
-    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn), 1);
-    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows);
+    if ((st = tiled_segments(M, K, N, ws, ws_bytes, &t))) return st;
+    t.n_groups = tiled_choose_groups(t.cus, tn, host_rows, M - host_rows, K, std::max(1, lc.host_cus / tn), 1,
+                                     t.k_segs);
+    const TiledHbmPlan plan = tiled_choose_plan(t.cus, tn, t.n_groups, M - host_rows, t.k_segs);
     t.hbm_n1 = plan.n1;
     t.hbm_rb2 = plan.rb2;
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);

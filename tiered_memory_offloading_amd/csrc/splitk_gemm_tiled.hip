@@ -188,7 +188,8 @@ __device__ __forceinline__ void tile_step(const unsigned char* sa, const unsigne
 }
 
 // Write a finished tile (wave rows 16 RB wm .. +16 RB): rows below P,
-// columns below N.  F8: each sum times its row's scale (y row yrow0 + row).
+// columns below N.  F8 with `scale`: each sum times its row's scale (y row
+// yrow0 + row); a K segment's partial sums are stored unscaled.
 template <int RB, bool F8 = false>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[RB][4], int64_t P, int64_t row0, int64_t N,
                                            int64_t col0, int64_t M, int64_t yrow0, float* __restrict__ y, int wm,
@@ -199,7 +200,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[RB][4], int64_t 
     const int64_t row = row0 + wm * 16 * RB + rb2 * 16 + r4;
     f32x4_t sc = {1.f, 1.f, 1.f, 1.f};
     if constexpr (F8)
-      if (row < P) sc = *reinterpret_cast<const f32x4_t*>(scale + yrow0 + row);   // P is a multiple of 16
+      if (scale && row < P) sc = *reinterpret_cast<const f32x4_t*>(scale + yrow0 + row);   // P: a multiple of 16
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int64_t n = col0 + wn * 64 + cb * 16 + i16;
@@ -334,12 +335,14 @@ __device__ __forceinline__ void hbm_issue8(const HbmDma8& d, int64_t s, int64_t 
 // same ceil(K / 32) MFMAs as in the host role.  RAGGED: K is not a multiple
 // of 64.
 // F8: `a` holds e4m3 codes (K bytes per row), the slot's A part 64 bytes per
-// row, and the tile is stored times the rows' scales.
+// row, and the tile is stored times the rows' scales (when `scale` is given).
+// Only k in [k0, k1) is summed: k0 a multiple of 256, k1 = K or a multiple of
+// 256 (a K segment; [0, K) unsplit).
 template <bool F8, bool COUNT, bool RAGGED, int RB>
 __device__ __forceinline__ void tile(const void* __restrict__ a, int64_t P, int64_t row0,
-                                     const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t M,
-                                     int64_t yrow0, float* __restrict__ y, const float* __restrict__ scale,
-                                     unsigned char* lds, uint64_t& nbytes) {
+                                     const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K, int64_t k0,
+                                     int64_t k1, int64_t M, int64_t yrow0, float* __restrict__ y,
+                                     const float* __restrict__ scale, unsigned char* lds, uint64_t& nbytes) {
   constexpr int kSlotA = F8 ? kHbmSlotA8 : kHbmSlotA;   // A part of a slot; then x rows
   constexpr int kSlot = kSlotA + kHbmSlotA;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -351,7 +354,7 @@ __device__ __forceinline__ void tile(const void* __restrict__ a, int64_t P, int6
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t T = (K + 63) >> 6;
+  const int64_t T0 = k0 >> 6, T = (k1 + 63) >> 6;   // 64-k steps [T0, T)
   const HbmDma d = hbm_dma(static_cast<const uint16_t*>(a), P, row0, 32 * RB, x, N, col0, K, wave, lane);
   HbmDma8 d8;
   if constexpr (F8) d8 = hbm_dma8(static_cast<const unsigned char*>(a), P, row0, 32 * RB, K, wave, lane);
@@ -361,11 +364,11 @@ __device__ __forceinline__ void tile(const void* __restrict__ a, int64_t P, int6
     else
       hbm_issue<COUNT, RAGGED>(d, s, K, slot, wave, nbytes);
   };
-  issue(0, lds + half);
-  for (int64_t s = 0; s < T; ++s) {
+  issue(T0, lds + half);
+  for (int64_t s = T0; s < T; ++s) {
     vm_wait<0>();
     __builtin_amdgcn_s_barrier();
-    const int slot = (int)(s & 1);
+    const int slot = (int)((s - T0) & 1);
     if (s + 1 < T) issue(s + 1, lds + (slot ^ 1) * kSlot + half);
     const unsigned char* sa = lds + slot * kSlot;
     const unsigned char* sx = sa + kSlotA;
@@ -440,11 +443,13 @@ __device__ __forceinline__ void host_a_issue8(const unsigned char* __restrict__ 
 // The tile of `tile` for host rows: A through two super-slots (one super-step
 // in flight while the other is consumed), x through kHostSX one-step slots.
 // F8: A holds e4m3 codes, super-steps of 8 k-steps, stored times the scales.
+// Only k in [k0, k1) is summed, as in `tile` (k0 a multiple of 256, so a
+// segment starts on a super-step).
 template <bool F8, bool COUNT, bool RAGGED>
 __device__ __forceinline__ void tile_host(const void* __restrict__ a, int64_t P, int64_t row0,
                                           const uint16_t* __restrict__ x, int64_t N, int64_t col0, int64_t K,
-                                          int64_t M, float* __restrict__ y, const float* __restrict__ scale,
-                                          unsigned char* lds, uint64_t& nbytes) {
+                                          int64_t k0, int64_t k1, int64_t M, float* __restrict__ y,
+                                          const float* __restrict__ scale, unsigned char* lds, uint64_t& nbytes) {
   constexpr int kSteps = F8 ? 2 * kSuper : kSuper;   // k-steps per super-step
   const uint16_t* const a16 = static_cast<const uint16_t*>(a);
   const unsigned char* const a8 = static_cast<const unsigned char*>(a);
@@ -463,23 +468,24 @@ __device__ __forceinline__ void tile_host(const void* __restrict__ a, int64_t P,
   for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t T = (K + 31) >> 5, TS = (T + kSteps - 1) / kSteps;
+  const int64_t t0 = k0 >> 5, T = (k1 + 31) >> 5;               // 32-k steps [t0, T)
+  const int64_t S0 = t0 / kSteps, TS = (T + kSteps - 1) / kSteps;   // super-steps [S0, TS)
   const TileDma d = tile_dma(a16, P, row0, kBM, x, N, col0, K, wave, lane);   // x waves use it
   unsigned char* const ring_a = lds;
   unsigned char* const ring_x = lds + 2 * kSuperSlot;
   if (is_a) {
-    a_issue(0, ring_a, wave, lane);
+    a_issue(S0, ring_a, wave, lane);
   } else {
 #pragma unroll
-    for (int s = 0; s < kHostSX - 1; ++s)
-      if (s < T) tile_issue<COUNT, RAGGED>(d, s, K, ring_x + s * kSlotA, wave, nbytes);
+    for (int i = 0; i < kHostSX - 1; ++i)
+      if (t0 + i < T) tile_issue<COUNT, RAGGED>(d, t0 + i, K, ring_x + i * kSlotA, wave, nbytes);
   }
   // Step s: A waves wait for super-step s / kSteps at its first step; x waves for
   // step s.  After the barrier (every read of step s - 1 retired), the first
   // step of a super-step refills the other super-slot with the next super-step
   // and every step refills x's slot of step s - 1.
   int rx = 0;
-  for (int64_t s = 0; s < T; ++s) {
+  for (int64_t s = t0; s < T; ++s) {
     const int ss = (int)(s & (kSteps - 1));
     const int64_t S = s / kSteps;
     if (is_a) {
@@ -490,13 +496,13 @@ __device__ __forceinline__ void tile_host(const void* __restrict__ a, int64_t P,
     __builtin_amdgcn_s_barrier();
     if (is_a) {
       if (ss == 0 && S + 1 < TS)
-        a_issue(S + 1, ring_a + ((S + 1) & 1) * kSuperSlot, wave, lane);
+        a_issue(S + 1, ring_a + ((S + 1 - S0) & 1) * kSuperSlot, wave, lane);
     } else {
       if (s + kHostSX - 1 < T)
         tile_issue<COUNT, RAGGED>(d, s + kHostSX - 1, K, ring_x + (rx == 0 ? kHostSX - 1 : rx - 1) * kSlotA, wave,
                                   nbytes);
     }
-    tile_step<RAGGED, true, 8, F8>(ring_a + (S & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
+    tile_step<RAGGED, true, 8, F8>(ring_a + ((S - S0) & 1) * kSuperSlot, ring_x + rx * kSlotA, ss, wm, wn, lane,
                             32 * s + 8 * (lane >> 4) < K, acc);
     rx = rx == kHostSX - 1 ? 0 : rx + 1;
   }
@@ -506,13 +512,17 @@ __device__ __forceinline__ void tile_host(const void* __restrict__ a, int64_t P,
 // HBM rows: hbm_n1 row tiles of 256 rows, then the rest in tiles of 32 RB2
 // rows (tiled_choose_plan).  F8: A holds e4m3 codes and row_scale the rows'
 // scales; else A holds bf16 and row_scale is unused.  RAGGED: K is not a
-// multiple of 64 (the HBM step).
+// multiple of 64 (the HBM step).  K is summed in segs segments of seg_len
+// (tiled_k_seg_len): unsplit (segs = 1) tiles go to y, else each segment's
+// partial tile to ws + seg N M (same layout as y, unscaled), added up later
+// by reduce_segments.  A unit of work is a (row tile, segment, column tile)
+// for the HBM role and a (row block, segment) for a host group.
 template <bool F8, bool COUNT, bool RAGGED, int RB2>
 __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     const void* __restrict__ a_host, const void* __restrict__ a_hbm, int64_t M, int64_t K, int64_t host_rows,
     const uint16_t* __restrict__ x, int64_t N, float* __restrict__ y, const float* __restrict__ row_scale,
-    int n_groups, int cus, int n_xcd, int64_t hbm_n1, unsigned long long* __restrict__ counters,
-    unsigned long long* __restrict__ xcc_masks) {
+    int n_groups, int cus, int n_xcd, int64_t hbm_n1, int64_t seg_len, int segs, float* __restrict__ ws,
+    unsigned long long* __restrict__ counters, unsigned long long* __restrict__ xcc_masks) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   uint64_t nbytes = 0;
   const int tn = (int)((N + kBN - 1) / kBN);
@@ -520,8 +530,11 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   const int64_t P = M - host_rows;
   constexpr int kRows2 = 32 * RB2;
   const int64_t rows2 = P - (int64_t)kBM * hbm_n1;
-  const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks, hbm_n1 * tn);
+  const int64_t per_row = (int64_t)segs * tn;   // units per row tile
+  const TiledWork w = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks * segs, hbm_n1 * per_row);
   const bool host_role = w.host;
+  auto out_of = [&](int seg) { return segs > 1 ? ws + (int64_t)seg * N * M : y; };
+  const float* const scale = segs > 1 ? nullptr : row_scale;
   // Where the schedule's placement assumption can be checked: each host
   // work-group ORs the bit of the XCD it runs on (the hardware's XCC id
   // register) into its group's mask.  One bit per group means the group's
@@ -532,24 +545,31 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
     atomicOr(&xcc_masks[w.first], 1ull << xcc);
   }
   if (host_role) {
-    for (int64_t rb = w.first; rb < w.end; rb += w.stride) {
+    for (int64_t it = w.first; it < w.end; it += w.stride) {
+      const int64_t rb = it / segs;
+      const int seg = (int)(it % segs);
+      const int64_t k0 = seg * seg_len, k1 = k0 + seg_len < K ? k0 + seg_len : K;
       __syncthreads();   // the ring is reused
-      tile_host<F8, COUNT, RAGGED>(a_host, host_rows, rb * kBM, x, N, (int64_t)w.col_tile * kBN, K, M, y, row_scale,
-                                   lds, nbytes);
+      tile_host<F8, COUNT, RAGGED>(a_host, host_rows, rb * kBM, x, N, (int64_t)w.col_tile * kBN, K, k0, k1, M,
+                                   out_of(seg), scale, lds, nbytes);
     }
   } else {
     for (int64_t t = w.first; t < w.end; t += w.stride) {
+      const int seg = (int)(t / tn % segs);
+      const int64_t k0 = seg * seg_len, k1 = k0 + seg_len < K ? k0 + seg_len : K;
       __syncthreads();   // the ring is reused
-      tile<F8, COUNT, RAGGED, kBM / 32>(a_hbm, P, t / tn * kBM, x, N, t % tn * kBN, K, M, host_rows, y, row_scale,
-                                        lds, nbytes);
+      tile<F8, COUNT, RAGGED, kBM / 32>(a_hbm, P, t / per_row * kBM, x, N, t % tn * kBN, K, k0, k1, M, host_rows,
+                                        out_of(seg), scale, lds, nbytes);
     }
     if (rows2 > 0) {
-      const TiledWork w2 = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks,
-                                      (rows2 + kRows2 - 1) / kRows2 * tn, true);
+      const TiledWork w2 = tiled_work(blockIdx.x, cus, n_xcd, n_groups, tn, host_blocks * segs,
+                                      (rows2 + kRows2 - 1) / kRows2 * per_row, true);
       for (int64_t t = w2.first; t < w2.end; t += w2.stride) {
+        const int seg = (int)(t / tn % segs);
+        const int64_t k0 = seg * seg_len, k1 = k0 + seg_len < K ? k0 + seg_len : K;
         __syncthreads();   // the ring is reused
-        tile<F8, COUNT, RAGGED, RB2>(a_hbm, P, kBM * hbm_n1 + t / tn * kRows2, x, N, t % tn * kBN, K, M, host_rows,
-                                     y, row_scale, lds, nbytes);
+        tile<F8, COUNT, RAGGED, RB2>(a_hbm, P, kBM * hbm_n1 + t / per_row * kRows2, x, N, t % tn * kBN, K, k0, k1, M,
+                                     host_rows, out_of(seg), scale, lds, nbytes);
       }
     }
   }
@@ -562,9 +582,58 @@ __global__ __launch_bounds__(kTT) void gemm_tiled_split(
   }
 }
 
+// y = ((ws[0] + ws[1]) + ...) + ws[segs - 1], element by element over the
+// N x M outputs (times the row's scale for F8), 4 outputs per thread (M is a
+// multiple of 16).
+template <bool F8>
+__global__ __launch_bounds__(256) void reduce_segments(const float* __restrict__ ws, int segs, int64_t NM, int64_t M,
+                                                       const float* __restrict__ scale, float* __restrict__ y) {
+  const int64_t n4 = NM / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(ws + 4 * i);
+    for (int sg = 1; sg < segs; ++sg) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ws + sg * NM + 4 * i);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    if constexpr (F8) {
+      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + (4 * i) % M);
+      acc[0] *= sc[0];
+      acc[1] *= sc[1];
+      acc[2] *= sc[2];
+      acc[3] *= sc[3];
+    }
+    *reinterpret_cast<f32x4_t*>(y + 4 * i) = acc;
+  }
+}
+
 }  // namespace
 
 int tiled_max_host_groups(int64_t N, int cus) { return tiled_max_groups(cus, (int)((N + kBN - 1) / kBN)); }
+
+dak_status tiled_segments(int64_t M, int64_t K, int64_t N, void* ws, uint64_t ws_bytes, TiledArgs* t) {
+  t->k_seg = K;
+  t->k_segs = 1;
+  t->ws = nullptr;
+  if (!ws) return DAK_OK;
+  const int64_t len = tiled_k_seg_len(M, N, K);
+  const int segs = tiled_k_segs(K, len);
+  if (segs == 1) return DAK_OK;
+  const uint64_t need = (uint64_t)segs * (uint64_t)N * (uint64_t)M * 4;
+  if (ws_bytes < need)
+    return fail(DAK_EINVAL, "workspace of %llu bytes; M=%lld K=%lld N=%lld needs %llu", (unsigned long long)ws_bytes,
+                (long long)M, (long long)K, (long long)N, (unsigned long long)need);
+  if ((uintptr_t)ws & 15) return fail(DAK_EINVAL, "workspace must be 16-byte aligned");
+  const void* dws = nullptr;
+  const dak_status st = check_tier_ptr(ws, need, Tier::kDevice, "ws", &dws);
+  if (st) return st;
+  t->k_seg = len;
+  t->k_segs = segs;
+  t->ws = static_cast<float*>(const_cast<void*>(dws));
+  return DAK_OK;
+}
 
 template <bool F8, int RB2>
 static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
@@ -572,7 +641,7 @@ static void launch_rb(const TiledArgs& g, bool count, int n_xcd) {
 #define DAK_TILED(C, R)                                                                                          \
   hipLaunchKernelGGL((gemm_tiled_split<F8, C, R, RB2>), dim3((unsigned)g.cus), dim3(kTT), 0, g.stream,           \
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.x, g.N, g.y, g.row_scale, g.n_groups, g.cus, \
-                     n_xcd, g.hbm_n1, g.counters, g.xcc_masks)
+                     n_xcd, g.hbm_n1, g.k_seg, g.k_segs, g.ws, g.counters, g.xcc_masks)
   if (count) {
     if (ragged) DAK_TILED(true, true); else DAK_TILED(true, false);
   } else {
@@ -600,6 +669,16 @@ void launch_gemm_tiled(const TiledArgs& g, bool count) {
     launch_height<true>(g, count, n_xcd);
   else
     launch_height<false>(g, count, n_xcd);
+  if (g.k_segs > 1) {
+    const int64_t n4 = g.N * g.M / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4 * (int64_t)g.cus);
+    if (g.f8)
+      hipLaunchKernelGGL(reduce_segments<true>, dim3(blocks), dim3(256), 0, g.stream, g.ws, g.k_segs, g.N * g.M, g.M,
+                         g.row_scale, g.y);
+    else
+      hipLaunchKernelGGL(reduce_segments<false>, dim3(blocks), dim3(256), 0, g.stream, g.ws, g.k_segs, g.N * g.M,
+                         g.M, g.row_scale, g.y);
+  }
 }
 
 }  // namespace dak

@@ -125,13 +125,15 @@ constexpr int64_t tiled_plan_tiles2(int64_t hbm_rows, const TiledHbmPlan& p) {
   return rest > 0 ? (rest + 32 * p.rb2 - 1) / (32 * p.rb2) : 0;
 }
 
-// Modelled duration of a plan, in units of kTiledRbFixed-offset tile rows:
-// the slowest HBM work-group over all XCDs.  Within an XCD of w HBM
-// work-groups the first s1 % w of them take one first-phase tile more, and
-// the last s2 % w one second-phase tile more.
-constexpr double tiled_plan_cost(int cus, int tn, int n_groups, int64_t hbm_rows, const TiledHbmPlan& p) {
+// Modelled duration of a plan, in units of kTiledRbFixed-offset tile rows
+// (of one K segment when K is split into `segs`): the slowest HBM work-group
+// over all XCDs.  Within an XCD of w HBM work-groups the first s1 % w of them
+// take one first-phase unit more, and the last s2 % w one second-phase unit
+// more.  A unit is a (row tile, K segment, column tile).
+constexpr double tiled_plan_cost(int cus, int tn, int n_groups, int64_t hbm_rows, const TiledHbmPlan& p,
+                                 int segs = 1) {
   const int n_xcd = tiled_xcds(cus);
-  const int64_t t1 = p.n1 * tn, t2 = tiled_plan_tiles2(hbm_rows, p) * tn;
+  const int64_t t1 = p.n1 * tn * segs, t2 = tiled_plan_tiles2(hbm_rows, p) * tn * segs;
   const double c1 = kTiledRbMax + kTiledRbFixed, c2 = p.rb2 + kTiledRbFixed;
   int64_t total = 0;
   for (int v = 0; v < n_xcd; ++v) total += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
@@ -155,13 +157,13 @@ constexpr double tiled_plan_cost(int cus, int tn, int n_groups, int64_t hbm_rows
 // each height (the tallest first), then first phases of whole rounds of
 // 256-row tiles followed by each second-phase height; a candidate replaces
 // the best only when strictly cheaper.
-constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t hbm_rows) {
+constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t hbm_rows, int segs = 1) {
   TiledHbmPlan best{0, kTiledRbMax};
   if (hbm_rows <= 0) return best;
-  double best_c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, best);
+  double best_c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, best, segs);
   for (int rb = kTiledRbMax - 1; rb >= kTiledRbMin; --rb) {
     const TiledHbmPlan p{0, rb};
-    const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p);
+    const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p, segs);
     if (c < best_c * (1.0 - 1e-9)) {
       best = p;
       best_c = c;
@@ -171,12 +173,12 @@ constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t 
   int64_t wgs = 0;
   for (int v = 0; v < n_xcd; ++v) wgs += tiled_cus_on(v, cus, n_xcd) - (int64_t)tiled_groups_on(v, n_groups, n_xcd) * tn;
   const int64_t all = (hbm_rows + 32 * kTiledRbMax - 1) / (32 * kTiledRbMax);
-  for (int64_t r1 = 1; r1 * wgs / tn < all; ++r1) {
-    const int64_t n1 = r1 * wgs / tn;
+  for (int64_t r1 = 1; r1 * wgs / (tn * segs) < all; ++r1) {
+    const int64_t n1 = r1 * wgs / (tn * segs);
     if (n1 < 1) continue;
     for (int rb = kTiledRbMax; rb >= kTiledRbMin; --rb) {
       const TiledHbmPlan p{n1, rb};
-      const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p);
+      const double c = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p, segs);
       if (c < best_c * (1.0 - 1e-9)) {
         best = p;
         best_c = c;
@@ -193,20 +195,20 @@ constexpr TiledHbmPlan tiled_choose_plan(int cus, int tn, int n_groups, int64_t 
 // modelled duration, a 256-row tile lasting `t_tile`.  elem_bytes: bytes per
 // weight (2 for bf16, 1 for FP8 codes, which feed the same bf16 MFMAs).
 constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_rows, int64_t hbm_rows, int64_t K,
-                                  TiledCost c, int elem_bytes = 2) {
-  const double t_tile = (double)((K + 31) / 32) * c.step_us;
-  const double t_host_tile = (double)((K + 31) / 32) * c.host_step_us;
-  const double block_bytes = 256.0 * (double)K * elem_bytes;
+                                  TiledCost c, int elem_bytes = 2, int segs = 1) {
+  const double t_tile = (double)((K + 31) / 32) * c.step_us / segs;
+  const double t_host_tile = (double)((K + 31) / 32) * c.host_step_us / segs;
+  const double block_bytes = 256.0 * (double)K * elem_bytes / segs;
   double t_host = 0.0;
-  int64_t left = (host_rows + 255) / 256;
+  int64_t left = (host_rows + 255) / 256 * segs;   // host items: (row block, K segment)
   while (left > 0) {
     const int64_t active = left < n_groups ? left : n_groups;
     t_host += tiled_smax(t_host_tile, block_bytes / (c.group_gbps * 1e3),
                          (double)active * block_bytes / (c.link_gbps * 1e3));
     left -= active;
   }
-  const TiledHbmPlan p = tiled_choose_plan(cus, tn, n_groups, hbm_rows);
-  const double t_hbm = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p) / (kTiledRbMax + kTiledRbFixed) * t_tile;
+  const TiledHbmPlan p = tiled_choose_plan(cus, tn, n_groups, hbm_rows, segs);
+  const double t_hbm = tiled_plan_cost(cus, tn, n_groups, hbm_rows, p, segs) / (kTiledRbMax + kTiledRbFixed) * t_tile;
   return tiled_max_d(t_host, t_hbm);
 }
 
@@ -216,21 +218,57 @@ constexpr double tiled_predict_us(int cus, int tn, int n_groups, int64_t host_ro
 // and which measured slower (all-host bf16 rows: 8 groups 4.22 ms, 16-24
 // groups 4.45-4.50 ms); 0 without host rows.
 constexpr int tiled_choose_groups(int cus, int tn, int64_t host_rows, int64_t hbm_rows, int64_t K, int cap,
-                                  int elem_bytes = 2, TiledCost c = kTiledCostMi355x) {
+                                  int elem_bytes = 2, int segs = 1, TiledCost c = kTiledCostMi355x) {
   if (host_rows <= 0) return 0;
-  const int64_t blocks = (host_rows + 255) / 256;
+  const int64_t blocks = (host_rows + 255) / 256 * segs;   // host items
   int hi = tiled_max_groups(cus, tn);
   if (cap < hi) hi = cap;
   if (blocks < hi) hi = (int)blocks;
   if (hi < 1) hi = 1;
-  double fastest = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c, elem_bytes);
+  double fastest = tiled_predict_us(cus, tn, 1, host_rows, hbm_rows, K, c, elem_bytes, segs);
   for (int g = 2; g <= hi; ++g) {
-    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes);
+    const double t = tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes, segs);
     fastest = t < fastest ? t : fastest;
   }
   for (int g = 1; g < hi; ++g)
-    if (tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes) <= fastest * 1.02) return g;
+    if (tiled_predict_us(cus, tn, g, host_rows, hbm_rows, K, c, elem_bytes, segs) <= fastest * 1.02) return g;
   return hi;
 }
+
+// K segments.  A shape whose 256 x 256 output tiles leave most of the CUs of
+// a round idle splits K into s = 2, 4 or 8 segments, whole multiples of 256 k
+// and at least 512 k each.  Each output element is then the sum, in segment
+// order, of one MFMA chain per segment, y = ((P0 + P1) + P2) + ..., the
+// partial sums passing through a workspace that a second kernel adds up.
+// s minimises a model of the whole op with all rows in HBM on the 256 CUs of
+// the reference device: the HBM plan's modelled duration (tiled_plan_cost,
+// units of a segment's tiles of K / (32 s) steps of 0.92 us each, a 256-row
+// tile being 12 units), plus, when split, reading s partial outputs and
+// writing y at 4 TB/s and 5 us for the second launch; a larger s must win by
+// 10 %.  The rule depends on M, N and K only, so the result bits depend on
+// neither the host share nor the device.  Returns the segment length (K when
+// unsplit); the count is ceil(K / length).
+constexpr int kTiledRefCus = 256, kTiledMaxSegs = 8;
+constexpr double tiled_split_us(int64_t M, int64_t N, int64_t K, int segs) {
+  const int tn = (int)((N + 255) / 256);
+  const TiledHbmPlan p = tiled_choose_plan(kTiledRefCus, tn, 0, M, segs);
+  const double t = tiled_plan_cost(kTiledRefCus, tn, 0, M, p, segs) / (kTiledRbMax + kTiledRbFixed) *
+                   (double)((K + 31) / 32) * 0.92 / (double)segs;
+  return segs == 1 ? t : t + (double)(segs + 1) * (double)N * (double)M * 4.0 / 4.0e6 + 5.0;
+}
+constexpr int64_t tiled_k_seg_len(int64_t M, int64_t N, int64_t K) {
+  int best = 1;
+  double best_t = tiled_split_us(M, N, K, 1);
+  for (int s = 2; s <= kTiledMaxSegs && s * 512 <= K; s *= 2) {
+    const double t = tiled_split_us(M, N, K, s);
+    if (t < best_t * 0.9) {
+      best = s;
+      best_t = t;
+    }
+  }
+  if (best == 1) return K;
+  return (K + 256 * best - 1) / (256 * best) * 256;
+}
+constexpr int tiled_k_segs(int64_t K, int64_t seg_len) { return (int)((K + seg_len - 1) / seg_len); }
 
 }  // namespace dak

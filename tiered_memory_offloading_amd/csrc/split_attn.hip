@@ -93,10 +93,12 @@ struct PagedRows {
 // Load one 16-token tile starting at ts.  K in the layout of the score
 // MFMA's A operand: lane l holds token ts + (l & 15), dims 32 j + 8 (l >> 4)
 // .. +7 (kt[j], j = 0..3: four 64-byte pieces of each token's 256-byte row).
-// V in the layout of the P.V products: load i covers tokens ts + 4 i + l / 16,
-// dims 8 (l % 16) .. +7 (1 KiB contiguous per load).  Tokens at or past te, or
-// a tile that does not exist, load zeros and count nothing.
-template <bool COUNT, class Rows>
+// V in the layout of the P.V products: load i covers tokens ts + 4 i + l / 16
+// (VG: ts + 4 (l / 16) + i, the tokens of the lane's scores), dims
+// 8 (l % 16) .. +7 (whole 256-byte rows; 1 KiB contiguous per load without
+// VG).  Tokens at or past te, or a tile that does not exist, load zeros and
+// count nothing.
+template <bool COUNT, bool VG, class Rows>
 __device__ __forceinline__ void load_tile(const Rows& rows, int64_t ts, int64_t te, bool exists, int lane,
                                           uint4 (&kt)[4], uint4 (&vv)[4], uint64_t& nbytes) {
   const int n = lane & 15, g = lane >> 4;
@@ -110,7 +112,7 @@ __device__ __forceinline__ void load_tile(const Rows& rows, int64_t ts, int64_t 
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = ts + 4 * i + g;
+    const int64_t t = VG ? ts + 4 * g + i : ts + 4 * i + g;
     const bool ok = exists && (t < te);
     const int64_t r = rows.off(ts, t) + 8 * n;
     vv[i] = ok ? ld16(rows.v + r) : make_uint4(0, 0, 0, 0);
@@ -212,38 +214,118 @@ __device__ __forceinline__ void attn_tile(const uint4 (&kt)[4], const uint4 (&vv
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Eight grouped heads take P.V on the matrix cores (attn_tile_pv); fewer
+// heads, whose rows would leave most of a 16-row operand empty, the fp32 path
+// (attn_tile).
+template <int G>
+inline constexpr bool kPvOnMatrixCores = G == 8;
+
+// Operands of v_mfma_f32_16x16x16_bf16: four bf16 per lane.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Fold one tile with P.V on the matrix cores (eight grouped heads).  The
+// scores' MFMA leaves lane l with head l & 15 at tokens 4 (l >> 4) .. +3, which
+// is exactly the A operand of v_mfma_f32_16x16x16_bf16 with rows = heads and
+// k = tokens; V (loaded with VG) gives the B operand of column block c: lane l
+// takes output dim 8 (l & 15) + c of its four tokens, element c of each of
+// its four 16-byte V pieces.  Eight such MFMAs (c = 0..7) cover the 128 dims:
+// oa[c] holds o[head 4 (l >> 4) + r][dim 8 (l & 15) + c], r = 0..3, of which
+// lane groups 0 and 1 hold the real heads.  p is rounded once to bf16, and l
+// is a ninth MFMA of the same p against a B of ones (la[r] = l[head
+// 4 (l >> 4) + r]), so o is exactly c l whenever every V row is a power of
+// two c, as on the fp32 path.  A grown running max rescales oa and la by the
+// factors of heads 4 (l >> 4) + r, fetched from lanes 4 (l >> 4) + r.
+template <int G>
+__device__ __forceinline__ void attn_tile_pv(const uint4 (&kt)[4], const uint4 (&vv)[4], int64_t ts, int64_t te,
+                                             int lane, const bf16x8_t (&qf)[4], float qscale, float& m_lane,
+                                             f32x4_t& la, f32x4_t (&oa)[8]) {
+  const int hl = lane & 15, grp = lane >> 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt[j]), qf[j], acc, 0, 0, 0);
+  float sc[4];
+  if (ts + kTile <= te) {   // uniform: every token of the tile is valid
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = acc[r] * qscale;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (ts + 4 * grp + r < te) ? acc[r] * qscale : kNegInf;
+  }
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m_lane, mt);
+  const float ms = (mn == kNegInf) ? 0.f : mn;
+  if (__any(hl < G && mn > m_lane)) {   // uniform: some real head's running max grew
+    const float al = exp2_fast(m_lane - ms);
+    float a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = __shfl(al, 4 * grp + r, 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) la[r] = la[r] * a[r];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oa[c][r] = oa[c][r] * a[r];
+  }
+  m_lane = mn;
+  bf16x4_t pb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pb[r] = (__bf16)(hl < G ? exp2_fast(sc[r] - ms) : 0.f);
+  const short4_t pa = __builtin_bit_cast(short4_t, pb);
+  const short4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};   // bf16 1.0
+  la = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, la, 0, 0, 0);
+  const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w}, w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+  const uint32_t w2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w}, w3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int w = c >> 1;
+    uint32_t b01, b23;
+    if (c & 1) {
+      b01 = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
+      b23 = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
+    } else {
+      b01 = (w0[w] & 0xffffu) | (w1[w] << 16);
+      b23 = (w2[w] & 0xffffu) | (w3[w] << 16);
+    }
+    const short4_t vb = __builtin_bit_cast(short4_t, make_uint2(b01, b23));
+    oa[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, oa[c], 0, 0, 0);
+  }
+}
+
 // Walk tokens [tb, te) of one (b, g) in 16-token tiles, updating the wave's
 // online-softmax state (qf: the Q^T fragments of the group's G heads).
 //   U > 0: groups of U tiles, each group loaded and then folded in;
 //   U < 0: software-pipelined by one tile: tile j + 1's loads are issued
 //          before tile j is folded in, so a wave always has a tile in flight.
 // The tiles are folded in the same order either way (the same bits).
-template <int G, int U, bool COUNT, class Rows>
-__device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_t te, const bf16x8_t (&qf)[4],
-                                            float qscale, float& m_lane, float (&l)[G], float (&o)[G][8], int lane,
-                                            float* pb, uint64_t& nbytes) {
+// fold(kt, vv, ts) folds the tile that starts at ts; VG: the V layout of
+// attn_tile_pv.
+template <int U, bool COUNT, bool VG, class Rows, class Fold>
+__device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_t te, int lane, uint64_t& nbytes,
+                                            Fold&& fold) {
   const int64_t ntiles = te > tb ? (te - tb + kTile - 1) / kTile : 0;
   if constexpr (U < 0) {
     uint4 ka[4], va[4], kb[4], vb[4];
-    load_tile<COUNT>(rows, tb, te, ntiles > 0, lane, ka, va, nbytes);
+    load_tile<COUNT, VG>(rows, tb, te, ntiles > 0, lane, ka, va, nbytes);
     for (int64_t j = 0; j < ntiles; j += 2) {
       const int64_t ts = tb + j * kTile;
-      load_tile<COUNT>(rows, ts + kTile, te, j + 1 < ntiles, lane, kb, vb, nbytes);
-      attn_tile<G>(ka, va, ts, te, lane, qf, qscale, m_lane, l, o, pb);
+      load_tile<COUNT, VG>(rows, ts + kTile, te, j + 1 < ntiles, lane, kb, vb, nbytes);
+      fold(ka, va, ts);
       if (j + 1 >= ntiles) break;   // uniform
-      load_tile<COUNT>(rows, ts + 2 * kTile, te, j + 2 < ntiles, lane, ka, va, nbytes);
-      attn_tile<G>(kb, vb, ts + kTile, te, lane, qf, qscale, m_lane, l, o, pb);
+      load_tile<COUNT, VG>(rows, ts + 2 * kTile, te, j + 2 < ntiles, lane, ka, va, nbytes);
+      fold(kb, vb, ts + kTile);
     }
   } else {
     for (int64_t t0 = 0; t0 < ntiles; t0 += U) {
       uint4 kv[U][4], vv[U][4];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        load_tile<COUNT>(rows, tb + (t0 + u) * kTile, te, t0 + u < ntiles, lane, kv[u], vv[u], nbytes);
+        load_tile<COUNT, VG>(rows, tb + (t0 + u) * kTile, te, t0 + u < ntiles, lane, kv[u], vv[u], nbytes);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (t0 + u < ntiles)
-          attn_tile<G>(kv[u], vv[u], tb + (t0 + u) * kTile, te, lane, qf, qscale, m_lane, l, o, pb);
+        if (t0 + u < ntiles) fold(kv[u], vv[u], tb + (t0 + u) * kTile);
     }
   }
 }
@@ -276,30 +358,57 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
-  // The wave's probability buffer: its own region of red_o, which it writes
-  // only after the walk (16 G + G floats <= G kD).
-  float* pb = red_o + wave * G * kD;
   const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
   const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
-  if (!poison) attn_tokens<G, U, COUNT>(rows, tb, te, qf, qscale, m_lane, l, o, lane, pb, nbytes);
-
-  // Every head's running max, from the lane that holds it (lane h, h < G).
   float m[G];
+  if constexpr (kPvOnMatrixCores<G>) {
+    f32x4_t la = {0.f, 0.f, 0.f, 0.f}, oa[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) m[h] = __shfl(m_lane, h, 64);
-  // Merge the four lane groups (xor 16, then xor 32); they share each head's
-  // max, so the merge's factors are exp2(0) = 1.
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    float m2[G], l2[G], o2[G][8];
+    for (int cb = 0; cb < 8; ++cb) oa[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (!poison)
+      attn_tokens<U, COUNT, true>(rows, tb, te, lane, nbytes, [&](const uint4(&kt)[4], const uint4(&vv)[4], int64_t ts) {
+        attn_tile_pv<G>(kt, vv, ts, te, lane, qf, qscale, m_lane, la, oa);
+      });
+    // Each head's m from lane h, l from lane group h / 4 (every lane of a
+    // group holds the same la), and o into the layout below: lane n < 16
+    // takes heads 0-3 from its own accumulators and heads 4-7 from lane n + 16.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      m2[h] = m[h];
-      l2[h] = __shfl_xor(l[h], off, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o2[h][e] = __shfl_xor(o[h][e], off, 64);
+      m[h] = __shfl(m_lane, h, 64);
+      l[h] = __shfl(la[h & 3], 16 * (h >> 2), 64);
     }
-    merge_state<G>(m, l, o, m2, l2, o2);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < G) o[r][cb] = oa[cb][r];
+        if (4 + r < G) o[4 + r][cb] = __shfl_xor(oa[cb][r], 16, 64);
+      }
+  } else {
+    // The wave's probability buffer: its own region of red_o, which it writes
+    // only after the walk (16 G + G floats <= G kD).
+    float* pb = red_o + wave * G * kD;
+    if (!poison)
+      attn_tokens<U, COUNT, false>(rows, tb, te, lane, nbytes, [&](const uint4(&kt)[4], const uint4(&vv)[4], int64_t ts) {
+        attn_tile<G>(kt, vv, ts, te, lane, qf, qscale, m_lane, l, o, pb);
+      });
+    // Every head's running max, from the lane that holds it (lane h, h < G).
+#pragma unroll
+    for (int h = 0; h < G; ++h) m[h] = __shfl(m_lane, h, 64);
+    // Merge the four lane groups (xor 16, then xor 32); they share each head's
+    // max, so the merge's factors are exp2(0) = 1.
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      float m2[G], l2[G], o2[G][8];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m2[h] = m[h];
+        l2[h] = __shfl_xor(l[h], off, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o2[h][e] = __shfl_xor(o[h][e], off, 64);
+      }
+      merge_state<G>(m, l, o, m2, l2, o2);
+    }
   }
   __syncthreads();   // every wave's walk, and so its use of the probability buffer, is done
   // Lanes 0..15 hold the wave's state for dims 8*lane .. +7.

@@ -52,24 +52,27 @@ namespace {
 
 constexpr int kF8Waves = 4;
 constexpr int kF8Threads = 64 * kF8Waves;
-constexpr int kF8KC = 256;             // k per chunk
-constexpr int kF8ARow = kF8KC;         // bytes per staged A row
-constexpr int kF8XRow = kF8KC * 2;     // bytes per staged x row
-constexpr int kF8Steps = kF8KC / 32;   // MFMA steps per chunk
+constexpr int kF8KC = 256;             // k per chunk (the default; 128 for wide items without host rows)
+constexpr int kF8ARow = kF8KC;         // bytes per staged A row of a 256-k chunk
 constexpr int64_t kF8MaxN = 64;
 
 // XR: activation rows staged per chunk when NB = 1 (2, 4, 8 or 16); NB > 1
-// stages all 16 NB rows.
-template <int NB, int RB, int XR = 16>
+// stages all 16 NB rows.  KC: k per chunk, 256 or 128; a staged A row holds
+// KC codes, an x row KC bf16 values.
+template <int NB, int RB, int XR = 16, int KC = kF8KC>
 struct F8Shape {
   static_assert(NB == 1 || XR == 16, "partial activation blocks only for one column block");
   static_assert(XR == 2 || XR == 4 || XR == 8 || XR == 16, "XR is a power of two");
+  static_assert(KC == 256 || KC == 128, "chunks of 256 or 128 k");
+  static constexpr int ROW_A = KC;                   // bytes per staged A row
+  static constexpr int ROW_X = 2 * KC;               // bytes per staged x row
+  static constexpr int STEPS = KC / 32;              // MFMA steps per chunk
   static constexpr int R = 16 * RB;                  // A rows per item
   static constexpr int XROWS = NB == 1 ? XR : 16 * NB;
-  static constexpr int A_BYTES = R * kF8ARow;
-  static constexpr int X_BYTES = XROWS * kF8XRow;
+  static constexpr int A_BYTES = R * ROW_A;
+  static constexpr int X_BYTES = XROWS * ROW_X;
   static constexpr int SLOT = A_BYTES + X_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024;     // 4 A rows per instruction
+  static constexpr int A_INSTR = A_BYTES / 1024;     // 1024 / ROW_A A rows per instruction
   static constexpr int INSTR = SLOT / 1024;
   // Wave w issues instructions w, w + 4, ...: LO or LO + 1 of them per chunk.
   static constexpr int LO = INSTR / kF8Waves;
@@ -78,9 +81,13 @@ struct F8Shape {
   static constexpr int P = kF8Waves / RB;            // k-phases
   static_assert(MAX_PER_WAVE * 2 <= 63, "vmcnt range");
   static_assert(kF8Waves * NB * 64 * 16 <= SLOT, "the phase partials fit in one slot");
+  // 16-byte piece p of staged A row r sits at position p ^ swz_a(r): with
+  // 256-byte rows p ^ (r & 15); with 128-byte rows p ^ ((r >> 1) & 7), so the
+  // 16 rows of a fragment read (8 codes per lane) fall on distinct bank groups.
+  static __device__ __forceinline__ int swz_a(int r) { return KC == 256 ? (r & 15) : ((r >> 1) & 7); }
 };
 
-constexpr int f8_slot_bytes(int nb, int rb, int xr) { return 16 * rb * kF8ARow + (nb == 1 ? xr : 16 * nb) * kF8XRow; }
+constexpr int f8_slot_bytes(int nb, int rb, int xr) { return 16 * rb * kF8ARow + (nb == 1 ? xr : 16 * nb) * 2 * kF8KC; }
 
 // Ring depth: three slots when they fit in half of the CU's LDS, else two.
 constexpr int f8_stages(int nb, int rb, int xr = 16) { return 3 * f8_slot_bytes(nb, rb, xr) <= (80 << 10) ? 3 : 2; }
@@ -94,9 +101,9 @@ __device__ __forceinline__ void f8_wait_later(int64_t later) {
   else vm_wait<0>();
 }
 
-template <int NB, int RB, int XR, bool COUNT>
+template <int NB, int RB, int XR, bool COUNT, int KC = kF8KC>
 struct F8Item {
-  using S = F8Shape<NB, RB, XR>;
+  using S = F8Shape<NB, RB, XR, KC>;
 
   // DMA chunk c of the item whose first A row is `a` into `slot`.  Pieces past
   // K and activation rows past N are fetched from an in-bounds address and
@@ -110,15 +117,17 @@ struct F8Item {
       if (ins >= S::INSTR) break;   // uniform
       const void* src;
       if (ins < S::A_INSTR) {   // uniform
-        const int r = 4 * ins + (lane >> 4);
-        const int piece = (lane & 15) ^ (r & 15);
-        const int64_t k = c * kF8KC + piece * 16;
+        constexpr int LPR = S::ROW_A / 16;   // lanes per A row
+        const int r = (64 / LPR) * ins + lane / LPR;
+        const int piece = (lane % LPR) ^ S::swz_a(r);
+        const int64_t k = c * KC + piece * 16;
         src = a + (int64_t)r * K + (k < K ? k : 0);
         if (COUNT && k < K) nbytes += 16;
       } else {
-        const int xr = 2 * (ins - S::A_INSTR) + (lane >> 5);
-        const int piece = (lane & 31) ^ (xr & 15);
-        const int64_t k = c * kF8KC + piece * 8;
+        constexpr int LPR = S::ROW_X / 16;   // lanes per x row
+        const int xr = (64 / LPR) * (ins - S::A_INSTR) + lane / LPR;
+        const int piece = (lane % LPR) ^ (xr & 15);
+        const int64_t k = c * KC + piece * 8;
         src = x + (xr < N ? xr : 0) * K + (k < K ? k : 0);
       }
       dma16(src, slot + ins * 1024);
@@ -131,19 +140,19 @@ struct F8Item {
     const int i16 = lane & 15, g = lane >> 4;
     const int ra = 16 * rb + i16;
 #pragma unroll
-    for (int t = 0; t < kF8Steps; ++t) {
+    for (int t = 0; t < S::STEPS; ++t) {
       if (t % S::P != phase) continue;   // uniform
       // K is a multiple of 16, so a lane's 8 k values are all in or all out.
-      const bool kok = c * kF8KC + 32 * t + 8 * g < K;
+      const bool kok = c * KC + 32 * t + 8 * g < K;
       const int pa = 2 * t + (g >> 1);
-      uint2 a8 = *reinterpret_cast<const uint2*>(slot + ra * kF8ARow + ((pa ^ (ra & 15)) << 4) + 8 * (g & 1));
+      uint2 a8 = *reinterpret_cast<const uint2*>(slot + ra * S::ROW_A + ((pa ^ S::swz_a(ra)) << 4) + 8 * (g & 1));
       if (!kok) a8 = make_uint2(0, 0);
       const uint4 af = e4m3x8_to_bf16(a8);
       const int px = 4 * t + g;
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         const int xr = NB == 1 ? (i16 & (XR - 1)) : 16 * cb + i16;   // staged row of column 16 cb + i16
-        uint4 xf = *reinterpret_cast<const uint4*>(slot + S::A_BYTES + xr * kF8XRow + ((px ^ (xr & 15)) << 4));
+        uint4 xf = *reinterpret_cast<const uint4*>(slot + S::A_BYTES + xr * S::ROW_X + ((px ^ (xr & 15)) << 4));
         if (!kok) xf = make_uint4(0, 0, 0, 0);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(xf), acc[cb], 0, 0, 0);
       }
@@ -151,22 +160,22 @@ struct F8Item {
   }
 };
 
-template <int NB, int RB, int XR, int STAGES, bool COUNT>
+template <int NB, int RB, int XR, int STAGES, bool COUNT, int KC = kF8KC>
 __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
     const unsigned char* __restrict__ a_host, const unsigned char* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const unsigned char* __restrict__ a_stage, int64_t stage_rows,
     const float* __restrict__ row_scale, const uint16_t* __restrict__ x, int64_t N,
     float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
     unsigned long long* __restrict__ counters) {
-  using S = F8Shape<NB, RB, XR>;
-  using I = F8Item<NB, RB, XR, COUNT>;
+  using S = F8Shape<NB, RB, XR, KC>;
+  using I = F8Item<NB, RB, XR, COUNT, KC>;
   __shared__ __attribute__((aligned(16))) unsigned char s0[S::SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char s1[S::SLOT];
   __shared__ __attribute__((aligned(16))) unsigned char s2[STAGES > 2 ? S::SLOT : 16];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rb = wave % RB, phase = wave / RB;
-  const int64_t nch = (K + kF8KC - 1) / kF8KC;
+  const int64_t nch = (K + KC - 1) / KC;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
   int64_t it = host_role ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - host_wgs;
@@ -270,11 +279,11 @@ struct F8Args {
   hipStream_t stream;
 };
 
-template <int NB, int RB, int XR, int ST, bool COUNT>
+template <int NB, int RB, int XR, int ST, bool COUNT, int KC = kF8KC>
 void launch_f8_nb_rb_st(const F8Args& g) {
-  static_assert(ST * F8Shape<NB, RB, XR>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
+  static_assert(ST * F8Shape<NB, RB, XR, KC>::SLOT <= (160 << 10), "ring exceeds the CU's LDS");
   const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_fp8_split<NB, RB, XR, ST, COUNT>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
+  hipLaunchKernelGGL((gemm_fp8_split<NB, RB, XR, ST, COUNT, KC>), dim3((unsigned)grid), dim3(kF8Threads), 0, g.stream,
                      g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.row_scale, g.x, g.N, g.y,
                      g.host_wgs, g.host_items, g.hbm_items, g.counters);
 }
@@ -288,6 +297,15 @@ void launch_f8_nb_rb_st(const F8Args& g) {
 // to launches with a host role).  The depth changes no arithmetic.
 template <int NB, int RB, int XR, bool COUNT>
 void launch_f8_nb_rb(const F8Args& g) {
+  // 64-row items at N > 32 without host rows: chunks of 128 k, two slots of
+  // 24 KiB, three work-groups per CU.  The work-groups of a CU then walk the
+  // same chunk of the activations at about the same time and share its lines
+  // in the CU's L1, where a 256-k chunk holds 32 KiB of activations for each
+  // 16 KiB of weights.  The chunk length changes no arithmetic (one MFMA
+  // chain per output over the 32-k steps in order, RB = 4 having one phase).
+  if constexpr (NB == 4 && RB == 4) {
+    if (g.host_wgs == 0) return launch_f8_nb_rb_st<NB, RB, XR, 2, COUNT, 128>(g);
+  }
   constexpr int ST = f8_stages(NB, RB, XR);
   if constexpr (ST == 2 && 3 * F8Shape<NB, RB, XR>::SLOT <= (160 << 10)) {
     const uint64_t host_inflight = (uint64_t)g.host_wgs * 2 * 16 * RB * kF8ARow;

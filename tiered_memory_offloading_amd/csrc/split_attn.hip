@@ -98,26 +98,42 @@ struct PagedRows {
 // 8 (l % 16) .. +7 (whole 256-byte rows; 1 KiB contiguous per load without
 // VG).  Tokens at or past te, or a tile that does not exist, load zeros and
 // count nothing.
+//
+// The loads go through buffer resources whose range is the tile's valid rows
+// (ts, te and exists are uniform over the wave, and a tile never straddles a
+// page, so its rows are one contiguous run): a lane past the range reads zeros
+// without touching memory.  No load sits behind a per-lane branch, so the
+// compiler keeps the next tile's loads in flight while a tile is folded in.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16_rsrc(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 template <bool COUNT, bool VG, class Rows>
 __device__ __forceinline__ void load_tile(const Rows& rows, int64_t ts, int64_t te, bool exists, int lane,
                                           uint4 (&kt)[4], uint4 (&vv)[4], uint64_t& nbytes) {
   const int n = lane & 15, g = lane >> 4;
-  {
-    const int64_t t = ts + n;
-    const bool ok = exists && (t < te);
-    const int64_t r = rows.off(ts, t) + 8 * g;
+  const int64_t nv = te - ts < kTile ? te - ts : kTile;
+  const int valid = exists && nv > 0 ? (int)nv : 0;   // uniform
+  const int64_t r0 = rows.off(ts, ts);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(rows.k + r0, valid * kD * 2);
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(rows.v + r0, valid * kD * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kt[j] = ok ? ld16(rows.k + r + 32 * j) : make_uint4(0, 0, 0, 0);
-    if (COUNT && ok) nbytes += 64;
-  }
+  for (int j = 0; j < 4; ++j) kt[j] = ld16_rsrc(rk, (n * kD + 8 * g + 32 * j) * 2);
+  if (COUNT && n < valid) nbytes += 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = VG ? ts + 4 * g + i : ts + 4 * i + g;
-    const bool ok = exists && (t < te);
-    const int64_t r = rows.off(ts, t) + 8 * n;
-    vv[i] = ok ? ld16(rows.v + r) : make_uint4(0, 0, 0, 0);
-    if (COUNT && ok) nbytes += 16;
+    const int t = VG ? 4 * g + i : 4 * i + g;
+    vv[i] = ld16_rsrc(rv, (t * kD + 8 * n) * 2);
+    if (COUNT && t < valid) nbytes += 16;
   }
+  // All eight loads leave before anything that uses them: left to itself the
+  // scheduler starts the score products on the first K pieces and reuses their
+  // registers for the last V loads, which then wait a whole round trip (over
+  // the host link, microseconds).
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fold one loaded tile into the wave's online-softmax state.
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
     unsigned long long* __restrict__ counters) {
   __shared__ float red_o[kAttnWaves * G * kD];
   __shared__ float red_ml[kAttnWaves * G * 2];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
   if (host_role) {
@@ -577,7 +593,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_paged(
   __shared__ float red_o[kAttnWaves * G * kD];
   __shared__ float red_ml[kAttnWaves * G * 2];
   __shared__ int bad_w[kAttnWaves];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint64_t nbytes = 0;
   const bool host_role = (int)blockIdx.x < host_wgs;
   if (host_role) {

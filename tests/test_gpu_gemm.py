@@ -213,6 +213,36 @@ def test_llama70b_linears_full_size(name, M, K):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("M,K,N,hs", [(10240, 8192, 16, (1, 2, 4)), (8192, 28672, 16, (1, 2)),
+                                      (28672, 4096, 64, (1, 3)), (4096, 14336, 64, (1,))])
+def test_small_host_shares_on_a_host_xcd(M, K, N, hs):
+    # DAK paper §4.1's disjoint CU groups: a host share whose bytes take at most
+    # three times the HBM part at the two tiers' rates runs its host
+    # work-groups on an XCD of their own (the 70B-shaped QKV and down at
+    # N = 16, the Llama-8B gate+up and down at N = 64).  Where they run
+    # changes no bit, and every weight byte is read once from its tier.
+    A, X = synth.gemm_inputs(M, K, N, seed=6, device="cuda")
+    g = torch.Generator().manual_seed(9)
+    rows = torch.randperm(M, generator=g)[:64].tolist() + [0, 63, M - 1]
+    ref = og.gemm_rows(og.to_f64(A[rows]), og.to_f64(X))
+    y0 = run(A, X, 64, 0)
+    assert og.normwise_error(y0[:, rows].numpy(), ref) <= TOL
+    x = X.cuda()
+    for h in hs:
+        host_b = h * 64 * K * 2
+        assert host_b * 110 <= 3 * (M - h * 64) * K * 2   # the share the rule gives a host XCD
+        S = dak.place_matrix(A, 64, h)
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        y = dak.splitk_gemm(S, x, cfg=dak.LaunchConfig(byte_counters=cnt))
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), y0), h
+        assert cnt.tolist() == [host_b, (M - h * 64) * K * 2], (h, cnt.tolist())
+        assert torch.equal(dak.splitk_gemm(S, x).cpu(), y0), h
+        del S
+    del A
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # Wide activations (N > 256): the tiled MFMA kernel of the compute-bound regime
 # ---------------------------------------------------------------------------

@@ -19,3 +19,15 @@ def test_tiled_schedule_covers_every_tile_once(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_split_roles_cover_every_work_group_once(tmp_path):
+    """The split kernels' role layout (csrc/split_roles.hpp), with and without
+    an XCD of the host role's own: every host work-group and every HBM work
+    number exactly once, host work-groups only on XCD 0 when it is reserved."""
+    exe = str(tmp_path / "roles")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", CSRC, os.path.join(HERE, "split_roles_check.cpp"),
+                    "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "split_roles.hpp"
+
 namespace dak {
 
 struct StagedArgs {
@@ -20,6 +22,8 @@ struct StagedArgs {
   int host_wgs;
   int64_t host_items, hbm_items;
   int cus;   // compute units of the device (picks the ring depth at N > 32)
+  int n_xcd;      // XCDs of the device
+  bool host_xcd;  // the host role has XCD 0 to itself (use_host_xcd)
   unsigned long long* counters;
   hipStream_t stream;
 };
@@ -37,5 +41,8 @@ uint64_t staged_host_inflight(int64_t N, int row_blocks);
 // Launch.  The ring depth never changes the arithmetic (a step's k-phase is
 // its index within K), so it may depend on the split: see stages_for_launch.
 void launch_gemm_staged(const StagedArgs& g, int row_blocks, bool count);
+// Work-groups of the launch (with host_xcd, n_xcd per round of which one is a
+// host work-group or idle).
+int64_t staged_grid(const StagedArgs& g);
 
 }  // namespace dak

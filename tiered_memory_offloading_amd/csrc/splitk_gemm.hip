@@ -557,10 +557,12 @@ extern "C" dak_status dak_splitk_gemm_ws(const dak_split_matrix* A, const void* 
     t.hbm_items = (M - t.host_rows) / item_rows;
     t.host_wgs = (int)gemm_host_workgroups(t.host_items, lc, staged_host_inflight(N, rbw));
     if ((st = device_cus(&t.cus))) return st;
+    t.n_xcd = tiled_xcds(t.cus);
+    t.host_xcd = use_host_xcd(t.host_rows * K * 2, (M - t.host_rows) * K * 2, t.host_wgs, t.n_xcd);
     t.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
     t.stream = static_cast<hipStream_t>(stream);
-    if (t.host_wgs + t.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
     if (t.host_wgs + t.hbm_items == 0) return DAK_OK;
+    if (staged_grid(t) > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
     launch_gemm_staged(t, rbw, (lc.flags & DAK_FLAG_COUNT_BYTES) != 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail_hip((int)e, "staged gemm kernel launch");

@@ -137,7 +137,7 @@ template <int NB, int RB, int STAGES, bool COUNT, int KC = kKC>
 __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
     const uint16_t* __restrict__ a_host, const uint16_t* __restrict__ a_hbm, int64_t M, int64_t K,
     int64_t host_rows, const uint16_t* __restrict__ a_stage, int64_t stage_rows, const uint16_t* __restrict__ x,
-    int64_t N, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    int64_t N, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items, int n_xcd,
     unsigned long long* __restrict__ counters) {
   using S = StagedShape<NB, RB, KC>;
   using I = StagedItem<NB, RB, COUNT, KC>;
@@ -149,14 +149,16 @@ __global__ __launch_bounds__(kSThreads) void gemm_staged_split(
   const int rb = wave % RB, phase = wave / RB;
   const int64_t nch = (K + KC - 1) / KC;
   uint64_t nbytes = 0;
-  const bool host_role = (int)blockIdx.x < host_wgs;
+  const SplitRole role = split_role(blockIdx.x, host_wgs, n_xcd);
+  if (role.idle) return;   // uniform: an idle slot on the host XCD
+  const bool host_role = role.host;
+  int64_t it = role.index;
   // Spread DMA instructions over the waves, except in host work-groups of
   // 16-row items.  Measured on the Llama-8B decode linears: gate+up (64-row
   // items) 8 % faster at x = 0 and 2-4 % at x = 0.05-0.25; 16-row host items
   // lost 2-3 % when spread (down at N = 16 and 64), so they keep consecutive
   // instructions.
   const bool spread = !(host_role && RB == 1);
-  int64_t it = host_role ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - host_wgs;
   const int64_t items = host_role ? host_items : hbm_items;
   const int64_t stride = host_role ? host_wgs : items;   // HBM work-groups take one item
   for (; it < items; it += stride) {
@@ -243,6 +245,12 @@ constexpr bool stages_fit() {
          StagedShape<NB, RB>::PER_WAVE * (ST - 2) <= 63;
 }
 
+}  // namespace
+
+int64_t staged_grid(const StagedArgs& g) { return split_grid(g.host_wgs, g.hbm_items, g.host_xcd ? g.n_xcd : 0); }
+
+namespace {
+
 // Without a host role: three slots also where they need the whole CU (N > 32,
 // items of 16 or 32 rows: 120 or 144 KiB), provided the grid then still runs
 // in one round of one work-group per CU (measured at N = 64: 4096-row ops 5-9 %
@@ -250,16 +258,14 @@ constexpr bool stages_fit() {
 // Deeper rings at x = 0 measured no better (the four Llama-8B linears at
 // N = 16: 110-125 us per step for every depth from 2 to 8).
 bool deep_ring(int nb, int rb, const StagedArgs& g) {
-  return stages_for(nb, rb) == 2 && 3 * (16 * rb + 16 * nb) * kRowB <= (160 << 10) &&
-         g.host_wgs + g.hbm_items <= g.cus;
+  return stages_for(nb, rb) == 2 && 3 * (16 * rb + 16 * nb) * kRowB <= (160 << 10) && staged_grid(g) <= g.cus;
 }
 
 template <int NB, int RB, int ST, bool COUNT, int KC = kKC>
 void launch_nb_rb_st(const StagedArgs& g) {
-  const int64_t grid = g.host_wgs + g.hbm_items;
-  hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT, KC>), dim3((unsigned)grid), dim3(kSThreads), 0, g.stream,
-                     g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.N, g.y, g.host_wgs,
-                     g.host_items, g.hbm_items, g.counters);
+  hipLaunchKernelGGL((gemm_staged_split<NB, RB, ST, COUNT, KC>), dim3((unsigned)staged_grid(g)), dim3(kSThreads), 0,
+                     g.stream, g.a_host, g.a_hbm, g.M, g.K, g.host_rows, g.a_stage, g.stage_rows, g.x, g.N, g.y,
+                     g.host_wgs, g.host_items, g.hbm_items, g.host_xcd ? g.n_xcd : 0, g.counters);
 }
 
 // Work-groups of one instance resident per CU at once (LDS and registers),
@@ -296,7 +302,7 @@ bool launch_deepest(const StagedArgs& g) {
     }
     const int occ = staged_occupancy<NB, RB, ST, COUNT>();
     const uint64_t host_inflight = (uint64_t)g.host_wgs * (ST - 1) * 16 * RB * kRowB;
-    if (occ > 0 && g.host_wgs + g.hbm_items <= (int64_t)g.cus * occ && host_inflight <= kHostInflightBytes) {
+    if (occ > 0 && staged_grid(g) <= (int64_t)g.cus * occ && host_inflight <= kHostInflightBytes) {
       launch_nb_rb_st<NB, RB, ST, COUNT>(g);
       return true;
     }

@@ -141,8 +141,9 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  *                  0 = per-operator default from the library's host-role
  *                  sweep on MI355X (the fewest that reach the full link rate;
  *                  tuning_defaults.hpp, generated from the sweep table): split
- *                  GEMM N <= 4 and 64 < N <= 256, and split attention, one
- *                  swept cap each; split GEMM 4 < N <= 64 (bf16 and FP8): the
+ *                  GEMM N <= 4 (and FP8 at N = 1) and 64 < N <= 256, and
+ *                  split attention, one swept cap each; split GEMM
+ *                  4 < N <= 64 (bf16) and 2 <= N <= 64 (FP8): the
  *                  fewest whose staged chunks in flight cover about 256 KiB,
  *                  within the sweep's bounds; N > 256: no cap, the
  *                  launch picks its group count from a time model of the
@@ -156,7 +157,8 @@ int64_t dak_host_workgroups(int64_t items, int32_t cap);
  *                  wave issues before consuming the first; one of 1, 2, 4, 8.
  *                  0 = sized so that all host work-groups together keep about
  *                  256 KiB in flight (the link's bandwidth-delay product).  A
- *                  step is 512 k of the wave's 4 rows (GEMM, N <= 4), a 256-k
+ *                  step is 512 k of the wave's 4 rows (GEMM, N <= 4; FP8 at
+ *                  N = 1: 1024 k), a 256-k
  *                  chunk of its 16 rows (GEMM, 64 < N <= 256, at most 2
  *                  chunks) or 16 tokens of K and V (attention; clamped to what
  *                  registers allow).  The split GEMM for 4 < N <= 64 and for
@@ -299,15 +301,17 @@ typedef struct {
  * and every host byte crosses the link once.
  *   A     the FP8 split matrix
  *   x     bf16 [N, K] in device memory
- *   N     1 .. 2048: decode batches (N <= 64) take the memory-bound kernel;
- *         wider activations (DAK §4.2.1's compute-bound regime, where halving
+ *   N     1 .. 2048: N = 1 takes plain fp32 FMAs (codes widened to fp32
+ *         exactly), 2 <= N <= 64 the memory-bound LDS-ring kernel on the
+ *         matrix cores; wider activations (DAK §4.2.1's compute-bound regime, where halving
  *         the bytes of a tile-row doubles the turning point's host share)
  *         take the tiled kernel of dak_splitk_gemm with FP8 A tiles, the
  *         codes widened to bf16 (exact) before the same bf16 MFMA
  *   y     fp32 [N, M] in device memory; fully written
- *   cfg   nullable launch configuration (the window does not apply: the
- *         kernels stage fixed-depth rings; for N > 64 host_cus caps the host
- *         groups as in dak_splitk_gemm)
+ *   cfg   nullable launch configuration (the window applies at N = 1 as in
+ *         dak_splitk_gemm's FMA path; the other kernels stage fixed-depth
+ *         rings; for N > 64 host_cus caps the host groups as in
+ *         dak_splitk_gemm)
  * Errors: DAK_EINVAL for shapes/pointers outside the above, DAK_EUNSUPPORTED
  * for N > 2048 and for a staged host part (DAK_FLAG_STAGED_HOST) with
  * N > 64.  A NaN code gives NaN in its row. */

@@ -263,6 +263,117 @@ __global__ __launch_bounds__(kF8Threads) void gemm_fp8_split(
   }
 }
 
+// ---------------------------------------------------------------------------
+// FMA path (N = 1)
+// ---------------------------------------------------------------------------
+// A single activation row leaves a matrix core almost idle and the LDS ring's
+// staging costs as much as it saves, so N = 1 takes plain fp32 FMAs, as in the
+// bf16 kernel's path for N <= 4.  A wave owns 4 rows; step s covers k in
+// [1024 s, 1024 s + 1024), lane l the 16 codes at k = 1024 s + 16 l .. +15 of
+// each row (one 1 KiB piece per row and step, contiguous over the lanes).
+// Codes widen to fp32 exactly (v_cvt_scalef32_pk_f32_fp8 with scale 1), the
+// activation from bf16; per lane the order is steps ascending, then the 16
+// elements ascending; the 64 lane partials are added by a fixed xor
+// butterfly, and the row's scale multiplies the finished sum.  Both roles
+// run this sequence.
+constexpr int kF8FmaRW = 4;                       // rows per wave
+constexpr int kF8FmaItemRows = kF8FmaRW * 4;      // four waves
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int U, bool COUNT>
+__device__ __forceinline__ void fma8_rows(const unsigned char* __restrict__ a, int64_t K,
+                                          const uint16_t* __restrict__ x, float (&acc)[kF8FmaRW], int lane,
+                                          uint64_t& nbytes) {
+  const int64_t nsteps = (K + 1023) >> 10;
+  for (int64_t s0 = 0; s0 < nsteps; s0 += U) {
+    uint4 av[U][kF8FmaRW];
+    uint4 xv[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = ((s0 + u) << 10) + lane * 16;
+      const bool ok = (s0 + u < nsteps) && (k < K);   // K is a multiple of 16
+#pragma unroll
+      for (int r = 0; r < kF8FmaRW; ++r)
+        av[u][r] = ok ? *reinterpret_cast<const uint4*>(a + r * K + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) xv[u][j] = ok ? ld16(x + k + 8 * j) : make_uint4(0, 0, 0, 0);
+      if (COUNT && ok) nbytes += 16 * kF8FmaRW;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= nsteps) break;   // uniform: skip steps past the end
+      float xf[16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xf[8 * j + 2 * q] = bf_lo(w[q]);
+          xf[8 * j + 2 * q + 1] = bf_hi(w[q]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kF8FmaRW; ++r) {
+        const uint32_t w[4] = {av[u][r].x, av[u][r].y, av[u][r].z, av[u][r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[q], 1.0f, false);
+          const f32x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[q], 1.0f, true);
+          acc[r] = __builtin_fmaf(c0.x, xf[4 * q], acc[r]);
+          acc[r] = __builtin_fmaf(c0.y, xf[4 * q + 1], acc[r]);
+          acc[r] = __builtin_fmaf(c1.x, xf[4 * q + 2], acc[r]);
+          acc[r] = __builtin_fmaf(c1.y, xf[4 * q + 3], acc[r]);
+        }
+      }
+    }
+  }
+}
+
+// Reduce the lane partials of rows row0 .. row0 + 3 and store their scaled
+// sums y[row0 + r].
+__device__ __forceinline__ void fma8_store(float (&acc)[kF8FmaRW], const float* __restrict__ scale,
+                                           float* __restrict__ y, int64_t row0, int lane) {
+  float tot[kF8FmaRW];
+#pragma unroll
+  for (int r = 0; r < kF8FmaRW; ++r) tot[r] = wave_sum(acc[r]);
+#pragma unroll
+  for (int r = 0; r < kF8FmaRW; ++r)
+    if (lane == r) y[row0 + r] = tot[r] * scale[row0 + r];
+}
+
+template <int UH, int UG, bool COUNT>
+__global__ __launch_bounds__(256) void gemm_fp8_fma_split(
+    const unsigned char* __restrict__ a_host, const unsigned char* __restrict__ a_hbm, int64_t K, int64_t host_rows,
+    const unsigned char* __restrict__ a_stage, int64_t stage_rows, const float* __restrict__ row_scale,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int host_wgs, int64_t host_items, int64_t hbm_items,
+    unsigned long long* __restrict__ counters) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t nbytes = 0;
+  const bool host_role = (int)blockIdx.x < host_wgs;
+  if (host_role) {
+    for (int64_t it = blockIdx.x; it < host_items; it += host_wgs) {
+      const int64_t row = it * kF8FmaItemRows + wave * kF8FmaRW;
+      float acc[kF8FmaRW] = {};
+      fma8_rows<UH, COUNT>(a_host + row * K, K, x, acc, lane, nbytes);
+      fma8_store(acc, row_scale, y, row, lane);
+    }
+  } else {
+    const int64_t it = (int64_t)blockIdx.x - host_wgs;
+    if (it < hbm_items) {
+      const int64_t lrow = it * kF8FmaItemRows + wave * kF8FmaRW;
+      float acc[kF8FmaRW] = {};
+      fma8_rows<UG, COUNT>(hbm_row(a_stage, stage_rows, a_hbm, lrow, K), K, x, acc, lane, nbytes);
+      fma8_store(acc, row_scale, y, host_rows + lrow, lane);
+    }
+  }
+  if (COUNT) {
+    uint64_t v = nbytes;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&counters[host_role ? 0 : 1], (unsigned long long)v);
+  }
+}
+
 struct F8Args {
   const unsigned char *a_host, *a_hbm;
   int64_t M, K, host_rows;
@@ -344,6 +455,26 @@ void launch_f8(const F8Args& g, int rb) {
   }
 }
 
+// The FMA path.  HBM work-groups keep 4 steps of loads in flight (16 KiB of
+// codes per step and work-group); host work-groups `window` steps.
+template <int UH, bool COUNT>
+void launch_f8_fma_w(const F8Args& g) {
+  const int64_t grid = g.host_wgs + g.hbm_items;
+  hipLaunchKernelGGL((gemm_fp8_fma_split<UH, 4, COUNT>), dim3((unsigned)grid), dim3(256), 0, g.stream, g.a_host,
+                     g.a_hbm, g.K, g.host_rows, g.a_stage, g.stage_rows, g.row_scale, g.x, g.y, g.host_wgs,
+                     g.host_items, g.hbm_items, g.counters);
+}
+
+template <bool COUNT>
+void launch_f8_fma(const F8Args& g, int window) {
+  switch (window) {
+    case 1: return launch_f8_fma_w<1, COUNT>(g);
+    case 2: return launch_f8_fma_w<2, COUNT>(g);
+    case 8: return launch_f8_fma_w<8, COUNT>(g);
+    default: return launch_f8_fma_w<4, COUNT>(g);
+  }
+}
+
 // Rows per item: taller items share each staged activation chunk over more
 // weight rows, as long as at least 384 items remain to spread over the CUs.
 int f8_row_blocks(int64_t M, int64_t m) {
@@ -392,9 +523,14 @@ extern "C" dak_status dak_splitk_gemm_fp8_ws(const dak_split_matrix_fp8* A, cons
   // Decode batches (N <= 64) take the memory-bound ring kernel below; wider
   // activations the compute-bound tiled kernel with FP8 A tiles.
   const bool tiled = N > kF8MaxN;
-  const int rb = tiled ? 1 : f8_row_blocks(M, m);
+  const bool fma = N == 1;
+  const int rb = tiled || fma ? 1 : f8_row_blocks(M, m);
   LaunchCfg lc;
-  dak_status st = resolve_cfg(cfg, tiled ? HostDefaults{kGemmTiledMaxHostCus} : HostDefaults{f8_host_cus(N, rb)}, &lc);
+  dak_status st = resolve_cfg(cfg,
+                              tiled ? HostDefaults{kGemmTiledMaxHostCus}
+                              : fma ? kGemmFmaDefaults
+                                    : HostDefaults{f8_host_cus(N, rb)},
+                              &lc);
   if (st) return st;
 
   const int64_t host_rows = h * m;
@@ -454,19 +590,28 @@ extern "C" dak_status dak_splitk_gemm_fp8_ws(const dak_split_matrix_fp8* A, cons
   g.x = static_cast<const uint16_t*>(dx);
   g.N = N;
   g.y = y;
-  const int64_t item_rows = 16 * rb;
+  const int64_t item_rows = fma ? kF8FmaItemRows : 16 * rb;
   g.host_items = g.host_rows / item_rows;
   g.hbm_items = (M - g.host_rows) / item_rows;
-  g.host_wgs = (int)host_workgroups(g.host_items, lc.host_cus);
+  // FMA path: a host work-group keeps at least one 16 KiB step of codes in flight.
+  g.host_wgs = (int)(fma ? gemm_host_workgroups(g.host_items, lc, 16u << 10) : host_workgroups(g.host_items, lc.host_cus));
   if ((st = device_cus(&g.cus))) return st;
   g.counters = reinterpret_cast<unsigned long long*>(lc.byte_counters);
   g.stream = static_cast<hipStream_t>(stream);
   if (g.host_wgs + g.hbm_items > 0x7fffffff) return fail(DAK_EINVAL, "grid too large");
   if (g.host_wgs + g.hbm_items == 0) return DAK_OK;
-  if (lc.flags & DAK_FLAG_COUNT_BYTES)
+  const bool count = (lc.flags & DAK_FLAG_COUNT_BYTES) != 0;
+  if (fma) {
+    const int window = lc.window ? lc.window : auto_window(g.host_wgs, 16u << 10, 8);
+    if (count)
+      launch_f8_fma<true>(g, window);
+    else
+      launch_f8_fma<false>(g, window);
+  } else if (count) {
     launch_f8<true>(g, rb);
-  else
+  } else {
     launch_f8<false>(g, rb);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "fp8 gemm kernel launch");
   return DAK_OK;

@@ -1,7 +1,8 @@
 // Split GEMM over FP8 weights: y = s . (x . e4m3(A)^T) with A's first h
 // tile-rows of e4m3 codes in pinned host memory, the rest in HBM, one fp32
 // scale per row and bf16 activations.  This file holds the memory-bound
-// kernel for decode batches (1 <= N <= 64) and the entry point; wider
+// kernels for decode batches (plain fp32 FMAs at N = 1, the LDS ring below
+// for 2 <= N <= 64) and the entry point; wider
 // activations (the compute-bound regime, DAK paper §4.2.1) go to the tiled
 // kernel with FP8 A tiles (splitk_gemm_tiled.hip), where halving the bytes of
 // a tile-row moves the turning point B_h / B_i to twice the host share.
@@ -520,8 +521,9 @@ extern "C" dak_status dak_splitk_gemm_fp8_ws(const dak_split_matrix_fp8* A, cons
   if (N < 1) return fail(DAK_EINVAL, "N=%lld must be >= 1", (long long)N);
   if (N > kTiledMaxN) return fail(DAK_EUNSUPPORTED, "N=%lld > %lld for FP8 weights", (long long)N, (long long)kTiledMaxN);
   if (K > (int64_t(1) << 40) || M > (int64_t(1) << 40)) return fail(DAK_EINVAL, "M or K too large");
-  // Decode batches (N <= 64) take the memory-bound ring kernel below; wider
-  // activations the compute-bound tiled kernel with FP8 A tiles.
+  // Decode batches take the memory-bound kernels below (the FMA path at
+  // N = 1, the ring for 2 <= N <= 64); wider activations the compute-bound
+  // tiled kernel with FP8 A tiles.
   const bool tiled = N > kF8MaxN;
   const bool fma = N == 1;
   const int rb = tiled || fma ? 1 : f8_row_blocks(M, m);

@@ -31,8 +31,8 @@ def _gpu():
 
 def _ops():
     """A mixed sequence: GEMMs on every path the flag takes (N = 1, 16, 64,
-    100; FP8 at N = 16), and split attention with request units and with
-    ragged (request, KV head) units.  Each op writes its own output."""
+    100; FP8 at N = 1 and 16), and split attention with request units and
+    with ragged (request, KV head) units.  Each op writes its own output."""
     ops, refs, outs = [], [], []
     for seed, (M, K, N, h) in enumerate([(512, 1024, 1, 3), (1024, 768, 16, 5), (768, 512, 64, 2),
                                          (512, 512, 100, 4), (256, 256, 3, 0)]):
@@ -42,12 +42,13 @@ def _ops():
         ops.append((S, lambda S_, cfg, x=x, y=y: dak.splitk_gemm(S_, x, y=y, cfg=cfg)))
         outs.append(y)
         refs.append(gemm(to_f64(A), to_f64(X)))
-    codes, scale, X = synth.fp8_gemm_inputs(512, 1024, 16, seed=90)
-    S8 = dak.place_matrix_fp8(codes, scale, 64, 3)
-    x8, y8 = X.cuda(), torch.empty((16, 512), dtype=torch.float32, device="cuda")
-    ops.append((S8, lambda S_, cfg: dak.splitk_gemm_fp8(S_, x8, y=y8, cfg=cfg)))
-    outs.append(y8)
-    refs.append(of.gemm_fp8(codes, scale, X))
+    for seed, N in enumerate((16, 1)):
+        codes, scale, X = synth.fp8_gemm_inputs(512, 1024, N, seed=90 + seed)
+        S8 = dak.place_matrix_fp8(codes, scale, 64, 3)
+        x8, y8 = X.cuda(), torch.empty((N, 512), dtype=torch.float32, device="cuda")
+        ops.append((S8, lambda S_, cfg, x8=x8, y8=y8: dak.splitk_gemm_fp8(S_, x8, y=y8, cfg=cfg)))
+        outs.append(y8)
+        refs.append(of.gemm_fp8(codes, scale, X))
     for seed, (B, Hq, Hkv, ctx, h, unit, lens) in enumerate([(4, 16, 4, 2500, 1, dak.KV_UNIT_REQUEST, None),
                                                               (3, 8, 2, 3000, 3, dak.KV_UNIT_HEAD, [3000, 17, 2049])]):
         q, K, V = synth.attn_inputs(B, Hq, Hkv, 128, ctx, seed=95 + seed)

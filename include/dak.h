@@ -369,7 +369,9 @@ typedef struct {
 } dak_split_kv;
 
 /* Bytes of device workspace dak_splitk_decode_attn needs for these shapes
- * (0 on invalid shapes). */
+ * (0 on invalid shapes): one record of head_dim + 2 floats per (request,
+ * query head, chunk), chunks of 4096 tokens where the (request, KV head)
+ * units times ceil(ctx / 4096) reach 1024 work items, else of 2048. */
 size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads);
 
 /* out[b, j, :] = sum_t softmax_t(scale * q[b, j] . K[b, g, t]) V[b, g, t, :]
@@ -396,8 +398,8 @@ dak_status dak_splitk_decode_attn(const void* q, const dak_split_kv* kv, int32_t
  * bytes, 16 MiB, kept until the process ends).  Nothing is allocated or
  * freed by the call.  Arguments, results, determinism and errors are those of
  * dak_splitk_decode_attn without ws/ws_bytes; in addition DAK_EINVAL when
- * dak_decode_attn_workspace_bytes(kv, n_q_heads) exceeds the array (e.g.
- * batch * n_q_heads * ceil(ctx / 2048) above 32263 records of 520 bytes).
+ * dak_decode_attn_workspace_bytes(kv, n_q_heads) exceeds the array (more
+ * than 32263 records of 520 bytes).
  * Every call on a device shares that device's array: calls that overlap in
  * time on one device (different streams, or different host threads without
  * ordering between their streams) race on it and their outputs are then

@@ -224,11 +224,18 @@ def test_attention_shape_errors_are_reported_before_any_launch():
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 32, C.c_float(float("inf")), None, None, 0, None, None) == L.DAK_EINVAL
     # workspace too small is caught before pointers are looked at
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 32, C.c_float(0.1), None, None, 16, None, None) == L.DAK_EINVAL
-    # workspace size: B * Hq * chunks * (D + 2) fp32, chunks of 2048 tokens
+    # workspace size: B * Hq * chunks * (D + 2) fp32, chunks of 2048 tokens,
+    # or of 4096 where (B * Hkv) * ceil(ctx / 4096) >= 1024 items
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 32) == 16 * 32 * 1 * 130 * 4
-    kv2 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768)
-    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 16 * 130 * 4   # 2048-token chunks
+    kv2 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768)   # 128 units x 8 chunks of 4096
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 8 * 130 * 4
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 30) == 0
+    kv3 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 28673)   # 128 units x 8 chunks of 4096
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv3), 32) == 16 * 32 * 8 * 130 * 4
+    kv4 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 28672)   # 7 chunks of 4096: 2048-token chunks
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv4), 32) == 16 * 32 * 14 * 130 * 4
+    kv5 = L.SplitKVDesc(None, None, None, None, 4, 1, 8, 128, 32768)    # 32 units: 2048-token chunks
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv5), 32) == 4 * 32 * 16 * 130 * 4
 
 
 def test_mfma_probe_argument_errors_before_any_launch():
@@ -313,11 +320,11 @@ def test_noalloc_attention_rejects_shapes_beyond_its_scratch_before_any_launch()
     lib = dak.library()
     cap = lib.dak_decode_attn_scratch_max_bytes()
     assert cap == 16 << 20
-    # 16 requests x 64 query heads x 32768 tokens: 16 * 64 * 16 records of 520 bytes fit
+    # 16 requests x 64 query heads x 32768 tokens: 16 * 64 * 8 records of 520 bytes fit
     kv = L.SplitKVDesc(None, None, None, None, 16, 0, 8, 128, 32768)
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 64) <= cap
-    # twice the batch does not
-    kv = L.SplitKVDesc(None, None, None, None, 32, 0, 8, 128, 32768)
+    # four times the batch (64 * 64 * 8 records) does not
+    kv = L.SplitKVDesc(None, None, None, None, 64, 0, 8, 128, 32768)
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 64) > cap
     st = lib.dak_splitk_decode_attn_noalloc(None, C.byref(kv), 64, C.c_float(0.1), None, None, None)
     assert st == L.DAK_EINVAL

@@ -37,9 +37,20 @@ namespace dak {
 namespace {
 
 constexpr int kD = 128;                 // the only head_dim the kernels handle
-constexpr int kChunk = 2048;            // tokens per work item
+// Tokens per work item: 4096 where a launch still has at least four items per
+// CU of MI355X (1024), else 2048, so small batches keep enough items to fill
+// the CUs.  Measured at 16 x 32768 tokens, x = 0, same box: eight heads
+// 389-394 -> 384 us, four heads 408 -> 401-407 us (fewer chunk records to
+// write and merge, twice the tokens per wave between them).  The rule sees
+// the units and the context only, never the split, so the bits do not depend
+// on it.  The paged kernel keeps 2048 (a wave's tokens then span at most 32
+// pages of 16 tokens).
+constexpr int kChunkSmall = 2048, kChunkLarge = 4096;
+constexpr int64_t kLargeChunkItems = 1024;
+inline int attn_chunk(int64_t units, int64_t ctx) {
+  return units * ((ctx + kChunkLarge - 1) / kChunkLarge) >= kLargeChunkItems ? kChunkLarge : kChunkSmall;
+}
 constexpr int kAttnWaves = 4;
-constexpr int kWaveTokens = kChunk / kAttnWaves;
 constexpr int kTile = 16;               // tokens per tile (4 loads of K + 4 of V per lane)
 constexpr float kNegInf = -INFINITY;
 
@@ -352,7 +363,7 @@ __device__ __forceinline__ void attn_tokens(const Rows& rows, int64_t tb, int64_
 // partial with o = l = NaN, which makes its rows NaN after the combine.
 template <int G, int U, bool COUNT, class Rows>
 __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const Rows& rows, bool poison, int64_t b,
-                                          int g, int c, int64_t len, int Hq, int C, float qscale,
+                                          int g, int c, int chunk, int64_t len, int Hq, int C, float qscale,
                                           float* __restrict__ o_ws, float* __restrict__ ml_ws, float* red_o,
                                           float* red_ml, int wave, int lane, uint64_t& nbytes) {
   const int dq = (lane & 15) * 8;
@@ -374,8 +385,9 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ q, const 
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
-  const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
-  const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
+  const int wave_tokens = chunk / kAttnWaves;
+  const int64_t tb = (int64_t)c * chunk + (int64_t)wave * wave_tokens;
+  const int64_t te = tb + wave_tokens < len ? tb + wave_tokens : len;
   float m[G];
   if constexpr (kPvOnMatrixCores<G>) {
     f32x4_t la = {0.f, 0.f, 0.f, 0.f}, oa[8];
@@ -497,7 +509,7 @@ template <int G, int UH, int UG, bool COUNT>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_host, const uint16_t* __restrict__ v_host,
     const uint16_t* __restrict__ k_hbm, const uint16_t* __restrict__ v_hbm, int64_t h_units, int Hkv, int Hq,
-    int64_t ctx, int C, const int32_t* __restrict__ ctx_lens, float qscale, float* __restrict__ o_ws,
+    int64_t ctx, int C, int chunk, const int32_t* __restrict__ ctx_lens, float qscale, float* __restrict__ o_ws,
     float* __restrict__ ml_ws, int host_wgs, int64_t host_items, int64_t hbm_items, int64_t stage_units,
     unsigned long long* __restrict__ counters) {
   __shared__ float red_o[kAttnWaves * G * kD];
@@ -511,9 +523,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
       int c;
       item_of(it, h_units, u, c);
       const int64_t b = u / Hkv, len = valid_len(ctx_lens, b, ctx);
-      if ((int64_t)c * kChunk >= len) continue;   // uniform
+      if ((int64_t)c * chunk >= len) continue;   // uniform
       const DenseRows rows{k_host + u * ctx * kD, v_host + u * ctx * kD};
-      attn_item<G, UH, COUNT>(q, rows, false, b, (int)(u % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o, red_ml,
+      attn_item<G, UH, COUNT>(q, rows, false, b, (int)(u % Hkv), c, chunk, len, Hq, C, qscale, o_ws, ml_ws, red_o, red_ml,
                               wave, lane, nbytes);
     }
   } else {
@@ -524,12 +536,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_split(
       item_of(it, hbm_items / C, u, c);
       const int64_t gu = h_units + u;
       const int64_t b = gu / Hkv, len = valid_len(ctx_lens, b, ctx);
-      if ((int64_t)c * kChunk < len) {
+      if ((int64_t)c * chunk < len) {
         // units [0, stage_units) of the HBM role come from a staged copy of
         // the host units (DAK_FLAG_STAGED_HOST), passed as k_host / v_host
         const DenseRows rows{hbm_row(k_host, stage_units, k_hbm, u, ctx * kD),
                              hbm_row(v_host, stage_units, v_hbm, u, ctx * kD)};
-        attn_item<G, UG, COUNT>(q, rows, false, b, (int)(gu % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o,
+        attn_item<G, UG, COUNT>(q, rows, false, b, (int)(gu % Hkv), c, chunk, len, Hq, C, qscale, o_ws, ml_ws, red_o,
                                 red_ml, wave, lane, nbytes);
       }
     }
@@ -557,8 +569,9 @@ __device__ __forceinline__ void paged_item(const uint16_t* __restrict__ q, const
                                            float* red_ml, int* bad_w, int wave, int lane, uint64_t& nbytes) {
   const int64_t b = u / Hkv;
   const int64_t len = valid_len(ctx_lens, b, (int64_t)max_pages << shift);
-  if ((int64_t)c * kChunk >= len) return;   // uniform: no tokens in this chunk
-  const int64_t tb = (int64_t)c * kChunk + (int64_t)wave * kWaveTokens;
+  constexpr int kWaveTokens = kChunkSmall / kAttnWaves;
+  if ((int64_t)c * kChunkSmall >= len) return;   // uniform: no tokens in this chunk
+  const int64_t tb = (int64_t)c * kChunkSmall + (int64_t)wave * kWaveTokens;
   const int64_t te = tb + kWaveTokens < len ? tb + kWaveTokens : len;
   const int64_t p0 = tb >> shift;
   int id = 0;
@@ -578,7 +591,8 @@ __device__ __forceinline__ void paged_item(const uint16_t* __restrict__ q, const
   for (int w = 0; w < kAttnWaves; ++w) poison |= bad_w[w];
   const PagedRows rows{pool_k, pool_v, shift, p0, id};
   // attn_item ends with a barrier, after which bad_w may be rewritten.
-  attn_item<G, U, COUNT>(q, rows, poison != 0, b, (int)(u % Hkv), c, len, Hq, C, qscale, o_ws, ml_ws, red_o, red_ml,
+  attn_item<G, U, COUNT>(q, rows, poison != 0, b, (int)(u % Hkv), c, kChunkSmall, len, Hq, C, qscale, o_ws, ml_ws,
+                         red_o, red_ml,
                          wave, lane, nbytes);
 }
 
@@ -632,7 +646,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_paged(
 // dimension over the chunks in chunk order; the chunk loads are independent, so
 // many are in flight at once.
 __global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_ws, const float* __restrict__ ml_ws,
-                                                   int C_ws, int Hq, int64_t ctx,
+                                                   int C_ws, int chunk, int Hq, int64_t ctx,
                                                    const int32_t* __restrict__ ctx_lens, float* __restrict__ out) {
   __shared__ float sm[2 * 256];
   const int64_t row = blockIdx.x;
@@ -641,9 +655,9 @@ __global__ __launch_bounds__(kD) void attn_combine(const float* __restrict__ o_w
   const float* ow = o_ws + row * C_ws * kD;
   // The chunks that hold tokens of this row's request.
   const int64_t len = valid_len(ctx_lens, row / Hq, ctx);
-  const int C = (int)((len + kChunk - 1) / kChunk);
+  const int C = (int)((len + chunk - 1) / chunk);
   float O = 0.f, L = 0.f;
-  // Chunks in groups of 256 (C is at most ctx / kChunk).
+  // Chunks in groups of 256 (C is at most ctx / chunk).
   float M = kNegInf;
   for (int c0 = 0; c0 < C; c0 += 256) {
     const int n = C - c0 < 256 ? C - c0 : 256;
@@ -686,7 +700,7 @@ struct AttnArgs {
   int64_t batch, h_units;
   int Hkv, Hq;
   int64_t ctx;
-  int C;
+  int C, chunk;   // chunks per request and tokens per chunk
   const int32_t* ctx_lens;
   float qscale;
   float *o_ws, *ml_ws, *out;
@@ -732,7 +746,7 @@ struct DenseLaunch {
     const int64_t grid = a.host_wgs + a.hbm_items;
     hipLaunchKernelGGL((attn_partial_split<G, Un::kH, Un::kG, COUNT>), dim3((unsigned)grid), dim3(kAttnWaves * 64),
                        0, a.stream, a.q, a.k_host, a.v_host, a.k_hbm, a.v_hbm, a.h_units, a.Hkv, a.Hq, a.ctx, a.C,
-                       a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.stage_units,
+                       a.chunk, a.ctx_lens, a.qscale, a.o_ws, a.ml_ws, a.host_wgs, a.host_items, a.hbm_items, a.stage_units,
                        a.counters);
   }
 };
@@ -810,7 +824,8 @@ bool attn_shapes_ok(const dak_split_kv* kv, int32_t n_q_heads) {
 extern "C" size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads) {
   using namespace dak;
   if (!attn_shapes_ok(kv, n_q_heads)) return 0;
-  const int64_t C = (kv->ctx + kChunk - 1) / kChunk;
+  const int chunk = attn_chunk(kv->batch * kv->n_kv_heads, kv->ctx);
+  const int64_t C = (kv->ctx + chunk - 1) / chunk;
   return (size_t)(kv->batch * n_q_heads * C) * (kD + 2) * sizeof(float);
 }
 
@@ -917,7 +932,8 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   a.Hkv = (int)Hkv;
   a.Hq = n_q_heads;
   a.ctx = ctx;
-  a.C = (int)((ctx + kChunk - 1) / kChunk);
+  a.chunk = attn_chunk(units, ctx);
+  a.C = (int)((ctx + a.chunk - 1) / a.chunk);
   a.qscale = scale * 1.4426950408889634f;   // scores in log2 units: exp2 gives e^(scale * q.k)
   a.o_ws = static_cast<float*>(ws);
   a.ml_ws = a.o_ws + (size_t)B * n_q_heads * a.C * kD;
@@ -932,7 +948,7 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
-                     n_q_heads, ctx, a.ctx_lens, out);
+                     a.chunk, n_q_heads, ctx, a.ctx_lens, out);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "attention combine launch");
   return DAK_OK;
@@ -974,7 +990,9 @@ bool paged_shapes_ok(const dak_paged_kv* kv, int32_t n_q_heads) {
          kv->hbm_pages < (int64_t(1) << 31);
 }
 
-int64_t paged_chunks(const dak_paged_kv* kv) { return ((int64_t)kv->max_pages * kv->page + kChunk - 1) / kChunk; }
+int64_t paged_chunks(const dak_paged_kv* kv) {
+  return ((int64_t)kv->max_pages * kv->page + kChunkSmall - 1) / kChunkSmall;
+}
 
 }  // namespace
 }  // namespace dak
@@ -1064,7 +1082,7 @@ extern "C" dak_status dak_paged_decode_attn(const void* q, const dak_paged_kv* k
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "paged attention partial launch");
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * n_q_heads)), dim3(kD), 0, a.stream, a.o_ws, a.ml_ws, a.C,
-                     n_q_heads, (int64_t)kv->max_pages * kv->page, a.ctx_lens, out);
+                     kChunkSmall, n_q_heads, (int64_t)kv->max_pages * kv->page, a.ctx_lens, out);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip((int)e, "paged attention combine launch");
   return DAK_OK;

@@ -370,8 +370,9 @@ typedef struct {
 
 /* Bytes of device workspace dak_splitk_decode_attn needs for these shapes
  * (0 on invalid shapes): one record of head_dim + 2 floats per (request,
- * query head, chunk), chunks of 4096 tokens where the (request, KV head)
- * units times ceil(ctx / 4096) reach 1024 work items, else of 2048. */
+ * query head, chunk), chunks of 4096 tokens where kv has no ctx_lens array
+ * and the (request, KV head) units times ceil(ctx / 4096) reach 1024 work
+ * items, else of 2048. */
 size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads);
 
 /* out[b, j, :] = sum_t softmax_t(scale * q[b, j] . K[b, g, t]) V[b, g, t, :]

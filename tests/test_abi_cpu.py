@@ -225,7 +225,8 @@ def test_attention_shape_errors_are_reported_before_any_launch():
     # workspace too small is caught before pointers are looked at
     assert lib.dak_splitk_decode_attn(None, C.byref(kv), 32, C.c_float(0.1), None, None, 16, None, None) == L.DAK_EINVAL
     # workspace size: B * Hq * chunks * (D + 2) fp32, chunks of 2048 tokens,
-    # or of 4096 where (B * Hkv) * ceil(ctx / 4096) >= 1024 items
+    # or of 4096 where no length array is given and (B * Hkv) * ceil(ctx /
+    # 4096) >= 1024 items
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv), 32) == 16 * 32 * 1 * 130 * 4
     kv2 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768)   # 128 units x 8 chunks of 4096
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv2), 32) == 16 * 32 * 8 * 130 * 4
@@ -236,6 +237,9 @@ def test_attention_shape_errors_are_reported_before_any_launch():
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv4), 32) == 16 * 32 * 14 * 130 * 4
     kv5 = L.SplitKVDesc(None, None, None, None, 4, 1, 8, 128, 32768)    # 32 units: 2048-token chunks
     assert lib.dak_decode_attn_workspace_bytes(C.byref(kv5), 32) == 4 * 32 * 16 * 130 * 4
+    # with per-request lengths (any non-null array; not read here): 2048-token chunks
+    kv6 = L.SplitKVDesc(None, None, None, None, 16, 4, 8, 128, 32768, 0, 0, 0x1000)
+    assert lib.dak_decode_attn_workspace_bytes(C.byref(kv6), 32) == 16 * 32 * 16 * 130 * 4
 
 
 def test_mfma_probe_argument_errors_before_any_launch():

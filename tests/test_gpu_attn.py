@@ -204,37 +204,41 @@ def test_ragged_lengths_match_the_oracle_at_every_split():
         assert torch.equal(run_kv(q, K, V, h, scale, unit=dak.KV_UNIT_HEAD, lens=lens), base), h
 
 
-def test_large_chunks_with_ragged_lengths_and_head_units():
+def test_chunk_length_at_full_size_with_head_units_and_ragged_lengths():
     # 16 requests x 32768 tokens on 8 KV heads make 1024 work items of 4096
-    # tokens, so this launch takes 4096-token chunks.  Ragged lengths at those
-    # chunk edges (and at the 2048-token ones) and head-unit host shares keep
-    # the all-HBM bits; every valid request's rows match the oracle.
+    # tokens: without a length array this launch takes 4096-token chunks, with
+    # one (ragged batches) 2048-token chunks.  Head-unit host shares keep the
+    # all-HBM bits in both, each tier's bytes are read once, and every valid
+    # request's rows match the oracle.
     B, Hq, Hkv, D, ctx = 16, 32, 8, 128, 32768
     q, K, V = synth.attn_inputs(B, Hq, Hkv, D, ctx, seed=43, device="cuda")
-    lens = torch.tensor([32768, 1, 4095, 4096, 4097, 8192, 2048, 2049, 30000, 12345, 16, 17, 20480, 4,
-                         31000, 32767], dtype=torch.int32)
+    ragged = torch.tensor([32768, 1, 4095, 4096, 4097, 8192, 2048, 2049, 30000, 12345, 16, 17, 20480, 4,
+                           31000, 32767], dtype=torch.int32)
     scale = 1.0 / np.sqrt(D)
     cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
-    kv = dak.place_kv(K, V, 0, ctx_lens=lens)
-    assert dak.decode_attn_workspace_bytes(kv, Hq) == B * Hq * 8 * (D + 2) * 4   # 8 chunks of 4096
-    base = run_kv(q, K, V, 0, scale, lens=lens)
-    for h, unit in ((3, dak.KV_UNIT_HEAD), (45, dak.KV_UNIT_HEAD), (2, dak.KV_UNIT_REQUEST)):
-        kv = dak.place_kv(K, V, h, unit=unit, ctx_lens=lens)
-        out = dak.splitk_decode_attn(q, kv, scale, cfg=dak.LaunchConfig(byte_counters=cnt.zero_()))
-        torch.cuda.synchronize()
-        assert torch.equal(out.cpu(), base), (h, unit)
-        per_unit = [int(lens[u // Hkv]) * D * 2 * 2 for u in range(B * Hkv)]
-        hu = h if unit == dak.KV_UNIT_HEAD else h * Hkv
-        assert cnt.tolist() == [sum(per_unit[:hu]), sum(per_unit[hu:])], (h, unit)
+    for lens, chunks in ((None, 8), (ragged, 16)):
+        kv = dak.place_kv(K, V, 0, ctx_lens=lens)
+        assert dak.decode_attn_workspace_bytes(kv, Hq) == B * Hq * chunks * (D + 2) * 4
         del kv
-    for b in range(B):
-        n = int(lens[b])
-        Kb, Vb = to_f64(K[b, :, :n]), to_f64(V[b, :, :n])
-        qb = to_f64(q[b])
-        for j in range(Hq):
-            gk = oa.kv_group(j, Hq, Hkv)
-            err = normwise_error(base[b, j].numpy(), oa.attend_one(qb[j], Kb[gk], Vb[gk], scale))
-            assert err <= TOL, (b, j, n, err)
+        base = run_kv(q, K, V, 0, scale, lens=lens)
+        n_of = [ctx] * B if lens is None else lens.tolist()
+        for h, unit in ((3, dak.KV_UNIT_HEAD), (45, dak.KV_UNIT_HEAD), (2, dak.KV_UNIT_REQUEST)):
+            kv = dak.place_kv(K, V, h, unit=unit, ctx_lens=lens)
+            out = dak.splitk_decode_attn(q, kv, scale, cfg=dak.LaunchConfig(byte_counters=cnt.zero_()))
+            torch.cuda.synchronize()
+            assert torch.equal(out.cpu(), base), (chunks, h, unit)
+            per_unit = [n_of[u // Hkv] * D * 2 * 2 for u in range(B * Hkv)]
+            hu = h if unit == dak.KV_UNIT_HEAD else h * Hkv
+            assert cnt.tolist() == [sum(per_unit[:hu]), sum(per_unit[hu:])], (chunks, h, unit)
+            del kv
+        for b in (range(B) if lens is not None else (0, 7, 15)):
+            n = n_of[b]
+            Kb, Vb = to_f64(K[b, :, :n]), to_f64(V[b, :, :n])
+            qb = to_f64(q[b])
+            for j in range(Hq):
+                gk = oa.kv_group(j, Hq, Hkv)
+                err = normwise_error(base[b, j].numpy(), oa.attend_one(qb[j], Kb[gk], Vb[gk], scale))
+                assert err <= TOL, (chunks, b, j, n, err)
     del K, V
     torch.cuda.empty_cache()
 

@@ -37,18 +37,20 @@ namespace dak {
 namespace {
 
 constexpr int kD = 128;                 // the only head_dim the kernels handle
-// Tokens per work item: 4096 where a launch still has at least four items per
-// CU of MI355X (1024), else 2048, so small batches keep enough items to fill
-// the CUs.  Measured at 16 x 32768 tokens, x = 0, same box: eight heads
-// 389-394 -> 384 us, four heads 408 -> 401-407 us (fewer chunk records to
-// write and merge, twice the tokens per wave between them).  The rule sees
-// the units and the context only, never the split, so the bits do not depend
-// on it.  The paged kernel keeps 2048 (a wave's tokens then span at most 32
-// pages of 16 tokens).
+// Tokens per work item: 4096 where every request holds the whole context (no
+// length array) and a launch still has at least four items per CU of MI355X
+// (1024), else 2048: small batches keep enough items to fill the CUs, and
+// with per-request lengths shorter chunks balance the uneven work (the
+// bench's ragged mix at x = 0: 219 us with 2048, 244 us with 4096).
+// Measured at 16 x 32768 tokens, x = 0, same box: eight heads 400-403 ->
+// 391 us, four heads unchanged to 3 % faster.  The rule sees the shape only,
+// never the split, so the bits do not depend on it.  The paged kernel keeps
+// 2048 (a wave's tokens then span at most 32 pages of 16 tokens).
 constexpr int kChunkSmall = 2048, kChunkLarge = 4096;
 constexpr int64_t kLargeChunkItems = 1024;
-inline int attn_chunk(int64_t units, int64_t ctx) {
-  return units * ((ctx + kChunkLarge - 1) / kChunkLarge) >= kLargeChunkItems ? kChunkLarge : kChunkSmall;
+inline int attn_chunk(int64_t units, int64_t ctx, bool has_lens) {
+  return !has_lens && units * ((ctx + kChunkLarge - 1) / kChunkLarge) >= kLargeChunkItems ? kChunkLarge
+                                                                                         : kChunkSmall;
 }
 constexpr int kAttnWaves = 4;
 constexpr int kTile = 16;               // tokens per tile (4 loads of K + 4 of V per lane)
@@ -824,7 +826,7 @@ bool attn_shapes_ok(const dak_split_kv* kv, int32_t n_q_heads) {
 extern "C" size_t dak_decode_attn_workspace_bytes(const dak_split_kv* kv, int32_t n_q_heads) {
   using namespace dak;
   if (!attn_shapes_ok(kv, n_q_heads)) return 0;
-  const int chunk = attn_chunk(kv->batch * kv->n_kv_heads, kv->ctx);
+  const int chunk = attn_chunk(kv->batch * kv->n_kv_heads, kv->ctx, kv->ctx_lens != nullptr);
   const int64_t C = (kv->ctx + chunk - 1) / chunk;
   return (size_t)(kv->batch * n_q_heads * C) * (kD + 2) * sizeof(float);
 }
@@ -932,7 +934,7 @@ dak_status decode_attn(const void* q, const dak_split_kv* kv, int32_t n_q_heads,
   a.Hkv = (int)Hkv;
   a.Hq = n_q_heads;
   a.ctx = ctx;
-  a.chunk = attn_chunk(units, ctx);
+  a.chunk = attn_chunk(units, ctx, kv->ctx_lens != nullptr);
   a.C = (int)((ctx + a.chunk - 1) / a.chunk);
   a.qscale = scale * 1.4426950408889634f;   // scores in log2 units: exp2 gives e^(scale * q.k)
   a.o_ws = static_cast<float*>(ws);
